@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each pin is a closed form, a library routine on a special case, a hand-worked
+value from ``tests/golden`` or a property the mathematics fixes, chosen so that
+a dropped term, a wrong sign or index, or a transposed operand in the oracle
+fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- formats
+def test_e4m3_all_codes_match_torch_and_round_trip():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        v = O.e4m3_decode(c)
+        if c & 0x7F == 0x7F:
+            assert math.isnan(v) and math.isnan(ref[c])
+            continue
+        assert v == ref[c], c
+        assert O.e4m3_encode(v) == c, c
+
+
+def test_e4m3_encode_matches_torch_cast_incl_ties():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.normal(0, 1, 4000),
+                        rng.normal(0, 0.01, 2000)]).astype(np.float32)
+    # exact midpoints between neighbouring codes (ties)
+    vals = np.array([O.e4m3_decode(c) for c in range(127)])
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    assert (got == ref).all()
+
+
+def test_e4m3_hand_cases():
+    for y, code in gold("hand_cases.json")["e4m3_encode"]["cases"]:
+        assert O.e4m3_encode(y) == code, y
+
+
+def test_bf16_round_matches_torch_and_hand():
+    for x, r in gold("hand_cases.json")["bf16_round"]["cases"]:
+        assert O.bf16_round(x) == r
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 10, 5000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = np.array([O.bf16_round(float(v)) for v in x], dtype=np.float32)
+    assert (got == ref).all()
+
+
+def test_store_records_structure():
+    cfg = O.OCfg(d=64, d_rope=16, n_heads=8)
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 1, (50, 64))
+    st = O.store_records(x, cfg)
+    n8 = 48
+    for r in range(50):
+        amax = np.float32(np.abs(x[r, :n8]).astype(np.float32).max())
+        scale = np.float32(amax / np.float32(448.0))
+        codes = st[r, :n8] / np.float64(scale)
+        # every fp8 value is an E4M3 value times the shared scale
+        e4 = torch.from_numpy(codes.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        assert np.array_equal(e4, codes)
+        # the largest magnitude maps to the top code
+        assert np.abs(codes).max() == 448.0
+        # relative error of an E4M3 rounding is at most 2^-4 (normal range)
+        big = np.abs(x[r, :n8]) > 8 * scale * 2.0 ** -6
+        assert (np.abs(st[r, :n8][big] - x[r, :n8][big]) <= np.abs(x[r, :n8][big]) * 2.0 ** -4 + 1e-12).all()
+        # RoPE dims are bf16 of the fp32 value
+        ref = torch.from_numpy(x[r, n8:].astype(np.float32)).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(st[r, n8:], ref)
+    # fp32 storage mode is plain fp32 rounding
+    cfg0 = O.OCfg(d=64, d_rope=16, n_heads=8, kv_mode=0)
+    assert np.array_equal(O.store_records(x, cfg0), x.astype(np.float32).astype(np.float64))
+    # all-zero record stores zeros
+    assert not O.store_records(np.zeros((1, 64)), cfg).any()
+
+
+def test_record_bytes_nearly_half():
+    g = gold("record_bytes.json")
+    fp8 = g["d"] - g["d_rope"]
+    bf = 2 * g["d_rope"]
+    assert (fp8, bf) == (g["fp8_bytes"], g["bf16_rope_bytes"])
+    assert (fp8 + bf) / (2 * g["d"]) == g["ratio"]
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_hand_position_1():
+    h = gold("hand_cases.json")["rope_position_1"]
+    cfg = O.OCfg(d=4, d_rope=4, n_heads=1, rope_base=h["base"])
+    got = O.rope(np.array([h["x"]]), h["pos"], cfg)[0]
+    assert np.allclose(got, h["expect"], rtol=0, atol=1e-15)
+
+
+def test_rope_properties():
+    cfg = O.OCfg(d=64, d_rope=16, n_heads=1)
+    rng = np.random.default_rng(5)
+    x, y = rng.normal(size=(2, 64))
+    # position 0 is the identity; only the last d_rope dims move
+    assert np.array_equal(O.rope(x[None], 0, cfg)[0], x)
+    rx = O.rope(x[None], 777, cfg)[0]
+    assert np.array_equal(rx[:48], x[:48])
+    # norm preserved per pair
+    assert np.allclose(np.hypot(rx[48::2], rx[49::2]), np.hypot(x[48::2], x[49::2]), rtol=1e-13)
+    # inner products depend only on the position difference
+    for a, b in [(3, 10), (1000, 1007), (123456, 123463)]:
+        l = O.rope(x[None], a, cfg)[0] @ O.rope(y[None], b, cfg)[0]
+        r = O.rope(x[None], 0, cfg)[0] @ O.rope(y[None], b - a, cfg)[0]
+        assert abs(l - r) < 1e-9
+    # a rotation by -p undoes a rotation by p
+    back = O.rope(O.rope(x[None], 4242, cfg), -4242, cfg)[0]
+    assert np.allclose(back, x, atol=1e-12)
+
+
+# ---------------------------------------------------------------- compressor
+def test_pool_hand_two_tokens():
+    h = gold("hand_cases.json")["two_token_pool"]
+    got = O.pool(np.array(h["kv"]), np.array(h["gate"]), [0], [2])[0]
+    assert np.allclose(got, h["expect"], atol=1e-14)
+
+
+def test_pool_equal_gates_is_mean_and_dominant_gate_selects():
+    rng = np.random.default_rng(9)
+    kv = rng.normal(size=(8, 32))
+    g = np.full((8, 32), 0.3)
+    assert np.allclose(O.pool(kv, g, [0], [8])[0], kv.mean(axis=0), atol=1e-14)
+    g2 = rng.normal(size=(8, 32))
+    g2[5, :] = 800.0
+    assert np.allclose(O.pool(kv, g2, [0], [8])[0], kv[5], atol=1e-12)
+    # per-channel independence and shift invariance of the gate
+    g3 = g2.copy()
+    g3[:, 7] += 11.0
+    a, b = O.pool(kv, g2, [0], [8])[0], O.pool(kv, g3, [0], [8])[0]
+    assert np.allclose(a, b, atol=1e-12)
+    g4 = rng.normal(size=(8, 32))
+    g5 = g4.copy()
+    g5[2, 3] += 1.0
+    a, b = O.pool(kv, g4, [0], [8])[0], O.pool(kv, g5, [0], [8])[0]
+    assert np.array_equal(np.delete(a, 3), np.delete(b, 3)) and a[3] != b[3]
+    # a convex combination stays within the per-channel range
+    e = O.pool(kv, g4, [0], [8])[0]
+    assert (e <= kv.max(0) + 1e-12).all() and (e >= kv.min(0) - 1e-12).all()
+
+
+def test_entry_counts_and_token_ranges():
+    g = gold("entry_counts.json")
+    cfg = O.OCfg()
+    for c in g["cases"]:
+        t = c["tokens"] - 1          # last position of a sequence of that length
+        assert O.n_visible("csa", t, cfg) == c["csa_entries"]
+        assert O.n_visible("hca", t, cfg) == c["hca_entries"]
+        if "hca_below" in c:
+            assert c["hca_entries"] < c["hca_below"]
+    for j, lo, hi in g["csa_token_ranges"]["cases"]:
+        assert O.csa_entry_tokens(j, cfg) == (lo, hi)
+    assert O.hca_entry_tokens(3, cfg) == (384, 512)
+
+
+def test_overlap_membership_by_planted_gate():
+    """A token dominating its gate shows up in exactly the entries whose
+    (backward-overlapped) window contains it: floor(s/4) and floor(s/4)+1."""
+    cfg = O.OCfg(d=16, d_rope=8, n_heads=1, kv_mode=0)
+    rng = np.random.default_rng(1)
+    T = 40
+    kv = rng.normal(size=(T, 16))
+    gate = rng.normal(size=(T, 16)) * 0.1
+    s = 13
+    gate[s] = 900.0
+    js = range(T // 4)
+    pooled = O.pool(kv, gate, [O.csa_entry_tokens(j, cfg)[0] for j in js],
+                    [O.csa_entry_tokens(j, cfg)[1] - O.csa_entry_tokens(j, cfg)[0] for j in js])
+    hit = [j for j in js if np.allclose(pooled[j], kv[s], atol=1e-9)]
+    assert hit == [s // 4, s // 4 + 1]
+
+
+# ---------------------------------------------------------------- indexer
+def test_index_scores_single_head_is_relu_dot():
+    rng = np.random.default_rng(2)
+    q = rng.normal(size=(1, 24))
+    k = rng.normal(size=(50, 24))
+    got = O.index_scores(q, np.ones(1), k)
+    ref = np.maximum(0.0, np.dot(k, q[0]))
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+    assert (got >= 0).all() and (got == 0).any()
+
+
+def test_index_scores_properties():
+    rng = np.random.default_rng(4)
+    H, D, N = 3, 5, 7                        # non-square on purpose
+    q = rng.normal(size=(H, D))
+    k = rng.normal(size=(N, D))
+    w1, w2 = rng.normal(size=H), rng.normal(size=H)
+    s1, s2 = O.index_scores(q, w1, k), O.index_scores(q, w2, k)
+    assert np.allclose(O.index_scores(q, w1 + w2, k), s1 + s2, atol=1e-12)      # linear in w
+    assert np.allclose(O.index_scores(2.5 * q, w1, k), 2.5 * s1, atol=1e-12)    # ReLU is positively homogeneous
+    perm = [2, 0, 1]
+    assert np.allclose(O.index_scores(q[perm], w1[perm], k), s1, atol=1e-12)   # head order is irrelevant
+    # a head whose dot products are all negative contributes nothing
+    qn = np.vstack([q, -k.sum(0) * 100])
+    kk = k.copy()
+    qn[-1] = -np.abs(qn[-1])
+    kk = np.abs(kk)
+    assert np.allclose(O.index_scores(qn, np.r_[w1, 5.0], kk), O.index_scores(q, w1, kk), atol=1e-12)
+    # each head sees the key through a dot product: single key, single head,
+    # zero out dims one at a time
+    e = O.index_scores(np.eye(D)[None, 3], np.ones(1), k)
+    assert np.allclose(e, np.maximum(0, k[:, 3]))
+
+
+# ---------------------------------------------------------------- top-k
+def test_topk_hand_and_lexsort():
+    h = gold("hand_cases.json")["topk_ties"]
+    for k, exp in h["cases"]:
+        assert O.topk(h["scores"], k).tolist() == exp
+    rng = np.random.default_rng(8)
+    for N, k in [(1000, 37), (4096, 512), (5, 5), (1, 3)]:
+        s = np.round(rng.normal(size=N), 1)                       # many ties
+        order = np.lexsort((np.arange(N), -s))
+        ref = np.sort(order[:min(k, N)])
+        got = O.topk(s, k)
+        assert got[:len(ref)].tolist() == ref.tolist()
+        assert (got[len(ref):] == -1).all()
+
+
+def test_topk_nan_lowest():
+    s = np.array([np.nan, 1.0, -5.0, np.nan, 0.0])
+    assert O.topk(s, 3).tolist() == [1, 2, 4]
+
+
+# ---------------------------------------------------------------- attention
+def test_attend_hand_sink_half():
+    h = gold("hand_cases.json")["sink_half"]
+    v = np.array([h["v"]])
+    q = np.zeros((1, 4))
+    o, sm = O.attend(q, [h["sink"]], v, 1.0, return_sink_mass=True)
+    assert np.allclose(o[0], h["expect"], atol=1e-15) and abs(sm[0] - h["sink_mass"]) < 1e-15
+
+
+def test_attend_sink_limits_and_single_record():
+    rng = np.random.default_rng(6)
+    q = rng.normal(size=(4, 16))
+    r = rng.normal(size=(9, 16))
+    # no sink: one record -> the record itself
+    o = O.attend(q, np.full(4, -np.inf), r[:1], 0.25)
+    assert np.allclose(o, np.broadcast_to(r[0], (4, 16)), atol=1e-15)
+    # a huge sink absorbs all mass
+    o, sm = O.attend(q, np.full(4, 1e4), r, 0.25, return_sink_mass=True)
+    assert np.abs(o).max() < 1e-300 and np.allclose(sm, 1.0)
+    # sink mass + attention mass = 1 for a finite sink, checked from outside:
+    # o computed with sink z equals (1 - sink_mass) * o computed without sink
+    z = rng.normal(size=4)
+    o1, sm1 = O.attend(q, z, r, 0.25, return_sink_mass=True)
+    o0 = O.attend(q, np.full(4, -np.inf), r, 0.25)
+    assert np.allclose(o1, (1 - sm1)[:, None] * o0, atol=1e-13)
+    lg = 0.25 * q @ r.T
+    assert np.allclose(sm1, np.exp(z) / (np.exp(z) + np.exp(lg).sum(1)), rtol=1e-12)
+
+
+def test_attend_without_sink_is_sdpa():
+    rng = np.random.default_rng(12)
+    H, d, n = 6, 32, 21
+    q = rng.normal(size=(H, d))
+    r = rng.normal(size=(n, d))
+    tau = 1 / math.sqrt(d)
+    got = O.attend(q, np.full(H, -np.inf), r, tau)
+    qt = torch.from_numpy(q)[None, :, None, :]                        # [1, H, 1, d]
+    kt = torch.from_numpy(r)[None, None].expand(1, H, n, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=tau)[0, :, 0].numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- composition
+def _sdpa_causal(qrot, recs, t, tau):
+    qt = torch.from_numpy(qrot)[None, :, None, :]
+    kt = torch.from_numpy(recs[: t + 1])[None, None].expand(1, qrot.shape[0], t + 1, recs.shape[1])
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=tau)[0, :, 0].numpy()
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_layer_reduces_to_dense_causal_mqa(kind):
+    """m=1, window of compression 1, top-k >= T and no raw window: every token is
+    its own entry, all are selected, so the layer is dense causal MQA over the
+    stored tokens (sink removed)."""
+    T, H, d = 24, 4, 32
+    cfg = O.OCfg(d=d, d_rope=8, n_heads=H, window=0, m_csa=1, w_csa=1, m_hca=1,
+                 idx_heads=2, idx_dim=16, topk=64)
+    rng = np.random.default_rng(21)
+    kv = rng.normal(size=(T, d))
+    gate = rng.normal(size=(T, d))
+    kI, gI = rng.normal(size=(2, T, 16))
+    q = rng.normal(size=(T, H, d))
+    qI = rng.normal(size=(T, 2, 16))
+    sinks = np.full(H, -np.inf)
+    pos = list(range(T))
+    if kind == "csa":
+        outs, idx = O.csa_layer(kv, gate, kI, gI, q, qI, None, sinks, pos, cfg)
+        for t in pos:
+            assert idx[t][: t + 1].tolist() == list(range(t + 1))
+    else:
+        outs = O.hca_layer(kv, gate, q, sinks, pos, cfg)
+    recs = O.window_records(kv, np.arange(T), cfg)
+    for t in pos:
+        ref = _sdpa_causal(O.query_rot(q[t], t, cfg), recs, t, cfg.tau)
+        assert np.allclose(outs[t], ref, rtol=1e-11, atol=1e-12), t
+
+
+def test_early_positions_attend_window_only():
+    """Before the first block completes (t < m-1) CSA sees only its window."""
+    cfg = O.OCfg(d=32, d_rope=8, n_heads=2, window=16, idx_heads=2, idx_dim=16, topk=8)
+    rng = np.random.default_rng(22)
+    T = 3
+    kv, gate = rng.normal(size=(2, T, 32))
+    kI, gI = rng.normal(size=(2, T, 16))
+    q = rng.normal(size=(T, 2, 32))
+    qI = rng.normal(size=(T, 2, 16))
+    outs, idx = O.csa_layer(kv, gate, kI, gI, q, qI, None, np.full(2, -np.inf), [0, 1, 2], cfg)
+    recs = O.window_records(kv, np.arange(T), cfg)
+    for t in range(T):
+        assert (idx[t] == -1).all()
+        assert np.allclose(outs[t], _sdpa_causal(O.query_rot(q[t], t, cfg), recs, t, cfg.tau), atol=1e-12)
+
+
+def test_planted_key_is_selected_first():
+    cfg = O.OCfg(d=32, d_rope=8, n_heads=2, idx_heads=4, idx_dim=16, topk=3)
+    rng = np.random.default_rng(23)
+    keys = O.store_index_rows(rng.normal(size=(200, 16)), cfg)
+    qI = rng.normal(size=(4, 16))
+    keys[77] = O.store_index_rows(qI[0][None] * 10, cfg)[0]
+    w = np.array([1.0, 0.0, 0.0, 0.0])
+    idx, s = O.csa_select(4 * 200 - 1, qI, w, keys, cfg)
+    assert 77 in idx.tolist() and np.argmax(s) == 77
+
+
+def test_window_membership():
+    cfg = O.OCfg(window=128)
+    assert list(O.window_tokens(0, cfg)) == [0]
+    assert list(O.window_tokens(127, cfg)) == list(range(128))
+    assert list(O.window_tokens(1000, cfg)) == list(range(873, 1001))
