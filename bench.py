@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: decode step of an interleaved CSA+HCA layer pair on one MI355X.
+
+A step = one pass of the whole decode hot path for a batch of requests:
+  CSA layer: append+compress -> indexer scoring -> top-k -> sparse MQA
+  HCA layer: append+compress -> dense MQA
+at the V4-Pro shape (128 heads x d 512, RoPE 64, window 128, indexer 64x128,
+top-1024), batch 32 at 128K context (32768 CSA entries, 1024 HCA entries per
+request), FP8/BF16 cache.  Every step appends the next token of every request,
+so one step in four completes a CSA entry and the compressor runs as in a real
+decode.  Inputs are synthetic, seeded, already resident in HBM when timing
+starts.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B] [--ctx N]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+METRIC = "CSA/HCA decode queries/s at 128K–1M ctx; % HBM BW and % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--ctx", type=int, default=131072)
+    ap.add_argument("--policy", default="auto", choices=["auto", "hi", "lo"])
+    ap.add_argument("--cpu-sample", type=int, default=8, help="queries timed on the CPU oracle (0: skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (traffic calibration under --pmc)")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    from long_context_compressed_02_amd import binding as B
+    from long_context_compressed_02_amd import synth
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    w = synth.CSA_DECODE_128K
+    Bsz, ctx = a.batch, a.ctx
+    steps, warm = a.steps, a.warmup
+    total_new = steps + warm
+    cfg = B.make_cfg(**w.shape())
+    policy = {"auto": B.DSV4_POLICY_AUTO, "hi": B.DSV4_POLICY_HI, "lo": B.DSV4_POLICY_LO}[a.policy]
+    H, d, HI_, dI, k = w.n_heads, w.d, w.idx_heads, w.idx_dim, w.topk
+
+    # ---------------------------------------------------------------- caches
+    need_blocks = (ctx + total_new + 127) // 128
+    bt = torch.arange(Bsz * need_blocks, dtype=torch.int32, device=dev).view(Bsz, need_blocks)
+    # interleave requests' blocks so physical placement is not contiguous per request
+    perm = torch.from_numpy(synth.permutation(w.wid, Bsz * need_blocks)).to(dev).to(torch.int32)
+    bt = perm[bt.view(-1).long()].view(Bsz, need_blocks).contiguous()
+    csa = B.LayerCache(cfg, B.DSV4_CSA, Bsz, need_blocks, Bsz * need_blocks, bt)
+    hca = B.LayerCache(cfg, B.DSV4_HCA, Bsz, need_blocks, Bsz * need_blocks, bt)
+    n_csa, n_hca = ctx // 4, ctx // 128
+    t_setup = time.time()
+    for r in range(Bsz):
+        rr = torch.full((n_csa,), r, dtype=torch.int32, device=dev)
+        B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_ENTRY, rr, torch.arange(n_csa, dtype=torch.int32, device=dev),
+                                   torch.from_numpy(synth.entries(w, r, n_csa, 0)).to(dev))
+        B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_INDEX_KEY, rr,
+                                   torch.arange(n_csa, dtype=torch.int32, device=dev),
+                                   torch.from_numpy(synth.index_keys(w, r, n_csa)).to(dev))
+        rh = torch.full((n_hca,), r, dtype=torch.int32, device=dev)
+        B.dsv4_cache_write_entries(cfg, hca, B.DSV4_TARGET_ENTRY, rh, torch.arange(n_hca, dtype=torch.int32, device=dev),
+                                   torch.from_numpy(synth.entries(w, r, n_hca, 1)).to(dev))
+        kv, gate, kI, gI = synth.window_tokens(w, r, 128, 0)
+        bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+        B.dsv4_state_write_tokens(cfg, csa, r, ctx - 128, bf(kv), bf(gate), bf(kI), bf(gI))
+        kv, gate, _, _ = synth.window_tokens(w, r, 128, 1)
+        B.dsv4_state_write_tokens(cfg, hca, r, ctx - 128, bf(kv), bf(gate))
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    # ---------------------------------------------------------------- per-step inputs (resident)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    rn = lambda *s: torch.randn(*s, generator=g, device=dev, dtype=torch.float32)
+    steps_in = []
+    for s in range(total_new):
+        steps_in.append(dict(
+            kv=rn(Bsz, d).bfloat16(), gate=rn(Bsz, d).bfloat16(), kI=rn(Bsz, dI).bfloat16(), gI=rn(Bsz, dI).bfloat16(),
+            kvh=rn(Bsz, d).bfloat16(), gateh=rn(Bsz, d).bfloat16(),
+            q=rn(Bsz, H, d).bfloat16(), qh=rn(Bsz, H, d).bfloat16(),
+            qI=rn(Bsz, HI_, dI).bfloat16(), w=rn(Bsz, HI_) / 8.0,
+            pos=torch.full((Bsz,), ctx + s, dtype=torch.int32, device=dev)))
+    req = torch.arange(Bsz, dtype=torch.int32, device=dev)
+    sinks = torch.from_numpy(synth.sinks(w)).to(dev)
+    ws = torch.empty(B.dsv4_workspace_bytes(cfg, Bsz, need_blocks * 32), dtype=torch.uint8, device=dev)
+    topk = torch.empty((Bsz, k), dtype=torch.int32, device=dev)
+    out_c = torch.empty((Bsz, H, d), dtype=torch.bfloat16, device=dev)
+    out_h = torch.empty((Bsz, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        x = steps_in[s]
+        B.dsv4_compress_kv_decode(cfg, csa, x["kv"], x["gate"], x["kI"], x["gI"], req, x["pos"], stream)
+        B.dsv4_index_topk_decode(cfg, csa, x["qI"], x["w"], req, x["pos"], topk, ws, stream)
+        B.dsv4_csa_attend_decode(cfg, csa, x["q"], req, x["pos"], topk, sinks, out_c, policy, stream)
+        B.dsv4_compress_kv_decode(cfg, hca, x["kvh"], x["gateh"], None, None, req, x["pos"], stream)
+        B.dsv4_hca_attend_decode(cfg, hca, x["qh"], req, x["pos"], sinks, out_h, policy, stream)
+
+    for s in range(warm):
+        step(s)
+    torch.cuda.synchronize()
+    for kid in range(B.DSV4_K_COUNT):
+        B.dsv4_timer_enable(kid, False)
+        B.dsv4_timer_read(kid, True)
+    # timed region (no per-kernel events: wall clock of K steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(warm, total_new):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+
+    # per-kernel durations over a second pass of the same steps, HIP events
+    # recorded by the library on the launch stream around each kernel
+    for kid in range(B.DSV4_K_COUNT):
+        B.dsv4_timer_enable(kid, True)
+    for s in range(warm, total_new):
+        step(s)
+    torch.cuda.synchronize()
+    kern = {}
+    names = {B.DSV4_K_COMPRESS: "compress", B.DSV4_K_INDEX_SCORE: "index_score", B.DSV4_K_TOPK: "topk",
+             B.DSV4_K_ATTEND: "attend"}
+    for kid, nm in names.items():
+        ms, n = B.dsv4_timer_read(kid, True)
+        B.dsv4_timer_enable(kid, False)
+        kern[nm] = dict(total_ms=ms, launches=n, avg_us=1e3 * ms / max(n, 1))
+
+    if a.calib_copy_mib:
+        src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- roofline
+    # algorithmic work per step (positions ctx+s, averaged over the timed steps)
+    n_vis = np.mean([(ctx + s + 1) // 4 for s in range(warm, total_new)])
+    n_h = np.mean([(ctx + s + 1) // 128 for s in range(warm, total_new)])
+    key_b = dI + 4                                      # E4M3 key + fp32 scale
+    score_bytes = Bsz * n_vis * (key_b + 4) + Bsz * HI_ * (dI + 4)       # keys+scales read, scores written, queries
+    score_flops = Bsz * n_vis * HI_ * dI * 2
+    rec_b = (d - 64) + 2 * 64 + 4                        # 580 B per stored record
+    csa_recs = Bsz * (k + 128)
+    hca_recs = Bsz * (n_h + 128)
+    attend_bytes_step = (csa_recs + hca_recs) * rec_b + 2 * (2 * Bsz * H * d * 2)
+    attend_flops_step = (csa_recs + hca_recs) * H * 4 * d
+    per_launch = {
+        "index_score": dict(bound="hbm", work=score_bytes, unit="GB/s", peak=HBM_PEAK_GBS),
+        "attend": dict(bound="mfma", work=attend_flops_step / 2, unit="TFLOP/s", peak=BF16_PEAK_TFLOPS),
+    }
+    dom = max(kern, key=lambda n_: kern[n_]["total_ms"])
+    if dom not in per_launch:
+        dom = "index_score"
+    pl = per_launch[dom]
+    avg_s = kern[dom]["avg_us"] * 1e-6
+    achieved = pl["work"] / avg_s / (1e9 if pl["unit"] == "GB/s" else 1e12)
+    roof = {"kernel": {"index_score": "k_index_score_decode", "attend": "k_attend"}[dom], "bound": pl["bound"],
+            "achieved": round(achieved, 2), "peak": pl["peak"], "unit": pl["unit"],
+            "frac": round(achieved / pl["peak"], 4), "traffic": None}
+    step_bytes = score_bytes + attend_bytes_step
+    value = Bsz / (ms_step * 1e-3)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if a.cpu_sample > 0:
+        cpu = cpu_baseline(w, a.cpu_sample, ctx + warm)
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8/bf16", "data": "synthetic",
+        "config": {"workload": f"V4-Pro CSA+HCA layer-pair decode, batch {Bsz} x {ctx // 1024}K ctx "
+                               f"({ctx // 4} CSA / {ctx // 128} HCA entries per request), top-{k}, "
+                               f"{H} heads x d {d}, window 128",
+                   "batch": Bsz, "ctx": ctx, "topk": k, "heads": H, "d": d, "policy": a.policy},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items()},
+        "launches_per_step": {n_: v["launches"] / steps for n_, v in kern.items()},
+        "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "attend_TFLOPs": round(attend_flops_step / (kern["attend"]["total_ms"] / steps * 1e-3) / 1e12, 1),
+        "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, nq, t):
+    """The oracle (as it stands) on a bounded sample: nq CSA+HCA queries of the
+    same workload at position t (index keys, top-k and attention per query)."""
+    from long_context_compressed_02_amd import synth
+    from oracle import oracle as O
+    oc = O.OCfg(**w.shape())
+    n = (t + 1) // 4
+    nh = (t + 1) // 128
+    q, qI, wt = synth.decode_queries(w, nq, sub=777)
+    qh, _, _ = synth.decode_queries(w, nq, sub=778)
+    sinks = synth.sinks(w)
+    prep = []
+    for r in range(nq):
+        prep.append(dict(keys_raw=synth.index_keys(w, r, n), ent_raw=synth.entries(w, r, n, 0),
+                         hca_raw=synth.entries(w, r, nh, 1), win=synth.window_tokens(w, r, 128, 0)[0],
+                         winh=synth.window_tokens(w, r, 128, 1)[0]))
+    t0 = time.time()
+    for r in range(nq):
+        p = prep[r]
+        keys = O.store_index_rows(p["keys_raw"], oc)
+        idx, _ = O.csa_select(t, qI[r], wt[r].astype(np.float64), keys, oc)
+        sel = [int(j) for j in idx if j >= 0]
+        ents = O.entries_from_values("csa", p["ent_raw"][sel], sel, oc)
+        win = O.window_records(p["win"], np.arange(t - 127, t + 1), oc)
+        O.attend(O.query_rot(q[r], t, oc), sinks, np.concatenate([ents, win]), oc.tau)
+        hents = O.entries_from_values("hca", p["hca_raw"], range(nh), oc)
+        winh = O.window_records(p["winh"], np.arange(t - 127, t + 1), oc)
+        O.attend(O.query_rot(qh[r], t, oc), sinks, np.concatenate([hents, winh]), oc.tau)
+    el = time.time() - t0
+    return {"value": round(nq / el, 3), "unit": "queries/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{nq} queries of the same workload (CSA indexer over {n} keys + top-{oc.topk} + sparse MQA, "
+                      f"and HCA MQA over {nh}+128 records), fp64, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,328 @@
+/*
+ * dsv4attn.h -- C ABI of libdsv4attn.so: CSA/HCA compressed attention
+ * (block compressor, lightning-indexer scoring, top-k, single-KV-head MQA with
+ * a raw sliding window and per-head sink) for AMD MI355X (gfx950).
+ *
+ * Sources for what each call computes (pages as published, sections named):
+ *  - vastsailsolution.com article on the DeepSeek-V4 report: section
+ *    "CSA -- compressed sparse attention" (data flow: compressor every 4
+ *    tokens, lightning indexer producing index keys and scores, top-k of 512 /
+ *    1024 entries, MQA over them plus 128 raw window tokens), section "HCA --
+ *    heavily compressed attention" (compressor every 128 tokens, no indexer,
+ *    dense MQA), and the paragraphs after it: sliding window of the last 128
+ *    raw tokens and a learnable per-head sink logit added to the softmax
+ *    denominator; RoPE on only the last 64 dims of query and KV; KV cache with
+ *    BF16 RoPE dims and FP8 for the rest; a per-request "state cache" (window
+ *    tokens plus the not-yet-compressible tail) and a "classic cache" whose
+ *    blocks cover lcm(4,128)=128 raw tokens = 32 CSA entries + 1 HCA entry.
+ *  - rqlyzj.com "three paradigm innovations" article, section 01: the
+ *    overlapping compression windows and the learned weighted merge of a
+ *    block's tokens (no decompression).
+ *  - hwcomputing.csdn.net "DeepSeek V4 底层逻辑全解析", section 二 (CSA in three
+ *    steps with overlap; Top-512 Flash / Top-1024 Pro) and section 四 (batch
+ *    invariance: no split-KV; two decode kernels that agree bit for bit).
+ *  - m.youleyou.com article on batch invariance, section "what was
+ *    sacrificed": split-KV and split-K are dropped; attention decode has one
+ *    kernel for a saturated GPU and one for an unsaturated GPU with identical
+ *    results.
+ *
+ * Conventions (all entry points):
+ *  - Every function returns a dsv4_status.  Arguments are validated on the
+ *    host before anything is launched; a failed check launches nothing.
+ *  - The caller owns all memory.  Pointers named *_dev are device pointers
+ *    (hipMalloc / torch CUDA tensors); the library never allocates device
+ *    memory and never synchronises.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) in call order.
+ *  - Integer index arrays (req, pos, cu_seqlens, block tables, top-k lists)
+ *    are device-resident int32.  Their values are not visible to the host:
+ *    kernels skip (and leave untouched) any item whose request, position or
+ *    block id is out of range instead of faulting.
+ *  - Activations (kv, gate, kI, gI, q, qI, out) are row-major in the dtype
+ *    given by cfg->act_dtype (bf16 or fp32).  w and sinks are fp32.
+ *  - Device pointers must be 16-byte aligned; pools 256-byte aligned.
+ *  - The library keeps no state between calls (the optional kernel timers
+ *    below excepted).  Results are bitwise deterministic and independent of
+ *    the batch (size, order, co-batched requests) and of the decode policy.
+ */
+#ifndef DSV4ATTN_H
+#define DSV4ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dsv4_status;
+#define DSV4_OK 0
+#define DSV4_ERR_INVALID_ARG 1   /* bad pointer, size, or configuration value */
+#define DSV4_ERR_UNSUPPORTED 2   /* valid but not built (e.g. a head dim without a kernel) */
+#define DSV4_ERR_WORKSPACE 3     /* workspace missing or smaller than dsv4_workspace_bytes */
+#define DSV4_ERR_LAUNCH 4        /* a kernel launch failed (hipGetLastError) */
+#define DSV4_ERR_HIP 5           /* another HIP runtime error */
+
+/* layer kinds */
+#define DSV4_CSA 0
+#define DSV4_HCA 1
+
+/* storage formats */
+#define DSV4_STORE_FP32 0        /* records / index keys as fp32 (reference-precision mode) */
+#define DSV4_STORE_FP8 1         /* records: E4M3 non-RoPE dims + one fp32 scale + BF16 RoPE dims;
+                                    index keys / queries: E4M3 + one fp32 scale per row */
+
+/* activation dtypes */
+#define DSV4_DT_F32 0
+#define DSV4_DT_BF16 1
+
+/* decode kernel policy (the two kernels give bitwise identical results) */
+#define DSV4_POLICY_AUTO 0
+#define DSV4_POLICY_HI 1         /* one workgroup per query, all heads: for a saturated GPU */
+#define DSV4_POLICY_LO 2         /* one workgroup per (query, 16-head group): for an unsaturated GPU */
+
+/* cache-write targets */
+#define DSV4_TARGET_ENTRY 0
+#define DSV4_TARGET_INDEX_KEY 1
+
+/* Raw tokens covered by one classic-cache block: lcm(4, 128). */
+#define DSV4_BLOCK_TOKENS 128
+
+/*
+ * Layer configuration.  Defaults in brackets are the V4-Pro shape.
+ *   d            head dim of query and the single KV head                 [512]
+ *   d_rope       RoPE dims, the LAST d_rope of d (pairs (2i, 2i+1),
+ *                angle pos * rope_base^(-2i/d_rope))                      [64]
+ *   n_heads      query heads sharing the KV head, multiple of 16           [128]
+ *   window       raw sliding window W: query t sees tokens t-W+1 .. t      [128]
+ *   m_csa        CSA stride m (entries per block 128/m)                    [4]
+ *   w_csa        CSA compression window: entry j pools tokens
+ *                [m*j - (w_csa - m), m*j + m - 1] (clipped at 0);
+ *                w_csa is m (no overlap) or 2m (overlap with the previous block) [8]
+ *   m_hca        HCA stride m' = window (no overlap)                       [128]
+ *   idx_heads    lightning-indexer heads (<= 64)                           [64]
+ *   idx_dim      indexer head dim (multiple of 32, <= 128)                 [128]
+ *   topk         entries kept per CSA query (<= 2048)                      [1024]
+ *   kv_store     DSV4_STORE_FP8 (production) or DSV4_STORE_FP32
+ *   idx_store    DSV4_STORE_FP8 (production) or DSV4_STORE_FP32
+ *   act_dtype    DSV4_DT_BF16 or DSV4_DT_F32 for kv/gate/kI/gI/q/qI/out
+ *   rope_base    [10000]
+ *   softmax_scale tau in tau * q.k                                         [1/sqrt(d)]
+ * Built head shapes: (d, d_rope) = (512, 64) and (64, 16).
+ */
+typedef struct dsv4_cfg {
+    int32_t d, d_rope, n_heads, window;
+    int32_t m_csa, w_csa, m_hca;
+    int32_t idx_heads, idx_dim, topk;
+    int32_t kv_store, idx_store, act_dtype;
+    float rope_base, softmax_scale;
+} dsv4_cfg;
+
+/*
+ * One layer's cache (a CSA layer and an HCA layer each have one; they may
+ * share block_table).  All memory is caller-allocated, sizes from
+ * dsv4_get_layout.
+ *   kind         DSV4_CSA or DSV4_HCA
+ *   entries      classic cache: [n_blocks][entry_block_bytes]; block b holds the
+ *                128/m entries of the 128 raw tokens mapped to b, entry j of a
+ *                request at slot j mod (128/m) of block block_table[r][j*m/128]
+ *   index_keys   CSA only (NULL for HCA): [n_blocks][index_block_bytes], the
+ *                compressed index keys laid out like `entries`
+ *   state        state cache: [n_req][state_bytes] -- the W most recent raw
+ *                tokens as stored records (ring, slot = pos mod W) and the raw
+ *                tail tokens still needed by the compressor (ring of
+ *                pending_slots raw fp32 tokens, slot = pos mod pending_slots)
+ *   block_table  device int32 [n_req][max_blocks]: physical block id of the
+ *                b-th 128-token span of request r
+ */
+typedef struct dsv4_cache {
+    int32_t kind;
+    int32_t n_req, max_blocks, n_blocks;
+    void *entries;
+    void *index_keys;
+    void *state;
+    const int32_t *block_table;
+} dsv4_cache;
+
+/*
+ * Byte layout of one layer's cache.
+ *  KV record (DSV4_STORE_FP8): bytes [0, d-d_rope) E4M3 codes of the non-RoPE
+ *    dims, then d_rope BF16 values (post-RoPE), then one fp32 scale; the value
+ *    of a code c is E4M3(c) * scale.  Padded to record_bytes (multiple of 64).
+ *  KV record (DSV4_STORE_FP32): d fp32 values (post-RoPE).
+ *  Index block: entries_per_block keys of index_key_bytes (E4M3 or fp32)
+ *    back to back, then (FP8 only) entries_per_block fp32 scales.
+ *  State (per request): window ring of `window` records at offset 0, pending
+ *    ring at pending_offset: pending_slots raw tokens, each
+ *    [kv d][gate d][kI idx_dim][gI idx_dim] fp32 (kI, gI for CSA only).
+ */
+typedef struct dsv4_layout {
+    int64_t record_bytes;
+    int64_t entries_per_block;
+    int64_t entry_block_bytes;
+    int64_t index_key_bytes;
+    int64_t index_block_bytes;
+    int64_t state_bytes;
+    int64_t pending_offset;
+    int64_t pending_slots;
+    int64_t pending_token_floats;
+} dsv4_layout;
+
+const char *dsv4_status_string(dsv4_status s);
+
+/* Validate cfg for a layer kind and fill *out.  DSV4_ERR_INVALID_ARG for values
+ * outside the documented ranges, DSV4_ERR_UNSUPPORTED for a head shape or
+ * storage mode without kernels. */
+dsv4_status dsv4_get_layout(const dsv4_cfg *cfg, int32_t kind, dsv4_layout *out);
+
+/* Workspace for dsv4_index_topk_{decode,prefill}: n_queries queries whose
+ * visible entry count is at most max_entries.  For the prefill call the
+ * library processes queries in groups that fit the workspace given, so any
+ * size >= dsv4_workspace_bytes(cfg, n_queries = 1, ...) is accepted. */
+dsv4_status dsv4_workspace_bytes(const dsv4_cfg *cfg, int32_t n_queries, int32_t max_entries,
+                                 int64_t *out);
+
+/*
+ * Append + compress, decode: one new token per request.
+ * Token b (position pos_dev[b], request req_dev[b]) is RoPE-rotated at its
+ * position, stored into the window ring, and pushed into the pending ring.  If
+ * it completes a block of the layer's stride (pos+1 divisible by m), the entry
+ * of that block is formed: per channel c, softmax over the block's tokens s of
+ * gate[s][c], weighted sum of kv[s][c]; RoPE at the block's last token; stored
+ * (FP8/BF16).  For a CSA layer the index key is formed the same way from
+ * (kI, gI), without RoPE.  Sources: vastsailsolution.com CSA/HCA sections and
+ * state/classic cache paragraph; rqlyzj.com section 01 (overlap, weighted
+ * merge).
+ *   kv, gate   [B][d] act dtype;  kI, gI [B][idx_dim] act dtype (CSA) or NULL (HCA)
+ *   req_dev    [B] request rows of the cache; pos_dev [B] new token positions
+ * Requests in one call must be distinct.  Run before the attention of the
+ * same step: the new token is visible to its own query.
+ */
+dsv4_status dsv4_compress_kv_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
+                                    const void *kv, const void *gate, const void *kI,
+                                    const void *gI, const int32_t *req_dev,
+                                    const int32_t *pos_dev, int32_t B, void *stream);
+
+/*
+ * Append + compress, prefill of a chunk per sequence (varlen).  Sequence i has
+ * tokens cu_seqlens_dev[i] .. cu_seqlens_dev[i+1]-1 of the packed inputs,
+ * request req_dev[i], first position pos0_dev[i] (= tokens already cached).
+ * Entries completed inside the chunk are formed exactly as in decode (bitwise
+ * identical to appending the same tokens one at a time); earlier tail tokens
+ * come from the state cache.  Afterwards the state cache holds the chunk's
+ * last window / tail tokens.
+ *   win_out_dev (required) receives the window records the chunk's queries
+ *   need, as stored records: for sequence i, (window + chunk_len_i) records
+ *   starting at record (cu_seqlens[i] + i*window) -- first the `window`
+ *   records of positions pos0-window .. pos0-1 (from the state cache; slots
+ *   for negative positions are left unspecified), then the chunk's tokens.
+ *   Size: (total_tokens + n_seq*window) * record_bytes.  Pass it to the
+ *   *_attend_prefill calls of the same chunk.
+ */
+dsv4_status dsv4_compress_kv_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache,
+                                     const void *kv, const void *gate, const void *kI,
+                                     const void *gI, const int32_t *cu_seqlens_dev,
+                                     const int32_t *req_dev, const int32_t *pos0_dev,
+                                     int32_t n_seq, int32_t total_tokens, void *win_out_dev,
+                                     void *stream);
+
+/*
+ * Lightning indexer + top-k, decode (CSA).  For query b at position t =
+ * pos_dev[b] over the visible entries j < floor((t+1)/m):
+ *   I[j] = sum_h w[b][h] * max(0, qI[b][h] . kI_j)
+ * with qI quantised like the index keys (E4M3, one scale per (query, head)),
+ * then the min(k, N) largest I by (score desc, index asc), written ascending
+ * to topk_dev[b][0..k), padded with -1.  Sources: vastsailsolution.com CSA
+ * section (indexer: query projected into ReLU index heads scored against the
+ * compressed index keys; top-k); xiaoyuzhoufm.com 1.1 (CSA applies DSA).
+ *   qI [B][idx_heads][idx_dim] act dtype;  w_dev [B][idx_heads] fp32 (NULL = all ones)
+ *   ws_dev / ws_bytes: workspace of at least
+ *   dsv4_workspace_bytes(cfg, B, max_blocks*128/m).
+ */
+dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
+                                   const void *qI, const float *w_dev, const int32_t *req_dev,
+                                   const int32_t *pos_dev, int32_t B, int32_t *topk_dev,
+                                   void *ws_dev, int64_t ws_bytes, void *stream);
+
+/* Same for the packed queries of a prefill chunk (positions pos0 + offset);
+ * topk_dev is [total_tokens][k]. */
+dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache,
+                                    const void *qI, const float *w_dev,
+                                    const int32_t *cu_seqlens_dev, const int32_t *req_dev,
+                                    const int32_t *pos0_dev, int32_t n_seq, int32_t total_tokens,
+                                    int32_t *topk_dev, void *ws_dev, int64_t ws_bytes,
+                                    void *stream);
+
+/*
+ * Sparse CSA attention, decode.  For query b (position t, request r), per head
+ * h, over A = {selected entries topk_dev[b][*] (valid, ascending)} followed by
+ * the window tokens max(0, t-W+1) .. t:
+ *   l_i = tau * qrot_h . v_i,  M = max(z_h, max l_i),
+ *   out_h = sum_i e^(l_i-M) v_i / (e^(z_h-M) + sum_i e^(l_i-M))
+ * where qrot is q rotated at t on its last d_rope dims and each stored record
+ * v_i serves as key and value.  Sources: vastsailsolution.com CSA section
+ * (MQA over selected entries + 128 raw window tokens) and sink paragraph.
+ *   q [B][n_heads][d] act dtype (un-rotated);  sinks_dev [n_heads] fp32;
+ *   out [B][n_heads][d] act dtype;  policy DSV4_POLICY_* (results identical).
+ */
+dsv4_status dsv4_csa_attend_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                   const int32_t *req_dev, const int32_t *pos_dev,
+                                   const int32_t *topk_dev, const float *sinks_dev, void *out,
+                                   int32_t B, int32_t policy, void *stream);
+
+/* Dense HCA attention, decode: as above over all complete HCA entries
+ * (j < floor((t+1)/m')) followed by the window.  Source: vastsailsolution.com
+ * HCA section (no indexer, no top-k, all entries with the window). */
+dsv4_status dsv4_hca_attend_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                   const int32_t *req_dev, const int32_t *pos_dev,
+                                   const float *sinks_dev, void *out, int32_t B, int32_t policy,
+                                   void *stream);
+
+/* Prefill variants: packed queries of a chunk (see dsv4_compress_kv_prefill for
+ * cu_seqlens/req/pos0), window records from win_dev (its win_out_dev). */
+dsv4_status dsv4_csa_attend_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                    const int32_t *cu_seqlens_dev, const int32_t *req_dev,
+                                    const int32_t *pos0_dev, int32_t n_seq, int32_t total_tokens,
+                                    const int32_t *topk_dev, const void *win_dev,
+                                    const float *sinks_dev, void *out, void *stream);
+dsv4_status dsv4_hca_attend_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                    const int32_t *cu_seqlens_dev, const int32_t *req_dev,
+                                    const int32_t *pos0_dev, int32_t n_seq, int32_t total_tokens,
+                                    const void *win_dev, const float *sinks_dev, void *out,
+                                    void *stream);
+
+/*
+ * Cache fill (benchmarks, tests, reloading a saved prefix).  Writes n entries
+ * (target DSV4_TARGET_ENTRY: a KV record, RoPE at the entry's block-end
+ * position m*j+m-1 then stored; DSV4_TARGET_INDEX_KEY: a CSA index key,
+ * stored) from fp32 values [n][dim].  Item i goes to request req_dev[i],
+ * entry entry_dev[i].  Items must address distinct entries.
+ */
+dsv4_status dsv4_cache_write_entries(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t target,
+                                     const int32_t *req_dev, const int32_t *entry_dev, int32_t n,
+                                     const float *values_dev, void *stream);
+
+/* Write raw tokens [pos0, pos0+n) of request `req` into its state cache (window
+ * ring and pending ring; only the last W resp. pending_slots tokens land), as
+ * the appends would have, without forming entries.  kv, gate [n][d] and
+ * kI, gI [n][idx_dim] (CSA; NULL for HCA) in the act dtype. */
+dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req,
+                                    int32_t pos0, int32_t n, const void *kv, const void *gate,
+                                    const void *kI, const void *gI, void *stream);
+
+/*
+ * Optional kernel timers (instrumentation; not thread-safe).  When enabled for
+ * a kernel id, every launch of that kernel is bracketed by HIP events on the
+ * launch stream; dsv4_timer_read synchronises on the last event and returns
+ * the summed elapsed milliseconds and launch count.
+ */
+#define DSV4_K_COMPRESS 0
+#define DSV4_K_INDEX_SCORE 1
+#define DSV4_K_TOPK 2
+#define DSV4_K_ATTEND 3
+#define DSV4_K_COUNT 4
+dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on);
+dsv4_status dsv4_timer_read(int32_t kernel_id, int32_t reset, double *total_ms, int64_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSV4ATTN_H */

@@ -1,0 +1,435 @@
+// api.cpp -- the C ABI of libdsv4attn: argument validation, layouts, dispatch
+// and the optional kernel timers.  Every check runs on the host before any
+// launch; a failed check launches nothing.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "launch.h"
+
+using namespace dsv4;
+
+namespace {
+
+bool pow2_divides_128(int v) { return v >= 1 && v <= 128 && (v & (v - 1)) == 0; }
+int64_t al(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+hipStream_t S(void *s) { return (hipStream_t)s; }
+
+// ---- timers
+struct TimerSlot {
+    bool on = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+    double total_ms = 0.0;
+    int64_t count = 0;
+};
+TimerSlot g_timers[DSV4_K_COUNT];
+std::mutex g_timer_mu;
+
+struct Timed {
+    int id;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timed(int id_, hipStream_t s_) : id(id_), s(s_) {
+        if (g_timers[id].on) {
+            hipEventCreate(&a);
+            hipEventCreate(&b);
+            hipEventRecord(a, s);
+        }
+    }
+    ~Timed() {
+        if (a) {
+            hipEventRecord(b, s);
+            std::lock_guard<std::mutex> lk(g_timer_mu);
+            g_timers[id].pending.emplace_back(a, b);
+        }
+    }
+};
+
+dsv4_status hip_status(hipError_t e) { return e == hipSuccess ? DSV4_OK : DSV4_ERR_LAUNCH; }
+
+dsv4_status check_cache(const Lay &L, const dsv4_cache *C, int kind) {
+    if (!C) return DSV4_ERR_INVALID_ARG;
+    if (C->kind != kind) return DSV4_ERR_INVALID_ARG;
+    if (C->n_req <= 0 || C->max_blocks <= 0 || C->n_blocks <= 0) return DSV4_ERR_INVALID_ARG;
+    if (!C->entries || !C->state || !C->block_table) return DSV4_ERR_INVALID_ARG;
+    if (kind == DSV4_CSA && !C->index_keys) return DSV4_ERR_INVALID_ARG;
+    if ((int64_t)C->max_blocks * kBlockTokens > (int64_t)1 << 30) return DSV4_ERR_INVALID_ARG;
+    if (((uintptr_t)C->entries | (uintptr_t)C->state) & 255) return DSV4_ERR_INVALID_ARG;
+    if (C->index_keys && ((uintptr_t)C->index_keys & 255)) return DSV4_ERR_INVALID_ARG;
+    (void)L;
+    return DSV4_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+int num_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            cus = prop.multiProcessorCount;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+bool pick_hi(int policy, int nq, int nhg) {
+    // HI needs whole 64-head workgroups; otherwise LO runs (same results)
+    if (nhg % 4 != 0) return false;
+    if (policy == DSV4_POLICY_HI) return true;
+    if (policy == DSV4_POLICY_LO) return false;
+    // a HI workgroup (64 heads of one query) occupies a CU; while there are
+    // fewer of them than CUs, LO spreads each query over nhg workgroups instead
+    return (int64_t)nq * (nhg / 4) >= num_cus();
+}
+
+}  // namespace
+
+namespace dsv4 {
+
+dsv4_status make_layout(const dsv4_cfg *c, int32_t kind, Lay *out) {
+    if (!c || !out) return DSV4_ERR_INVALID_ARG;
+    if (kind != DSV4_CSA && kind != DSV4_HCA) return DSV4_ERR_INVALID_ARG;
+    if (c->d <= 0 || c->d_rope <= 0 || c->d_rope > c->d || (c->d_rope & 1) || (c->d % 16) || (c->d_rope % 16))
+        return DSV4_ERR_INVALID_ARG;
+    if (c->n_heads < 1 || c->n_heads > 256) return DSV4_ERR_INVALID_ARG;
+    if (c->window < 0 || c->window > 1024) return DSV4_ERR_INVALID_ARG;
+    if (!pow2_divides_128(c->m_csa) || !(c->w_csa == c->m_csa || c->w_csa == 2 * c->m_csa))
+        return DSV4_ERR_INVALID_ARG;
+    if (!pow2_divides_128(c->m_hca)) return DSV4_ERR_INVALID_ARG;
+    if (c->idx_heads < 1 || c->idx_heads > 64) return DSV4_ERR_INVALID_ARG;
+    if (c->idx_dim < 32 || c->idx_dim > 128 || (c->idx_dim % 32)) return DSV4_ERR_INVALID_ARG;
+    if (c->topk < 1 || c->topk > 2048) return DSV4_ERR_INVALID_ARG;
+    if (c->kv_store != DSV4_STORE_FP8 && c->kv_store != DSV4_STORE_FP32) return DSV4_ERR_INVALID_ARG;
+    if (c->idx_store != DSV4_STORE_FP8 && c->idx_store != DSV4_STORE_FP32) return DSV4_ERR_INVALID_ARG;
+    if (c->act_dtype != DSV4_DT_F32 && c->act_dtype != DSV4_DT_BF16) return DSV4_ERR_INVALID_ARG;
+    if (!(c->rope_base > 0.0f) || !isfinite(c->rope_base)) return DSV4_ERR_INVALID_ARG;
+    if (!(c->softmax_scale > 0.0f) || !isfinite(c->softmax_scale)) return DSV4_ERR_INVALID_ARG;
+    const bool shape_built = (c->d == 512 && c->d_rope == 64) || (c->d == 64 && c->d_rope == 16);
+    if (!shape_built) return DSV4_ERR_UNSUPPORTED;
+    if (c->kv_store != DSV4_STORE_FP8 || c->idx_store != DSV4_STORE_FP8) return DSV4_ERR_UNSUPPORTED;
+
+    Lay L;
+    memset(&L, 0, sizeof(L));
+    L.kind = kind;
+    L.d = c->d;
+    L.dr = c->d_rope;
+    L.dn = c->d - c->d_rope;
+    L.H = c->n_heads;
+    L.W = c->window;
+    L.m = kind == DSV4_CSA ? c->m_csa : c->m_hca;
+    L.wc = kind == DSV4_CSA ? c->w_csa : c->m_hca;
+    L.epb = kBlockTokens / L.m;
+    L.kv_store = c->kv_store;
+    L.idx_store = c->idx_store;
+    L.act = c->act_dtype;
+    L.rope_base = c->rope_base;
+    L.tau = c->softmax_scale;
+    L.topk = c->topk;
+    if (c->kv_store == DSV4_STORE_FP8) {
+        L.rope_off = L.dn;
+        L.scale_off = L.dn + 2 * L.dr;
+        L.rec_bytes = (int)al(L.dn + 2 * L.dr + 4, 64);
+    } else {
+        L.rope_off = 0;
+        L.scale_off = 0;
+        L.rec_bytes = (int)al(4 * (int64_t)L.d, 64);
+    }
+    L.entry_block_bytes = (int64_t)L.epb * L.rec_bytes;
+    L.HI = c->idx_heads;
+    L.dI = c->idx_dim;
+    L.key_bytes = c->idx_store == DSV4_STORE_FP8 ? L.dI : 4 * L.dI;
+    L.key_scale_off = L.epb * L.key_bytes;
+    L.index_block_bytes = kind == DSV4_CSA ? al((int64_t)L.epb * L.key_bytes + (int64_t)L.epb * 4, 256) : 0;
+    L.pend_slots = L.wc;
+    L.pend_tok_floats = 2 * L.d + (kind == DSV4_CSA ? 2 * L.dI : 0);
+    L.pend_off = al((int64_t)L.W * L.rec_bytes, 256);
+    L.state_bytes = al(L.pend_off + (int64_t)L.pend_slots * L.pend_tok_floats * 4, 256);
+    *out = L;
+    return DSV4_OK;
+}
+
+}  // namespace dsv4
+
+extern "C" {
+
+const char *dsv4_status_string(dsv4_status s) {
+    switch (s) {
+        case DSV4_OK: return "ok";
+        case DSV4_ERR_INVALID_ARG: return "invalid argument";
+        case DSV4_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DSV4_ERR_WORKSPACE: return "workspace missing or too small";
+        case DSV4_ERR_LAUNCH: return "kernel launch failed";
+        case DSV4_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+dsv4_status dsv4_get_layout(const dsv4_cfg *cfg, int32_t kind, dsv4_layout *out) {
+    if (!out) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, kind, &L);
+    if (st != DSV4_OK) return st;
+    out->record_bytes = L.rec_bytes;
+    out->entries_per_block = L.epb;
+    out->entry_block_bytes = L.entry_block_bytes;
+    out->index_key_bytes = kind == DSV4_CSA ? L.key_bytes : 0;
+    out->index_block_bytes = L.index_block_bytes;
+    out->state_bytes = L.state_bytes;
+    out->pending_offset = L.pend_off;
+    out->pending_slots = L.pend_slots;
+    out->pending_token_floats = L.pend_tok_floats;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_workspace_bytes(const dsv4_cfg *cfg, int32_t n_queries, int32_t max_entries, int64_t *out) {
+    if (!out || n_queries < 0 || max_entries < 0) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, DSV4_CSA, &L);
+    if (st != DSV4_OK) return st;
+    *out = index_ws_bytes(L, n_queries, max_entries, nullptr, nullptr) + al((int64_t)n_queries * 8, 256);
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_compress_kv_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *kv,
+                                    const void *gate, const void *kI, const void *gI, const int32_t *req_dev,
+                                    const int32_t *pos_dev, int32_t B, void *stream) {
+    if (!cache) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, cache->kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, cache->kind)) != DSV4_OK) return st;
+    if (B < 0) return DSV4_ERR_INVALID_ARG;
+    if (B == 0) return DSV4_OK;
+    if (!kv || !gate || !req_dev || !pos_dev) return DSV4_ERR_INVALID_ARG;
+    if (cache->kind == DSV4_CSA && (!kI || !gI)) return DSV4_ERR_INVALID_ARG;
+    Timed tm(DSV4_K_COMPRESS, S(stream));
+    return hip_status(launch_compress_decode(L, *cache, kv, gate, kI, gI, req_dev, pos_dev, B, S(stream)));
+}
+
+dsv4_status dsv4_compress_kv_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *kv,
+                                     const void *gate, const void *kI, const void *gI,
+                                     const int32_t *cu_seqlens_dev, const int32_t *req_dev,
+                                     const int32_t *pos0_dev, int32_t n_seq, int32_t total_tokens,
+                                     void *win_out_dev, void *stream) {
+    if (!cache) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, cache->kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, cache->kind)) != DSV4_OK) return st;
+    if (n_seq < 0 || total_tokens < 0) return DSV4_ERR_INVALID_ARG;
+    if (n_seq == 0 || total_tokens == 0) return DSV4_OK;
+    if (!kv || !gate || !cu_seqlens_dev || !req_dev || !pos0_dev || !win_out_dev) return DSV4_ERR_INVALID_ARG;
+    if (cache->kind == DSV4_CSA && (!kI || !gI)) return DSV4_ERR_INVALID_ARG;
+    if (!aligned16(win_out_dev)) return DSV4_ERR_INVALID_ARG;
+    Timed tm(DSV4_K_COMPRESS, S(stream));
+    return hip_status(launch_compress_prefill(L, *cache, kv, gate, kI, gI, cu_seqlens_dev, req_dev, pos0_dev,
+                                              n_seq, total_tokens, (uint8_t *)win_out_dev, S(stream)));
+}
+
+static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, const void *qI, const float *w,
+                                     const int32_t *req_q, const int32_t *pos_q, int nq, int32_t *topk_dev,
+                                     uint8_t *ws, int64_t ws_bytes, hipStream_t s) {
+    const int64_t nmax = (int64_t)cache->max_blocks * L.epb;
+    IndexWs W;
+    const int64_t need = index_ws_bytes(L, nq, nmax, &W, ws);
+    if (need > ws_bytes) return DSV4_ERR_WORKSPACE;
+    if ((int64_t)W.s_max * L.topk > 16384) return DSV4_ERR_UNSUPPORTED;
+    hipError_t e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
+    if (e != hipSuccess) return DSV4_ERR_LAUNCH;
+    {
+        Timed tm(DSV4_K_INDEX_SCORE, s);
+        e = launch_score_decode(L, *cache, req_q, pos_q, nq, W, s);
+    }
+    if (e != hipSuccess) return DSV4_ERR_LAUNCH;
+    Timed tm(DSV4_K_TOPK, s);
+    return hip_status(launch_topk(L, *cache, req_q, pos_q, nq, W, topk_dev, s));
+}
+
+dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *qI,
+                                   const float *w_dev, const int32_t *req_dev, const int32_t *pos_dev,
+                                   int32_t B, int32_t *topk_dev, void *ws_dev, int64_t ws_bytes,
+                                   void *stream) {
+    Lay L;
+    dsv4_status st = make_layout(cfg, DSV4_CSA, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, DSV4_CSA)) != DSV4_OK) return st;
+    if (B < 0) return DSV4_ERR_INVALID_ARG;
+    if (B == 0) return DSV4_OK;
+    if (!qI || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
+    if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
+    return index_topk_common(L, cache, qI, w_dev, req_dev, pos_dev, B, topk_dev, (uint8_t *)ws_dev, ws_bytes,
+                             S(stream));
+}
+
+dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *qI,
+                                    const float *w_dev, const int32_t *cu_seqlens_dev, const int32_t *req_dev,
+                                    const int32_t *pos0_dev, int32_t n_seq, int32_t total_tokens,
+                                    int32_t *topk_dev, void *ws_dev, int64_t ws_bytes, void *stream) {
+    Lay L;
+    dsv4_status st = make_layout(cfg, DSV4_CSA, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, DSV4_CSA)) != DSV4_OK) return st;
+    if (n_seq < 0 || total_tokens < 0) return DSV4_ERR_INVALID_ARG;
+    if (n_seq == 0 || total_tokens == 0) return DSV4_OK;
+    if (!qI || !cu_seqlens_dev || !req_dev || !pos0_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
+    if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
+    // per-query (request, position) rows first, then groups of queries that fit
+    const int64_t rows_bytes = al((int64_t)total_tokens * 8, 256);
+    const int64_t nmax = (int64_t)cache->max_blocks * L.epb;
+    const int64_t per1 = index_ws_bytes(L, 1, nmax, nullptr, nullptr);
+    if (ws_bytes < rows_bytes + per1) return DSV4_ERR_WORKSPACE;
+    uint8_t *ws = (uint8_t *)ws_dev;
+    int32_t *req_q = (int32_t *)ws, *pos_q = req_q + total_tokens;
+    hipStream_t s = S(stream);
+    if (launch_expand_queries(cu_seqlens_dev, req_dev, pos0_dev, n_seq, total_tokens, req_q, pos_q, s) !=
+        hipSuccess)
+        return DSV4_ERR_LAUNCH;
+    int group = total_tokens;
+    while (group > 1 && rows_bytes + index_ws_bytes(L, group, nmax, nullptr, nullptr) > ws_bytes) group = (group + 1) / 2;
+    const int64_t qrow = (int64_t)L.HI * L.dI * (L.act == DSV4_DT_BF16 ? 2 : 4);
+    for (int q0 = 0; q0 < total_tokens; q0 += group) {
+        const int n = total_tokens - q0 < group ? total_tokens - q0 : group;
+        st = index_topk_common(L, cache, (const uint8_t *)qI + q0 * qrow, w_dev ? w_dev + (int64_t)q0 * L.HI : nullptr,
+                               req_q + q0, pos_q + q0, n, topk_dev + (int64_t)q0 * L.topk, ws + rows_bytes,
+                               ws_bytes - rows_bytes, s);
+        if (st != DSV4_OK) return st;
+    }
+    return DSV4_OK;
+}
+
+static dsv4_status attend_common(const dsv4_cfg *cfg, const dsv4_cache *cache, int kind, const void *q,
+                                 const int32_t *req, const int32_t *pos, const int32_t *cu, const int32_t *pos0,
+                                 int n_seq, int nq, const int32_t *topk, const void *win, const float *sinks,
+                                 void *out, int policy, bool prefill, void *stream) {
+    Lay L;
+    dsv4_status st = make_layout(cfg, kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, kind)) != DSV4_OK) return st;
+    if (nq < 0 || n_seq < 0) return DSV4_ERR_INVALID_ARG;
+    if (policy != DSV4_POLICY_AUTO && policy != DSV4_POLICY_HI && policy != DSV4_POLICY_LO)
+        return DSV4_ERR_INVALID_ARG;
+    if (nq == 0) return DSV4_OK;
+    if (!q || !sinks || !out || !req) return DSV4_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return DSV4_ERR_INVALID_ARG;
+    if (prefill && (!cu || !pos0 || n_seq == 0 || (L.W > 0 && !win))) return DSV4_ERR_INVALID_ARG;
+    if (!prefill && !pos) return DSV4_ERR_INVALID_ARG;
+    if (kind == DSV4_CSA && !topk) return DSV4_ERR_INVALID_ARG;
+    AttnArgs A;
+    memset(&A, 0, sizeof(A));
+    A.L = L;
+    A.C = *cache;
+    A.q = q;
+    A.req = req;
+    A.pos = pos;
+    A.cu = cu;
+    A.pos0 = pos0;
+    A.n_seq = n_seq;
+    A.topk = topk;
+    A.win = (const uint8_t *)win;
+    A.sinks = sinks;
+    A.out = out;
+    A.nq = nq;
+    A.nhg = (L.H + 15) / 16;
+    if (attend_list_max(L, *cache, kind == DSV4_CSA) * 4 > 96 * 1024) return DSV4_ERR_UNSUPPORTED;
+    const bool hi = pick_hi(policy, nq, A.nhg);
+    Timed tm(DSV4_K_ATTEND, S(stream));
+    return hip_status(launch_attend(A, kind == DSV4_CSA, prefill, hi, S(stream)));
+}
+
+dsv4_status dsv4_csa_attend_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                   const int32_t *req_dev, const int32_t *pos_dev, const int32_t *topk_dev,
+                                   const float *sinks_dev, void *out, int32_t B, int32_t policy, void *stream) {
+    return attend_common(cfg, cache, DSV4_CSA, q, req_dev, pos_dev, nullptr, nullptr, 0, B, topk_dev, nullptr,
+                         sinks_dev, out, policy, false, stream);
+}
+
+dsv4_status dsv4_hca_attend_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                   const int32_t *req_dev, const int32_t *pos_dev, const float *sinks_dev,
+                                   void *out, int32_t B, int32_t policy, void *stream) {
+    return attend_common(cfg, cache, DSV4_HCA, q, req_dev, pos_dev, nullptr, nullptr, 0, B, nullptr, nullptr,
+                         sinks_dev, out, policy, false, stream);
+}
+
+dsv4_status dsv4_csa_attend_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                    const int32_t *cu_seqlens_dev, const int32_t *req_dev, const int32_t *pos0_dev,
+                                    int32_t n_seq, int32_t total_tokens, const int32_t *topk_dev,
+                                    const void *win_dev, const float *sinks_dev, void *out, void *stream) {
+    return attend_common(cfg, cache, DSV4_CSA, q, req_dev, nullptr, cu_seqlens_dev, pos0_dev, n_seq, total_tokens,
+                         topk_dev, win_dev, sinks_dev, out, DSV4_POLICY_HI, true, stream);
+}
+
+dsv4_status dsv4_hca_attend_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *q,
+                                    const int32_t *cu_seqlens_dev, const int32_t *req_dev, const int32_t *pos0_dev,
+                                    int32_t n_seq, int32_t total_tokens, const void *win_dev,
+                                    const float *sinks_dev, void *out, void *stream) {
+    return attend_common(cfg, cache, DSV4_HCA, q, req_dev, nullptr, cu_seqlens_dev, pos0_dev, n_seq, total_tokens,
+                         nullptr, win_dev, sinks_dev, out, DSV4_POLICY_HI, true, stream);
+}
+
+dsv4_status dsv4_cache_write_entries(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t target,
+                                     const int32_t *req_dev, const int32_t *entry_dev, int32_t n,
+                                     const float *values_dev, void *stream) {
+    if (!cache) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, cache->kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, cache->kind)) != DSV4_OK) return st;
+    if (target != DSV4_TARGET_ENTRY && target != DSV4_TARGET_INDEX_KEY) return DSV4_ERR_INVALID_ARG;
+    if (target == DSV4_TARGET_INDEX_KEY && cache->kind != DSV4_CSA) return DSV4_ERR_INVALID_ARG;
+    if (n < 0) return DSV4_ERR_INVALID_ARG;
+    if (n == 0) return DSV4_OK;
+    if (!req_dev || !entry_dev || !values_dev) return DSV4_ERR_INVALID_ARG;
+    return hip_status(launch_write_entries(L, *cache, target, req_dev, entry_dev, n, values_dev, S(stream)));
+}
+
+dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t pos0,
+                                    int32_t n, const void *kv, const void *gate, const void *kI, const void *gI,
+                                    void *stream) {
+    if (!cache) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, cache->kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, cache->kind)) != DSV4_OK) return st;
+    if (req < 0 || req >= cache->n_req || pos0 < 0 || n < 0) return DSV4_ERR_INVALID_ARG;
+    if (n == 0) return DSV4_OK;
+    if (!kv || !gate) return DSV4_ERR_INVALID_ARG;
+    if (cache->kind == DSV4_CSA && (!kI || !gI)) return DSV4_ERR_INVALID_ARG;
+    return hip_status(launch_state_tokens(L, *cache, req, pos0, n, kv, gate, kI, gI, S(stream)));
+}
+
+dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on) {
+    if (kernel_id < 0 || kernel_id >= DSV4_K_COUNT) return DSV4_ERR_INVALID_ARG;
+    g_timers[kernel_id].on = on != 0;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_timer_read(int32_t kernel_id, int32_t reset, double *total_ms, int64_t *count) {
+    if (kernel_id < 0 || kernel_id >= DSV4_K_COUNT || !total_ms || !count) return DSV4_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    TimerSlot &t = g_timers[kernel_id];
+    dsv4_status st = DSV4_OK;
+    for (auto &pr : t.pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+            st = DSV4_ERR_HIP;
+        t.total_ms += ms;
+        t.count += 1;
+        hipEventDestroy(pr.first);
+        hipEventDestroy(pr.second);
+    }
+    t.pending.clear();
+    *total_ms = t.total_ms;
+    *count = t.count;
+    if (reset) {
+        t.total_ms = 0.0;
+        t.count = 0;
+    }
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// common.h -- internal layout and device helpers of libdsv4attn (gfx950).
+// Not part of the public ABI (include/dsv4attn.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsv4attn.h"
+
+namespace dsv4 {
+
+constexpr int kBlockTokens = DSV4_BLOCK_TOKENS;  // raw tokens per classic-cache block
+
+// Everything a kernel needs to address one layer's cache; built on the host
+// from (cfg, kind) and passed by value.
+struct Lay {
+    int kind;
+    int d, dr, dn;          // head dim, RoPE dims (the last dr), non-RoPE dims
+    int H, W;               // query heads, raw window
+    int m, wc;              // stride and compression window of this layer's compressor
+    int epb;                // entries per 128-token block
+    int rec_bytes;          // stored KV record stride
+    int rope_off;           // FP8 mode: byte offset of the bf16 RoPE dims
+    int scale_off;          // FP8 mode: byte offset of the fp32 scale
+    int64_t entry_block_bytes;
+    int HI, dI;             // indexer heads and dim (CSA)
+    int key_bytes;          // one stored index key
+    int key_scale_off;      // FP8 index keys: offset of the scales inside a block
+    int64_t index_block_bytes;
+    int64_t state_bytes;
+    int64_t pend_off;       // state: byte offset of the pending ring
+    int pend_slots;         // pending ring slots (= wc)
+    int pend_tok_floats;    // floats per pending token: kv d, gate d (+ kI dI, gI dI)
+    int topk;
+    int kv_store, idx_store, act;
+    float rope_base, tau;
+};
+
+// Host: validate a configuration and derive the layout.
+dsv4_status make_layout(const dsv4_cfg *cfg, int32_t kind, Lay *out);
+
+// ------------------------------------------------------------------ numerics
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> OCP E4M3 code, round to nearest even, saturating at +-448 (the
+// hardware conversion rounds to nearest even; inputs are clamped first so it
+// never sees an out-of-range value).
+__device__ __forceinline__ uint32_t fp8_code(float y) {
+    if (y != y) return 0x7fu;
+    y = fminf(fmaxf(y, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+}
+
+// Activation loads/stores in the configured dtype.
+__device__ __forceinline__ float load_act(const void *p, int64_t i, int act) {
+    if (act == DSV4_DT_BF16) return bf16_to_f32(((const uint16_t *)p)[i]);
+    return ((const float *)p)[i];
+}
+
+// cos/sin of pos * base^(-2i/dr): angle in fp64 so that large positions keep
+// full accuracy, result rounded to fp32.
+__device__ __forceinline__ void rope_cs(int64_t pos, int i, int dr, float base, float &c, float &s) {
+    double theta = pow((double)base, -2.0 * (double)i / (double)dr);
+    double ang = (double)pos * theta;
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    c = (float)cd;
+    s = (float)sd;
+}
+
+// Wave-wide reductions over the 64 lanes.  Max is exact (order-free); the sum
+// uses a fixed butterfly so every lane ends with the same bits.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// ------------------------------------------------------------------ cache addressing
+__device__ __forceinline__ int64_t block_id(const int32_t *bt, int max_blocks, int n_blocks, int r,
+                                            int64_t blk) {
+    if (blk < 0 || blk >= max_blocks) return -1;
+    int b = bt[(int64_t)r * max_blocks + blk];
+    return (b >= 0 && b < n_blocks) ? b : -1;
+}
+
+// Per-channel gated pooling of one compressor window: softmax over the
+// window's tokens of the gate logits, weighted sum of the values.  `get(s, &kv,
+// &g)` returns token s of the window (s = 0 .. n-1 in position order).  The
+// same operation sequence is used by the decode and prefill paths, so a
+// prefilled entry is bitwise equal to one built token by token.
+template <typename Get>
+__device__ __forceinline__ float pool_channel(int n, Get get) {
+    float mx = -INFINITY;
+    for (int s = 0; s < n; ++s) {
+        float v, g;
+        get(s, v, g);
+        mx = fmaxf(mx, g);
+    }
+    float den = 0.0f, num = 0.0f;
+    for (int s = 0; s < n; ++s) {
+        float v, g;
+        get(s, v, g);
+        float a = expf(g - mx);
+        den = den + a;
+        num = num + a * v;
+    }
+    return num / den;
+}
+
+}  // namespace dsv4

@@ -1,0 +1,60 @@
+// launch.h -- internal launchers shared between the kernel files and the C ABI.
+#pragma once
+#include "common.h"
+
+namespace dsv4 {
+
+hipError_t launch_compress_decode(const Lay &L, const dsv4_cache &C, const void *kv, const void *gate,
+                                  const void *kI, const void *gI, const int32_t *req,
+                                  const int32_t *pos, int B, hipStream_t s);
+hipError_t launch_compress_prefill(const Lay &L, const dsv4_cache &C, const void *kv, const void *gate,
+                                   const void *kI, const void *gI, const int32_t *cu,
+                                   const int32_t *req, const int32_t *pos0, int n_seq, int total,
+                                   uint8_t *win, hipStream_t s);
+hipError_t launch_write_entries(const Lay &L, const dsv4_cache &C, int target, const int32_t *req,
+                                const int32_t *ent, int n, const float *vals, hipStream_t s);
+hipError_t launch_state_tokens(const Lay &L, const dsv4_cache &C, int r, int64_t p0, int n,
+                               const void *kv, const void *gate, const void *kI, const void *gI,
+                               hipStream_t s);
+
+struct IndexWs {
+    uint8_t *q8;
+    float *wq;
+    float *scores;
+    int32_t *cand_idx;
+    uint32_t *cand_key;
+    int64_t ld;
+    int seg, s_max;
+};
+int topk_segment_len(int k, int64_t nmax);
+int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base);
+hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows, const IndexWs &ws,
+                          hipStream_t s);
+hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
+                               int n, const IndexWs &ws, hipStream_t s);
+hipError_t launch_topk(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos, int n,
+                       const IndexWs &ws, int32_t *out, hipStream_t s);
+hipError_t launch_expand_queries(const int32_t *cu, const int32_t *req, const int32_t *pos0, int n_seq,
+                                 int total, int32_t *req_q, int32_t *pos_q, hipStream_t s);
+
+struct AttnArgs {
+    Lay L;
+    dsv4_cache C;
+    const void *q;
+    const int32_t *req;     // decode
+    const int32_t *pos;     // decode
+    const int32_t *cu;      // prefill
+    const int32_t *pos0;    // prefill
+    int n_seq;
+    const int32_t *topk;    // CSA
+    const uint8_t *win;     // prefill window records
+    const float *sinks;
+    void *out;
+    int nq;
+    int nhg;                // head groups (ceil(H/16))
+};
+hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s);
+// Longest record list one attention query can have (sizes the per-query locator array in LDS).
+int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa);
+
+}  // namespace dsv4

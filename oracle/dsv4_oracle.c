@@ -29,11 +29,15 @@
  * those pins.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORC_API __attribute__((visibility("default")))
+
+/* Threads the parallel loops use (for reporting the CPU baseline). */
+ORC_API int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* Storage number formats.                                                   */

@@ -54,6 +54,7 @@ def lib():
         build()
         L = ctypes.CDLL(_SO)
         dp = ctypes.POINTER(ctypes.c_double)
+        L.orc_num_threads.restype = ctypes.c_int
         L.orc_e4m3_decode.restype = ctypes.c_double
         L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_encode.restype = ctypes.c_uint8
@@ -109,6 +110,10 @@ class OCfg:
 # ---------------------------------------------------------------------------
 # primitives
 # ---------------------------------------------------------------------------
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
 def e4m3_decode(code: int) -> float:
     return lib().orc_e4m3_decode(code)
 

@@ -1,0 +1,153 @@
+"""Test plumbing shared by the GPU parity tests: cache allocation, block tables,
+host-side decoding of the documented byte layouts, and tolerance checks.
+Nothing here implements the method; expected values come from oracle/."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from long_context_compressed_02_amd import binding as B
+from oracle import oracle as O
+
+DEV = "cuda"
+
+
+def cfgs(shape: dict, act=B.DSV4_DT_BF16, topk=None):
+    """The library's cfg and the oracle's cfg for the same shape."""
+    sh = dict(shape)
+    if topk is not None:
+        sh["topk"] = topk
+    lib_cfg = B.make_cfg(act_dtype=act, **sh)
+    ocfg = O.OCfg(**sh)
+    return lib_cfg, ocfg
+
+
+def block_table(ctx_tokens, extra_blocks=0, seed=0, max_blocks=None):
+    """Shuffled physical block ids: request r owns ceil((ctx_r+1)/128) blocks."""
+    need = [(c + 1 + 127) // 128 for c in ctx_tokens]
+    mb = max_blocks or max(need)
+    n_blocks = sum(need) + extra_blocks
+    perm = np.random.default_rng([99, seed]).permutation(n_blocks)
+    bt = np.full((len(ctx_tokens), mb), -1, dtype=np.int32)
+    k = 0
+    for r, n in enumerate(need):
+        bt[r, :n] = perm[k:k + n]
+        k += n
+    return torch.from_numpy(bt).to(DEV), n_blocks, mb
+
+
+def act_tensor(x: np.ndarray, act):
+    """Device activation tensor and the exact values it holds (float64)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if act == B.DSV4_DT_BF16:
+        t = t.to(torch.bfloat16)
+    return t.to(DEV), t.to(torch.float64).numpy()
+
+
+def i32(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.int32)).to(DEV)
+
+
+# ----------------------------------------------------------------- byte layouts
+def decode_records(raw: torch.Tensor, d: int, d_rope: int, rec_bytes: int) -> np.ndarray:
+    """Stored FP8/BF16 records (uint8 [n*rec_bytes]) -> float64 [n, d]."""
+    r = raw.view(-1, rec_bytes).cpu()
+    dn = d - d_rope
+    codes = r[:, :dn].contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    rope = r[:, dn:dn + 2 * d_rope].contiguous().view(torch.bfloat16).to(torch.float64)
+    scale = r[:, dn + 2 * d_rope:dn + 2 * d_rope + 4].contiguous().view(torch.float32).to(torch.float64)
+    return torch.cat([codes * scale, rope], dim=1).numpy()
+
+
+def decode_keys(raw_block: torch.Tensor, epb: int, d_i: int) -> np.ndarray:
+    """One index block -> float64 [epb, d_i]."""
+    r = raw_block.cpu()
+    codes = r[:epb * d_i].view(epb, d_i).contiguous().view(torch.float8_e4m3fn).to(torch.float64)
+    sc = r[epb * d_i:epb * d_i + 4 * epb].contiguous().view(torch.float32).to(torch.float64)
+    return (codes * sc[:, None]).numpy()
+
+
+def entry_rows(cache: B.LayerCache, r: int, js, bt_host) -> np.ndarray:
+    lay = cache.layout
+    cfg = cache.cfg
+    rows = []
+    for j in js:
+        blk = int(bt_host[r, (j * (128 // lay.entries_per_block)) // 128])
+        off = blk * lay.entry_block_bytes + (j % lay.entries_per_block) * lay.record_bytes
+        rows.append(cache.entries[off:off + lay.record_bytes])
+    return decode_records(torch.cat(rows), cfg.d, cfg.d_rope, lay.record_bytes)
+
+
+def key_rows(cache: B.LayerCache, r: int, js, bt_host) -> np.ndarray:
+    lay = cache.layout
+    cfg = cache.cfg
+    epb = lay.entries_per_block
+    out = []
+    blocks = {}
+    for j in js:
+        blk = int(bt_host[r, (j * (128 // epb)) // 128])
+        if blk not in blocks:
+            blocks[blk] = decode_keys(cache.index_keys[blk * lay.index_block_bytes:(blk + 1) * lay.index_block_bytes],
+                                      epb, cfg.idx_dim)
+        out.append(blocks[blk][j % epb])
+    return np.stack(out)
+
+
+def window_rows(cache: B.LayerCache, r: int, positions) -> np.ndarray:
+    lay = cache.layout
+    cfg = cache.cfg
+    base = r * lay.state_bytes
+    rows = [cache.state[base + (p % cfg.window) * lay.record_bytes: base + (p % cfg.window + 1) * lay.record_bytes]
+            for p in positions]
+    return decode_records(torch.cat(rows), cfg.d, cfg.d_rope, lay.record_bytes)
+
+
+# ----------------------------------------------------------------- comparisons
+def assert_records_close(got: np.ndarray, ref: np.ndarray, d_rope: int, max_flip_frac=2e-3, scale_rel=2e-6):
+    """Stored values agree up to the shared scale's last bits (the row's amax,
+    hence its fp32 scale, can differ by a few ulps when the stored vector was
+    computed -- pooled in fp32 on the GPU, fp64 in the oracle) except where the
+    two sides' pre-rounding values straddle a rounding boundary: then they
+    differ by one code step (E4M3: <= 2^-3 relative of the larger; BF16:
+    <= 2^-7 relative)."""
+    assert got.shape == ref.shape
+    dn = got.shape[1] - d_rope
+    diff = np.abs(got - ref) > scale_rel * np.maximum(np.abs(got), np.abs(ref))
+    frac = diff.mean()
+    assert frac <= max_flip_frac, f"{frac:.2e} of stored values differ"
+    if diff.any():
+        g, r = got[diff], ref[diff]
+        cols = np.nonzero(diff)[1]
+        step = np.where(cols < dn, 2.0 ** -3, 2.0 ** -7) * np.maximum(np.abs(g), np.abs(r))
+        # subnormal E4M3 codes: one step is 2^-9 * scale; bound by the row scale
+        scale = np.abs(ref[:, :dn]).max(axis=1, keepdims=True) / 448.0
+        sub = np.broadcast_to(scale, diff.shape)[diff] * 2.0 ** -9
+        assert (np.abs(g - r) <= np.maximum(step, sub) * 1.0001).all(), "a stored value is off by more than one step"
+
+
+def rel_err_per_head(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """max |got-ref| / max(max|ref|, 1e-6) per (query, head) over the head dim."""
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-6)
+    return num / den
+
+
+def topk_match(got: np.ndarray, ref: np.ndarray, scores: np.ndarray, k: int, band_rel=1e-6):
+    """Top-k sets agree except for indices whose oracle score is within
+    band_rel * max(1, |I_k|) of the oracle's k-th score.  Returns the number of
+    such tie swaps; asserts ordering / padding rules on the GPU list."""
+    g = got[got >= 0]
+    r = ref[ref >= 0]
+    assert len(g) == len(r), (len(g), len(r))
+    assert (np.diff(g) > 0).all(), "GPU list not strictly ascending"
+    assert (got[len(g):] == -1).all(), "padding must be -1 and at the end"
+    if len(r) == 0:
+        return 0
+    gs, rs = set(g.tolist()), set(r.tolist())
+    if gs == rs:
+        return 0
+    kth = np.sort(scores[r])[0] if len(r) else 0.0
+    band = band_rel * max(1.0, abs(kth))
+    for j in gs ^ rs:
+        assert abs(scores[j] - kth) <= band, f"index {j}: score {scores[j]!r} vs k-th {kth!r}"
+    return len(gs - rs)

@@ -1,0 +1,156 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function declared in include/dsv4attn.h, computes the documented layouts, and
+rejects bad arguments on the host with the documented status codes (nothing is
+launched on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_compressed_02_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsv4attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+FAKE = 1 << 20  # an aligned, never dereferenced address for host-only validation
+
+
+def declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsv4_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert len(names) >= 15
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_layout_production_shape():
+    cfg = B.make_cfg()
+    csa = B.dsv4_get_layout(cfg, B.DSV4_CSA)
+    hca = B.dsv4_get_layout(cfg, B.DSV4_HCA)
+    # record: 448 fp8 + 64 bf16 + fp32 scale = 580 B, padded to 640
+    assert csa.record_bytes == 640 and hca.record_bytes == 640
+    # a 128-token block holds 32 CSA entries and 1 HCA entry
+    assert csa.entries_per_block == 32 and hca.entries_per_block == 1
+    assert csa.entry_block_bytes == 32 * 640 and hca.entry_block_bytes == 640
+    assert csa.index_key_bytes == 128 and csa.index_block_bytes == 4352  # 32*128 + 32*4, 256-aligned
+    assert hca.index_block_bytes == 0
+    # state: window ring of 128 records + pending raw tokens (8 for CSA, 128 for HCA)
+    assert csa.pending_slots == 8 and hca.pending_slots == 128
+    assert csa.pending_token_floats == 2 * 512 + 2 * 128 and hca.pending_token_floats == 2 * 512
+    assert csa.pending_offset == 128 * 640
+    assert csa.state_bytes >= 128 * 640 + 8 * 1280 * 4
+
+
+def test_layout_tiny_shape():
+    cfg = B.make_cfg(d=64, d_rope=16, n_heads=8, window=16, idx_heads=4, idx_dim=32, topk=32)
+    lay = B.dsv4_get_layout(cfg, B.DSV4_CSA)
+    assert lay.record_bytes == 128 and lay.index_key_bytes == 32
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d", 0, B.DSV4_ERR_INVALID_ARG),
+    ("d_rope", 24, B.DSV4_ERR_INVALID_ARG),
+    ("d", 256, B.DSV4_ERR_UNSUPPORTED),
+    ("n_heads", 0, B.DSV4_ERR_INVALID_ARG),
+    ("window", -1, B.DSV4_ERR_INVALID_ARG),
+    ("m_csa", 3, B.DSV4_ERR_INVALID_ARG),
+    ("w_csa", 12, B.DSV4_ERR_INVALID_ARG),
+    ("m_hca", 100, B.DSV4_ERR_INVALID_ARG),
+    ("idx_heads", 65, B.DSV4_ERR_INVALID_ARG),
+    ("idx_dim", 48, B.DSV4_ERR_INVALID_ARG),
+    ("topk", 0, B.DSV4_ERR_INVALID_ARG),
+    ("topk", 4096, B.DSV4_ERR_INVALID_ARG),
+    ("act_dtype", 7, B.DSV4_ERR_INVALID_ARG),
+    ("softmax_scale", float("nan"), B.DSV4_ERR_INVALID_ARG),
+    ("rope_base", -1.0, B.DSV4_ERR_INVALID_ARG),
+])
+def test_invalid_config(field, value, status):
+    cfg = B.make_cfg()
+    setattr(cfg, field, value)
+    out = B.Layout()
+    assert B.lib().dsv4_get_layout(ctypes.byref(cfg), B.DSV4_CSA, ctypes.byref(out)) == status
+
+
+def _fake_cache(kind=B.DSV4_CSA, **kw):
+    c = B.Cache(kind, 4, 16, 64, FAKE, FAKE if kind == B.DSV4_CSA else None, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_compress_rejects_bad_arguments_before_launch():
+    L = B.lib()
+    cfg = B.make_cfg()
+    c = _fake_cache()
+    p = ctypes.c_void_p(FAKE)
+    # missing kv
+    assert L.dsv4_compress_kv_decode(ctypes.byref(cfg), ctypes.byref(c), None, p, p, p, p, p, 4, None) == 1
+    # CSA needs index inputs
+    assert L.dsv4_compress_kv_decode(ctypes.byref(cfg), ctypes.byref(c), p, p, None, None, p, p, 4, None) == 1
+    # negative batch
+    assert L.dsv4_compress_kv_decode(ctypes.byref(cfg), ctypes.byref(c), p, p, p, p, p, p, -1, None) == 1
+    # empty batch is a no-op
+    assert L.dsv4_compress_kv_decode(ctypes.byref(cfg), ctypes.byref(c), None, None, None, None, None, None, 0,
+                                     None) == 0
+    # cache kind mismatch / missing pools / unaligned pool
+    for bad in (dict(kind=5), dict(n_req=0), dict(index_keys=None), dict(entries=FAKE + 16), dict(state=None)):
+        cb = _fake_cache(**bad)
+        assert L.dsv4_compress_kv_decode(ctypes.byref(cfg), ctypes.byref(cb), p, p, p, p, p, p, 4, None) == 1
+    # prefill requires the window buffer
+    assert L.dsv4_compress_kv_prefill(ctypes.byref(cfg), ctypes.byref(c), p, p, p, p, p, p, p, 1, 10, None,
+                                      None) == 1
+
+
+def test_index_rejects_small_workspace():
+    L = B.lib()
+    cfg = B.make_cfg()
+    c = _fake_cache()
+    p = ctypes.c_void_p(FAKE)
+    need = B.dsv4_workspace_bytes(cfg, 4, 16 * 32)
+    assert need > 0
+    assert L.dsv4_index_topk_decode(ctypes.byref(cfg), ctypes.byref(c), p, p, p, p, 4, p, p, need - 4096,
+                                    None) == B.DSV4_ERR_WORKSPACE
+    assert L.dsv4_index_topk_decode(ctypes.byref(cfg), ctypes.byref(c), p, p, p, p, 4, p, None, need,
+                                    None) == B.DSV4_ERR_WORKSPACE
+    # HCA caches have no indexer
+    h = _fake_cache(B.DSV4_HCA)
+    assert L.dsv4_index_topk_decode(ctypes.byref(cfg), ctypes.byref(h), p, p, p, p, 4, p, p, need, None) == 1
+
+
+def test_attend_rejects_bad_arguments():
+    L = B.lib()
+    cfg = B.make_cfg()
+    c = _fake_cache()
+    h = _fake_cache(B.DSV4_HCA)
+    p = ctypes.c_void_p(FAKE)
+    # CSA needs a top-k list, bad policy, unaligned q
+    assert L.dsv4_csa_attend_decode(ctypes.byref(cfg), ctypes.byref(c), p, p, p, None, p, p, 4, 0, None) == 1
+    assert L.dsv4_hca_attend_decode(ctypes.byref(cfg), ctypes.byref(h), p, p, p, p, p, 4, 9, None) == 1
+    q_bad = ctypes.c_void_p(FAKE + 2)
+    assert L.dsv4_hca_attend_decode(ctypes.byref(cfg), ctypes.byref(h), q_bad, p, p, p, p, 4, 0, None) == 1
+    # prefill needs its window buffer
+    assert L.dsv4_hca_attend_prefill(ctypes.byref(cfg), ctypes.byref(h), p, p, p, p, 1, 8, None, p, p,
+                                     None) == 1
+    # write targets
+    assert L.dsv4_cache_write_entries(ctypes.byref(cfg), ctypes.byref(h), B.DSV4_TARGET_INDEX_KEY, p, p, 3, p,
+                                      None) == 1
+    assert L.dsv4_state_write_tokens(ctypes.byref(cfg), ctypes.byref(c), 4, 0, 3, p, p, p, p, None) == 1
+
+
+def test_status_strings_and_timers():
+    for s in range(6):
+        assert B.status_string(s)
+    assert B.lib().dsv4_timer_enable(99, 1) == 1
+    B.dsv4_timer_enable(B.DSV4_K_ATTEND, True)
+    assert B.dsv4_timer_read(B.DSV4_K_ATTEND) == (0.0, 0)
+    B.dsv4_timer_enable(B.DSV4_K_ATTEND, False)
