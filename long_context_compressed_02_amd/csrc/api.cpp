@@ -94,7 +94,8 @@ namespace dsv4 {
 dsv4_status make_layout(const dsv4_cfg *c, int32_t kind, Lay *out) {
     if (!c || !out) return DSV4_ERR_INVALID_ARG;
     if (kind != DSV4_CSA && kind != DSV4_HCA) return DSV4_ERR_INVALID_ARG;
-    if (c->d <= 0 || c->d_rope <= 0 || c->d_rope > c->d || (c->d_rope & 1) || (c->d % 16) || (c->d_rope % 16))
+    if (c->d <= 0 || c->d_rope <= 0 || c->d_rope > c->d || c->d_rope > 128 || (c->d_rope & 1) || (c->d % 16) ||
+        (c->d_rope % 16))
         return DSV4_ERR_INVALID_ARG;
     if (c->n_heads < 1 || c->n_heads > 256) return DSV4_ERR_INVALID_ARG;
     if (c->window < 0 || c->window > 1024) return DSV4_ERR_INVALID_ARG;
@@ -145,6 +146,8 @@ dsv4_status make_layout(const dsv4_cfg *c, int32_t kind, Lay *out) {
     L.key_bytes = c->idx_store == DSV4_STORE_FP8 ? L.dI : 4 * L.dI;
     L.key_scale_off = L.epb * L.key_bytes;
     L.index_block_bytes = kind == DSV4_CSA ? al((int64_t)L.epb * L.key_bytes + (int64_t)L.epb * 4, 256) : 0;
+    for (int i = 0; i < L.dr / 2 && i < 64; ++i)
+        L.theta[i] = pow((double)c->rope_base, -2.0 * (double)i / (double)L.dr);
     L.pend_slots = L.wc;
     L.pend_tok_floats = 2 * L.d + (kind == DSV4_CSA ? 2 * L.dI : 0);
     L.pend_off = al((int64_t)L.W * L.rec_bytes, 256);
@@ -238,7 +241,8 @@ static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, cons
     IndexWs W;
     const int64_t need = index_ws_bytes(L, nq, nmax, &W, ws);
     if (need > ws_bytes) return DSV4_ERR_WORKSPACE;
-    if ((int64_t)W.s_max * L.topk > 16384) return DSV4_ERR_UNSUPPORTED;
+    if ((int64_t)W.s_max * L.topk > 16384 || W.seg > 32768) return DSV4_ERR_UNSUPPORTED;
+    if (L.epb < 16) return DSV4_ERR_UNSUPPORTED;   // scoring reads 16-key runs inside one block
     hipError_t e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
     if (e != hipSuccess) return DSV4_ERR_LAUNCH;
     {
@@ -335,7 +339,7 @@ static dsv4_status attend_common(const dsv4_cfg *cfg, const dsv4_cache *cache, i
     A.out = out;
     A.nq = nq;
     A.nhg = (L.H + 15) / 16;
-    if (attend_list_max(L, *cache, kind == DSV4_CSA) * 4 > 96 * 1024) return DSV4_ERR_UNSUPPORTED;
+    if (attend_list_max(L, *cache, kind == DSV4_CSA) * 4 > kAttendMaxLocBytes) return DSV4_ERR_UNSUPPORTED;
     const bool hi = pick_hi(policy, nq, A.nhg);
     Timed tm(DSV4_K_ATTEND, S(stream));
     return hip_status(launch_attend(A, kind == DSV4_CSA, prefill, hi, S(stream)));

@@ -33,6 +33,7 @@ struct Lay {
     int topk;
     int kv_store, idx_store, act;
     float rope_base, tau;
+    double theta[64];       // RoPE frequencies base^(-2i/dr), i < dr/2 (fp64, from the host)
 };
 
 // Host: validate a configuration and derive the layout.
@@ -63,19 +64,22 @@ __device__ __forceinline__ float load_act(const void *p, int64_t i, int act) {
     return ((const float *)p)[i];
 }
 
-// cos/sin of pos * base^(-2i/dr): angle in fp64 so that large positions keep
-// full accuracy, result rounded to fp32.
-__device__ __forceinline__ void rope_cs(int64_t pos, int i, int dr, float base, float &c, float &s) {
-    double theta = pow((double)base, -2.0 * (double)i / (double)dr);
-    double ang = (double)pos * theta;
-    double sd, cd;
-    sincos(ang, &sd, &cd);
-    c = (float)cd;
-    s = (float)sd;
+// cos/sin of the RoPE angle pos * theta_i.  The angle is formed and reduced
+// modulo 2*pi in fp64 (Cody-Waite with 2*pi split into three parts whose
+// products with the quotient are exact for positions below 2^26), so large
+// positions keep full accuracy; the reduced angle's sine and cosine are then
+// taken in fp32.
+__device__ __forceinline__ void rope_cs(const Lay &L, int64_t pos, int i, float &c, float &s) {
+    const double ang = (double)pos * L.theta[i];
+    const double kq = rint(ang * 0.15915494309189535);          // 1 / (2*pi)
+    double r = __fma_rn(-kq, 6.28318530717958623200e+00, ang);  // 2*pi, split in three parts
+    r = __fma_rn(-kq, 2.44929359829470641e-16, r);
+    r = __fma_rn(-kq, -5.97232958240207e-33, r);
+    sincosf((float)r, &s, &c);
 }
 
-// Wave-wide reductions over the 64 lanes.  Max is exact (order-free); the sum
-// uses a fixed butterfly so every lane ends with the same bits.
+// Wave-wide max over the 64 lanes (exact, so the order of the butterfly does
+// not matter).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -70,11 +70,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
     return x.b;
 }
 
-__device__ __forceinline__ __bf16 f2bf(float f) {
-    union { uint16_t u; __bf16 b; } x;
-    x.u = bf16_bits(f);
-    return x.b;
-}
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ __bf16 f2bf(float f) { return (__bf16)f; }
 
 struct QueryInfo {
     int r;
@@ -165,14 +162,20 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
     constexpr bool HI = G > 1;
     constexpr int RBW = 4 / R;                   // record blocks of S per wave
     constexpr int DN = D - DR;
-    constexpr int REC = ((DN + 2 * DR + 4) + 63) / 64 * 64;
-    constexpr int RS = REC + 16;                 // LDS row stride (16 B pad against bank conflicts)
-    constexpr int ROPE_OFF = DN, SCALE_OFF = DN + 2 * DR;
+    constexpr int REC = ((DN + 2 * DR + 4) + 63) / 64 * 64;   // stored record stride in HBM
+    // LDS row: the record dequantised to bf16 codes (E4M3 -> bf16 is exact; the
+    // scale stays separate): [DN bf16 | DR bf16 | fp32 scale | pad]
+    constexpr int ROPE_OFF = 2 * DN, SCALE_OFF = 2 * D;
+    constexpr int RS = (2 * D + 4 + 15) / 16 * 16 + 16;     // 16 B pad against bank conflicts
+    constexpr int NCH = DN / 16;                 // HBM chunks of E4M3 codes
+    constexpr int RCH = DR / 8;                  // HBM chunks of bf16 RoPE dims
+    constexpr int LCH = NCH + RCH + 1;           // chunks loaded per record (codes, RoPE, scale)
+    constexpr int SCALE_OFF_HBM = DN + 2 * DR;   // 16-byte aligned: DN, DR multiples of 16
+    static_assert(SCALE_OFF_HBM % 16 == 0, "scale chunk alignment");
     constexpr int KN = (DN + 31) / 32, KR = (DR + 31) / 32;
     constexpr int DBN = DN / 16, DBR = DR / 16, DB = DBN + DBR;
-    constexpr int CPR = REC / 16;                // 16-byte chunks per record
-    constexpr int CPT = kTile * CPR / NT;        // chunks per thread per tile
-    static_assert(kTile * CPR % NT == 0, "tile chunks must divide evenly");
+    constexpr int TPR = NT / kTile;              // loader threads per record
+    constexpr int CPT = (LCH + TPR - 1) / TPR;   // 16-byte chunks per thread per tile
     constexpr int DBW = (DB + R - 1) / R;        // dim blocks of O held per wave
 
     __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * RS];
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
     __syncthreads();
     if (tid < DR / 2) {
         float c, sn;
-        rope_cs(Q.t, tid, DR, L.rope_base, c, sn);
+        rope_cs(L, Q.t, tid, c, sn);
         rope_tab[tid] = make_float2(c, sn);
     }
     if (tid == 0) {
@@ -270,6 +273,8 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
     const int32_t safe = safe_sh;
 
     // ---- running softmax state (lane's head) and output accumulators O^T
+    // softmax in base 2: logits carry tau*log2(e), exp is v_exp_f32
+    const float tau2 = L.tau * 1.4426950408889634f;
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 O[DBW];
 #pragma unroll
@@ -277,15 +282,22 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
     const int db0 = role * DBW;
     const int64_t ntiles = (Q.n_list + kTile - 1) / kTile;
 
+    // loader: thread tid fetches chunks (tid % TPR) + TPR*i of record tid / TPR
+    const int ld_rec = tid / TPR, ld_c0 = tid % TPR;
     auto load = [&](uint4 (&pre)[CPT], int64_t tl) {
+        const int64_t p = tl * kTile + ld_rec;
+        int32_t lc = p < Q.n_list ? locs[p] : kMasked;
+        if (lc == kMasked) lc = safe;
+        if (lc == kMasked) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) pre[i] = make_uint4(0, 0, 0, 0);
+            return;
+        }
+        const uint4 *src = (const uint4 *)loc_addr<PREFILL>(A, Q, lc);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            const int64_t p = tl * kTile + c / CPR;
-            int32_t lc = p < Q.n_list ? locs[p] : kMasked;
-            if (lc == kMasked) lc = safe;
-            pre[i] = lc == kMasked ? make_uint4(0, 0, 0, 0)
-                                   : *(const uint4 *)(loc_addr<PREFILL>(A, Q, lc) + (c % CPR) * 16);
+            const int c = ld_c0 + i * TPR;
+            if (c < LCH) pre[i] = src[c < NCH + RCH ? c : (SCALE_OFF_HBM / 16)];
         }
     };
 
@@ -303,13 +315,8 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
 #pragma unroll
             for (int ks = 0; ks < KN; ++ks) {
                 const int d0 = ks * 32 + 8 * g;
-                bf16x8 a;
-                if (d0 < DN) {
-                    uint2 cw = *(const uint2 *)(row + d0);
-                    a = cvt8(cw.x, cw.y);
-                } else {
-                    a = as_bf16x8(make_uint4(0, 0, 0, 0));
-                }
+                bf16x8 a = as_bf16x8(make_uint4(0, 0, 0, 0));
+                if (d0 < DN) a = *(const bf16x8 *)(row + 2 * d0);
                 an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qn[ks], an, 0, 0, 0);
             }
 #pragma unroll
@@ -324,7 +331,7 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
             for (int i = 0; i < 4; ++i) {
                 const int rr = rb * 16 + 4 * g + i;
                 const float sc = *(const float *)(tile + rr * RS + SCALE_OFF);
-                const float z = L.tau * (sc * an[i] + ar[i]);
+                const float z = tau2 * (sc * an[i] + ar[i]);
                 out[i] = valid(rr) ? z : -INFINITY;
             }
         };
@@ -359,11 +366,11 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) p[rb][i] = 0.0f;
         } else {
-            alpha = expf(m_run - m_new);
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p[rb][i] = expf(lg[rb][i] - m_new);
+                for (int i = 0; i < 4; ++i) p[rb][i] = __builtin_amdgcn_exp2f(lg[rb][i] - m_new);
         }
         float ps = 0.0f;
 #pragma unroll
@@ -390,9 +397,7 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
                 Pn[j] = f2bf(p[rb][i] * sc);
                 Pr[j] = f2bf(p[rb][i]);
             }
-            // transpose-read addresses: lanes (2r, 2r+1) of group g -> record of row r
-            const int r8 = c16 >> 1, h8 = c16 & 1;
-            const int rec8 = ks * 32 + (r8 < 4 ? 4 * g + r8 : 16 + 4 * g + r8 - 4);
+            // transpose-read addresses: lanes 4r..4r+3 of group g -> record of row r
             const int r16 = c16 >> 2, q16 = c16 & 3;
             const int rec16a = ks * 32 + 4 * g + r16;
             const int rec16b = ks * 32 + 16 + 4 * g + r16;
@@ -400,32 +405,33 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
             for (int ii = 0; ii < DBW; ++ii) {
                 const int db = db0 + ii;
                 if (db >= DB) break;
-                if (db < DBN) {
-                    i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (lds_i32x2_p)(tile + rec8 * RS + db * 16 + h8 * 8));
-                    bf16x8 va = cvt8((uint32_t)w[0], (uint32_t)w[1]);
-                    O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, Pn, O[ii], 0, 0, 0);
-                } else {
-                    const int cb = (db - DBN) * 16 + 4 * q16;
-                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4_p)(tile + rec16a * RS + ROPE_OFF + 2 * cb));
-                    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4_p)(tile + rec16b * RS + ROPE_OFF + 2 * cb));
-                    union { i16x4 s[2]; bf16x8 b; } cv;
-                    cv.s[0] = lo;
-                    cv.s[1] = hi;
-                    O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Pr, O[ii], 0, 0, 0);
-                }
+                // dims db*16 .. db*16+15 of the bf16 row (non-RoPE dims first, then RoPE)
+                const int cb = db * 16 + 4 * q16;
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(tile + rec16a * RS + 2 * cb));
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(tile + rec16b * RS + 2 * cb));
+                union { i16x4 s[2]; bf16x8 b; } cv;
+                cv.s[0] = lo;
+                cv.s[1] = hi;
+                O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, db < DBN ? Pn : Pr, O[ii], 0, 0, 0);
             }
         }
     };
 
     auto step = [&](uint4 (&pre)[CPT], int64_t tl) {
         __syncthreads();                                   // previous tile fully consumed
+        uint8_t *row = tile + ld_rec * RS;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT;
-            *(uint4 *)(tile + (c / CPR) * RS + (c % CPR) * 16) = pre[i];
+            const int c = ld_c0 + i * TPR;
+            if (c < NCH) {                       // 16 codes -> 16 bf16
+                const bf16x8 lo8 = cvt8(pre[i].x, pre[i].y), hi8 = cvt8(pre[i].z, pre[i].w);
+                *(bf16x8 *)(row + 32 * c) = lo8;
+                *(bf16x8 *)(row + 32 * c + 16) = hi8;
+            } else if (c < NCH + RCH) {          // RoPE dims, already bf16
+                *(uint4 *)(row + ROPE_OFF + 16 * (c - NCH)) = pre[i];
+            } else if (c == NCH + RCH) {         // scale
+                *(float *)(row + SCALE_OFF) = __uint_as_float(pre[i].x);
+            }
         }
         __syncthreads();                                   // tile visible
         if (tl + 2 < ntiles) load(pre, tl + 2);            // two tiles in flight during compute
@@ -442,10 +448,10 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
 
     // ---- sink and normalisation; output rows d = db*16 + 4g + i of head `head`
     if (!head_ok) return;
-    const float z = A.sinks[head];
+    const float z = A.sinks[head] * 1.4426950408889634f;
     const float M = fmaxf(m_run, z);
-    const float f = (m_run == -INFINITY) ? 0.0f : expf(m_run - M);
-    const float den = l_run * f + ((z == -INFINITY) ? 0.0f : expf(z - M));
+    const float f = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    const float den = l_run * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
     const float cf = den > 0.0f ? f / den : 0.0f;
     const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
 #pragma unroll
@@ -454,9 +460,9 @@ __global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
         if (db >= DB) break;
         const int dd = db * 16 + 4 * g;
         if (L.act == DSV4_DT_BF16) {
-            uint32_t w0 = (uint32_t)bf16_bits(O[ii][0] * cf) | ((uint32_t)bf16_bits(O[ii][1] * cf) << 16);
-            uint32_t w1 = (uint32_t)bf16_bits(O[ii][2] * cf) | ((uint32_t)bf16_bits(O[ii][3] * cf) << 16);
-            *(uint2 *)((uint16_t *)A.out + obase + dd) = make_uint2(w0, w1);
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 v = {f2bf(O[ii][0] * cf), f2bf(O[ii][1] * cf), f2bf(O[ii][2] * cf), f2bf(O[ii][3] * cf)};
+            *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
         } else {
             *(float4 *)((float *)A.out + obase + dd) =
                 make_float4(O[ii][0] * cf, O[ii][1] * cf, O[ii][2] * cf, O[ii][3] * cf);
@@ -473,8 +479,9 @@ template <int D, int DR, int G, int R, bool CSA, bool PREFILL>
 static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
     static bool attr = false;
     if (!attr) {
-        hipFuncSetAttribute((const void *)k_attend<D, DR, G, R, CSA, PREFILL>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+        hipError_t e = hipFuncSetAttribute((const void *)k_attend<D, DR, G, R, CSA, PREFILL>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kAttendMaxLocBytes);
+        if (e != hipSuccess) return e;
         attr = true;
     }
     const size_t lds = (size_t)attend_list_max(A.L, A.C, CSA) * 4;

@@ -36,7 +36,7 @@ __device__ void store_record(const Lay &L, float (&x)[(D / 64) > 0 ? D / 64 : 1]
             int dd = d0 + v;
             if (dd >= DN) {
                 float c, s;
-                rope_cs(pos, (dd - DN) / 2, DR, L.rope_base, c, s);
+                rope_cs(L, pos, (dd - DN) / 2, c, s);
                 float a = x[v], b = x[v + 1];
                 x[v] = a * c - b * s;
                 x[v + 1] = a * s + b * c;
@@ -46,7 +46,7 @@ __device__ void store_record(const Lay &L, float (&x)[(D / 64) > 0 ? D / 64 : 1]
         float other = __shfl_xor(x[0], 1);
         if (d0 >= DN) {
             float c, s;
-            rope_cs(pos, (d0 - DN) / 2, DR, L.rope_base, c, s);
+            rope_cs(L, pos, (d0 - DN) / 2, c, s);
             if ((lane & 1) == 0) x[0] = x[0] * c - other * s;
             else x[0] = other * s + x[0] * c;
         }

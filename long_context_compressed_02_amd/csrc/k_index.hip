@@ -24,6 +24,7 @@ namespace dsv4 {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- query quantisation
 // One wave per (query, head) row: E4M3 codes (zero-padded to 128 bytes) and
@@ -49,78 +50,118 @@ __global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, co
 }
 
 // ---------------------------------------------------------------- decode scoring
-// grid: (ceil(Nmax / 256), n_queries); block 256 = 4 waves x 64 keys.
+// grid: (ceil(Nmax / kKeysPerWG), n_queries); block 256 = 4 waves, each
+// streaming kKeysPerWave keys as 16-key sub-blocks, loads for the next group of
+// four sub-blocks in flight while the current group is on the MFMA.
+constexpr int kKeysPerWave = 256;
+constexpr int kKeysPerWG = 4 * kKeysPerWave;
+
+// HB: 16-row blocks of index heads (idx_heads <= 16*HB); FULL: idx_dim == 128
+// (no padded operand bytes).  Both are compile-time so that the loads and the
+// four MFMAs of a sub-block are straight-line code the compiler can pipeline.
+template <int HB, bool FULL>
 __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C, const uint8_t *q8,
                                                             const float *wq, const int32_t *req,
                                                             const int32_t *pos, float *scores,
                                                             int64_t ld) {
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);    // wave-uniform (scalar)
     const int r = req[q];
-    const int64_t t = pos[q];
-    if (r < 0 || r >= C.n_req || t < 0 || t >= (int64_t)C.max_blocks * kBlockTokens) return;
-    const int64_t N = (t + 1) / L.m;
-    const int64_t k0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+    const int t = pos[q];
+    if (r < 0 || r >= C.n_req || t < 0 || (int64_t)t >= (int64_t)C.max_blocks * kBlockTokens) return;
+    const int N = (t + 1) / L.m;
+    const int k0 = (blockIdx.x * 4 + wave) * kKeysPerWave;
     if (k0 >= N) return;
-    const int HB = (L.HI + 15) >> 4;
     const int dI = L.dI;
-    // A operand: query codes, rows = index heads
-    i32x8 A[4];
-    float wl[4][4];
+    // k-order of the 16x16x128 operands: lane group g holds bytes [16g, 16g+16)
+    // and [64+16g, 64+16g+16) of a row, so each 16-byte load instruction of a
+    // wave reads 64 contiguous bytes of every key row (same order on both sides).
+    const int o0 = 16 * g, o1 = 64 + 16 * g;
+    const bool v0 = FULL || o0 < dI, v1 = FULL || o1 < dI;   // chunks holding real bytes
+    const i32x4 z4 = {0, 0, 0, 0};
+    // A operand: query codes (zero-padded to 128 bytes per row), rows = index heads
+    i32x8 A[HB];
+    float wl[HB][4];
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
         const int row = hb * 16 + c16;
-        if (hb < HB && row < L.HI && 32 * g < dI) {
-            const uint4 *p = (const uint4 *)(q8 + ((int64_t)q * L.HI + row) * 128 + 32 * g);
-            uint4 u0 = p[0], u1 = p[1];
-            A[hb] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-        } else {
-            A[hb] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        const bool ok = row < L.HI;
+        const uint8_t *p = q8 + ((int64_t)q * L.HI + (ok ? row : 0)) * 128;
+        i32x8 a;
+        a.lo = *(const i32x4 *)(p + o0);
+        a.hi = *(const i32x4 *)(p + o1);
+        A[hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int h = hb * 16 + 4 * g + i;
-            wl[hb][i] = (hb < HB && h < L.HI) ? wq[(int64_t)q * L.HI + h] : 0.0f;
+            wl[hb][i] = h < L.HI ? wq[(int64_t)q * L.HI + h] : 0.0f;
         }
     }
-    // B operands: 4 sub-blocks of 16 keys, loaded up front (8 x 16 B in flight per lane)
-    i32x8 Bk[4];
-    float sk[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-        const int64_t j = k0 + sb * 16 + c16;
-        Bk[sb] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-        sk[sb] = 0.0f;
-        if (j < N) {
-            int64_t bid = block_id(C.block_table, C.max_blocks, C.n_blocks, r, (j * L.m) / kBlockTokens);
-            if (bid >= 0) {
-                const uint8_t *blk = (const uint8_t *)C.index_keys + bid * L.index_block_bytes;
-                const int slot = (int)(j % L.epb);
-                if (32 * g < dI) {
-                    const uint4 *p = (const uint4 *)(blk + (int64_t)slot * L.key_bytes + 32 * g);
-                    uint4 u0 = p[0], u1 = p[1];
-                    Bk[sb] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                }
-                sk[sb] = ((const float *)(blk + L.key_scale_off))[slot];
-            }
+    const int32_t *btr = C.block_table + (int64_t)r * C.max_blocks;
+    const int lane_off = c16 * L.key_bytes;
+    const uint8_t *pool = (const uint8_t *)C.index_keys;
+    // B operands: 16-key sub-blocks, each inside one 128-token cache block, so
+    // its block lookup is a wave-uniform scalar load; lane = key (c16).  An
+    // unmapped block reads block 0 and is masked by its zero scale.
+    auto load_sb = [&](int kb, i32x8 &Bk, float &sk) {
+        const int kc = kb < N ? kb : k0;                       // stay in mapped memory past the end
+        const int bid = __builtin_amdgcn_readfirstlane(btr[(kc * L.m) / kBlockTokens]);
+        const bool okb = bid >= 0 && bid < C.n_blocks && kb < N;
+        const uint8_t *base = pool + (int64_t)(okb ? bid : 0) * L.index_block_bytes;
+        const int slot0 = kc % L.epb;
+        const uint8_t *p = base + slot0 * L.key_bytes + lane_off;
+        if constexpr (FULL) {
+            Bk.lo = *(const i32x4 *)(p + o0);
+            Bk.hi = *(const i32x4 *)(p + o1);
+        } else {
+            // short keys: read inside the key (offset 0) and zero the padding
+            const i32x4 l0 = *(const i32x4 *)(p + (v0 ? o0 : 0));
+            const i32x4 l1 = *(const i32x4 *)(p + (v1 ? o1 : 0));
+            Bk.lo = v0 ? l0 : z4;
+            Bk.hi = v1 ? l1 : z4;
         }
-    }
+        const float s = ((const float *)(base + L.key_scale_off))[slot0 + c16];
+        sk = okb ? s : 0.0f;
+    };
+    float *srow = scores + (int64_t)q * ld;
+    auto score_sb = [&](int kb, const i32x8 &Bk, float sk) {
+        f32x4 acc[HB];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
+        for (int hb = 0; hb < HB; ++hb)
+            acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f},
+                                                                       0, 0, 0, 127, 0, 127);
         float part = 0.0f;
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-            if (hb < HB) {
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[hb], Bk[sb], acc, 0, 0, 0, 127, 0, 127);
+        for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part = part + fmaxf(acc[i], 0.0f) * wl[hb][i];
-            }
-        }
+            for (int i = 0; i < 4; ++i) part = part + fmaxf(acc[hb][i], 0.0f) * wl[hb][i];
         part = part + __shfl_xor(part, 16);
         part = part + __shfl_xor(part, 32);
-        const int64_t j = k0 + sb * 16 + c16;
-        if (g == 0 && j < N) scores[(int64_t)q * ld + j] = sk[sb] * part;
+        if (g == 0 && kb + c16 < N) srow[kb + c16] = sk * part;
+    };
+    constexpr int GS = 2;                          // sub-blocks per pipeline group
+    constexpr int NG = kKeysPerWave / 16 / GS;
+    i32x8 B0[GS], B1[GS];
+    float s0[GS], s1[GS];
+#pragma unroll
+    for (int i = 0; i < GS; ++i) load_sb(k0 + 16 * i, B0[i], s0[i]);
+#pragma unroll
+    for (int grp = 0; grp < NG; grp += 2) {
+        const int kg = k0 + grp * GS * 16;
+        if (kg >= N) break;                        // wave-uniform
+#pragma unroll
+        for (int i = 0; i < GS; ++i) load_sb(kg + GS * 16 + 16 * i, B1[i], s1[i]);
+#pragma unroll
+        for (int i = 0; i < GS; ++i) score_sb(kg + 16 * i, B0[i], s0[i]);
+        const int kh = kg + GS * 16;
+        if (kh >= N) break;
+        if (grp + 2 < NG) {
+#pragma unroll
+            for (int i = 0; i < GS; ++i) load_sb(kh + GS * 16 + 16 * i, B0[i], s0[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < GS; ++i) score_sb(kh + 16 * i, B1[i], s1[i]);
     }
 }
 
@@ -342,15 +383,23 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_merge(Lay L, const int32_
 
 static inline int64_t al256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-int topk_segment_len(int k, int64_t nmax) {
-    // LDS holds one segment of keys; the merge holds s_max * k keys + indices.
-    int seg = 16384;
-    while ((nmax + seg - 1) / seg * (int64_t)k > 16384 && seg < 32768) seg *= 2;
-    return seg;
+int topk_segment_len(int k, int64_t nmax, int nq, int cus) {
+    // One workgroup per segment; a query with more than one segment is merged
+    // from its segments' candidates (s_max * k <= 16384 keys in LDS).  Small
+    // batches use shorter segments so that the selection spreads over the CUs.
+    int64_t want = nq > 0 ? (cus + nq - 1) / nq : 1;
+    int64_t cap = 16384 / k;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    int64_t seg = (nmax + want - 1) / want;
+    seg = (seg + 1023) / 1024 * 1024;
+    if (seg < 4096) seg = 4096;
+    while ((nmax + seg - 1) / seg * (int64_t)k > 16384) seg += 1024;
+    return (int)seg;
 }
 
 int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base) {
-    const int seg = topk_segment_len(L.topk, nmax);
+    const int seg = topk_segment_len(L.topk, nmax, n, 256);
     const int s_max = nmax <= seg ? 1 : (int)((nmax + seg - 1) / seg);
     int64_t off = 0;
     int64_t o_q8 = off; off = al256(off + (int64_t)n * L.HI * 128);
@@ -405,8 +454,23 @@ hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows
 
 hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
                                int n, const IndexWs &ws, hipStream_t s) {
-    dim3 g((unsigned)((ws.ld + 255) / 256), n);
-    hipLaunchKernelGGL(k_index_score_decode, g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, ws.ld);
+    dim3 g((unsigned)((ws.ld + kKeysPerWG - 1) / kKeysPerWG), n);
+    const int hb = (L.HI + 15) / 16;
+    const bool full = L.dI == 128;
+#define DSV4_SCORE(HBV, FV) \
+    hipLaunchKernelGGL((k_index_score_decode<HBV, FV>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, ws.ld)
+    if (full) {
+        if (hb == 4) DSV4_SCORE(4, true);
+        else if (hb == 3) DSV4_SCORE(3, true);
+        else if (hb == 2) DSV4_SCORE(2, true);
+        else DSV4_SCORE(1, true);
+    } else {
+        if (hb == 4) DSV4_SCORE(4, false);
+        else if (hb == 3) DSV4_SCORE(3, false);
+        else if (hb == 2) DSV4_SCORE(2, false);
+        else DSV4_SCORE(1, false);
+    }
+#undef DSV4_SCORE
     return hipGetLastError();
 }
 
@@ -414,8 +478,11 @@ hipError_t launch_topk(const Lay &L, const dsv4_cache &C, const int32_t *req, co
                        const IndexWs &ws, int32_t *out, hipStream_t s) {
     static bool attr_done = false;
     if (!attr_done) {
-        hipFuncSetAttribute((const void *)k_topk_segment, hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * 4);
-        hipFuncSetAttribute((const void *)k_topk_merge, hipFuncAttributeMaxDynamicSharedMemorySize, 16384 * 8);
+        hipError_t e = hipFuncSetAttribute((const void *)k_topk_segment, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           32768 * 4);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)k_topk_merge, hipFuncAttributeMaxDynamicSharedMemorySize, 16384 * 8);
+        if (e != hipSuccess) return e;
         attr_done = true;
     }
     size_t lds = (size_t)ws.seg * 4;

@@ -26,7 +26,7 @@ struct IndexWs {
     int64_t ld;
     int seg, s_max;
 };
-int topk_segment_len(int k, int64_t nmax);
+int topk_segment_len(int k, int64_t nmax, int nq, int cus);
 int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base);
 hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows, const IndexWs &ws,
                           hipStream_t s);
@@ -55,6 +55,7 @@ struct AttnArgs {
 };
 hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s);
 // Longest record list one attention query can have (sizes the per-query locator array in LDS).
+constexpr int kAttendMaxLocBytes = 64 * 1024;
 int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa);
 
 }  // namespace dsv4
