@@ -252,6 +252,24 @@ dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
                                     void *stream);
 
 /*
+ * Exact top-k selection alone (the selection step of the two calls above), on
+ * caller-given fp32 rows.  Row i holds scores_dev[i*ld + j], j < n_dev[i]; its
+ * min(k, n) largest elements by (score desc, index asc) are written ascending
+ * to out_dev[i][0..k), padded with -1.  NaN ranks below every number, -0
+ * equals +0.  A row whose n lies outside [0, max_n] yields all -1.  Sources:
+ * vastsailsolution.com CSA section (keep the k most relevant entries).
+ *   scores_dev [n_rows][ld] fp32, ld >= max_n;  n_dev [n_rows] int32
+ *   k in [1, 2048];  max_n <= 2^30
+ *   ws_dev / ws_bytes: at least dsv4_topk_rows_ws_bytes(n_rows, max_n, k),
+ *   256-byte aligned.  Returns DSV4_ERR_UNSUPPORTED when max_n exceeds
+ *   4,194,304 (1024 segments of 4096).
+ */
+dsv4_status dsv4_topk_rows_ws_bytes(int32_t n_rows, int32_t max_n, int32_t k, int64_t *out);
+dsv4_status dsv4_topk_rows(const float *scores_dev, int64_t ld, const int32_t *n_dev, int32_t n_rows,
+                           int32_t max_n, int32_t k, int32_t *out_dev, void *ws_dev, int64_t ws_bytes,
+                           void *stream);
+
+/*
  * Sparse CSA attention, decode.  For query b (position t, request r), per head
  * h, over A = {selected entries topk_dev[b][*] (valid, ascending)} followed by
  * the window tokens max(0, t-W+1) .. t:

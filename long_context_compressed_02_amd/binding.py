@@ -32,7 +32,7 @@ EXPORTS = [
     "dsv4_compress_kv_prefill", "dsv4_index_topk_decode", "dsv4_index_topk_prefill",
     "dsv4_csa_attend_decode", "dsv4_hca_attend_decode", "dsv4_csa_attend_prefill",
     "dsv4_hca_attend_prefill", "dsv4_cache_write_entries", "dsv4_state_write_tokens",
-    "dsv4_timer_enable", "dsv4_timer_read",
+    "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows",
 ]
 
 
@@ -88,6 +88,8 @@ def lib():
             "dsv4_hca_attend_prefill": [cp, kp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp],
             "dsv4_cache_write_entries": [cp, kp, i32, vp, vp, i32, vp, vp],
             "dsv4_state_write_tokens": [cp, kp, i32, i32, i32, vp, vp, vp, vp, vp],
+            "dsv4_topk_rows_ws_bytes": [i32, i32, i32, ctypes.POINTER(i64)],
+            "dsv4_topk_rows": [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp],
             "dsv4_timer_enable": [i32, i32],
             "dsv4_timer_read": [i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         }
@@ -226,6 +228,19 @@ def dsv4_state_write_tokens(cfg, cache: LayerCache, req: int, pos0: int, kv, gat
                             stream=None):
     _ck("dsv4_state_write_tokens", lib().dsv4_state_write_tokens(
         ctypes.byref(cfg), ctypes.byref(cache.c), req, pos0, kv.shape[0], _p(kv), _p(gate), _p(kI), _p(gI),
+        _stream(stream)))
+
+
+def dsv4_topk_rows_ws_bytes(n_rows: int, max_n: int, k: int) -> int:
+    out = ctypes.c_int64()
+    _ck("dsv4_topk_rows_ws_bytes", lib().dsv4_topk_rows_ws_bytes(n_rows, max_n, k, ctypes.byref(out)))
+    return out.value
+
+
+def dsv4_topk_rows(scores, n, max_n: int, k: int, out, ws, stream=None):
+    """scores: fp32 [n_rows, ld] (row stride ld); n: int32 [n_rows]; out: int32 [n_rows, k]."""
+    _ck("dsv4_topk_rows", lib().dsv4_topk_rows(
+        _p(scores), scores.stride(0), _p(n), n.shape[0], max_n, k, _p(out), _p(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
 
 

@@ -241,7 +241,7 @@ static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, cons
     IndexWs W;
     const int64_t need = index_ws_bytes(L, nq, nmax, &W, ws);
     if (need > ws_bytes) return DSV4_ERR_WORKSPACE;
-    if ((int64_t)W.s_max * L.topk > 16384 || W.seg > 32768) return DSV4_ERR_UNSUPPORTED;
+    if (W.s_max > kTkMaxSeg) return DSV4_ERR_UNSUPPORTED;
     if (L.epb < 16) return DSV4_ERR_UNSUPPORTED;   // scoring reads 16-key runs inside one block
     hipError_t e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
     if (e != hipSuccess) return DSV4_ERR_LAUNCH;
@@ -264,6 +264,7 @@ dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
     if ((st = check_cache(L, cache, DSV4_CSA)) != DSV4_OK) return st;
     if (B < 0) return DSV4_ERR_INVALID_ARG;
     if (B == 0) return DSV4_OK;
+    if (B > kMaxGridRows) return DSV4_ERR_UNSUPPORTED;
     if (!qI || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
     if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
     return index_topk_common(L, cache, qI, w_dev, req_dev, pos_dev, B, topk_dev, (uint8_t *)ws_dev, ws_bytes,
@@ -294,6 +295,7 @@ dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
         hipSuccess)
         return DSV4_ERR_LAUNCH;
     int group = total_tokens;
+    if (group > kMaxGridRows) group = kMaxGridRows;
     while (group > 1 && rows_bytes + index_ws_bytes(L, group, nmax, nullptr, nullptr) > ws_bytes) group = (group + 1) / 2;
     const int64_t qrow = (int64_t)L.HI * L.dI * (L.act == DSV4_DT_BF16 ? 2 : 4);
     for (int q0 = 0; q0 < total_tokens; q0 += group) {
@@ -302,6 +304,43 @@ dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
                                req_q + q0, pos_q + q0, n, topk_dev + (int64_t)q0 * L.topk, ws + rows_bytes,
                                ws_bytes - rows_bytes, s);
         if (st != DSV4_OK) return st;
+    }
+    return DSV4_OK;
+}
+
+static void rows_layout(int k, Lay *L) {
+    memset(L, 0, sizeof(*L));
+    L->topk = k;
+    L->m = 1;
+}
+
+dsv4_status dsv4_topk_rows_ws_bytes(int32_t n_rows, int32_t max_n, int32_t k, int64_t *out) {
+    if (!out || n_rows < 0 || max_n < 0 || max_n > (1 << 30) || k < 1 || k > 2048) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    rows_layout(k, &L);
+    *out = index_ws_bytes(L, n_rows < kMaxGridRows ? n_rows : kMaxGridRows, max_n, nullptr, nullptr);
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_topk_rows(const float *scores_dev, int64_t ld, const int32_t *n_dev, int32_t n_rows,
+                           int32_t max_n, int32_t k, int32_t *out_dev, void *ws_dev, int64_t ws_bytes,
+                           void *stream) {
+    if (n_rows < 0 || max_n < 0 || max_n > (1 << 30) || k < 1 || k > 2048 || ld < max_n) return DSV4_ERR_INVALID_ARG;
+    if (n_rows == 0) return DSV4_OK;
+    if (!scores_dev || !n_dev || !out_dev) return DSV4_ERR_INVALID_ARG;
+    if (!ws_dev || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
+    Lay L;
+    rows_layout(k, &L);
+    IndexWs W;
+    const int chunk = n_rows < kMaxGridRows ? n_rows : kMaxGridRows;
+    if (index_ws_bytes(L, chunk, max_n, &W, (uint8_t *)ws_dev) > ws_bytes) return DSV4_ERR_WORKSPACE;
+    if (W.s_max > kTkMaxSeg) return DSV4_ERR_UNSUPPORTED;
+    Timed tm(DSV4_K_TOPK, S(stream));
+    for (int r0 = 0; r0 < n_rows; r0 += chunk) {
+        const int n = n_rows - r0 < chunk ? n_rows - r0 : chunk;
+        const hipError_t e = launch_topk_rows(scores_dev + (int64_t)r0 * ld, ld, n_dev + r0, n, max_n, k, W,
+                                              out_dev + (int64_t)r0 * k, S(stream));
+        if (e != hipSuccess) return DSV4_ERR_LAUNCH;
     }
     return DSV4_OK;
 }

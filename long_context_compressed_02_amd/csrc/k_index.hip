@@ -14,10 +14,12 @@
 // entries).
 //
 // Decode scoring is HBM-bound (132 B of key + scale per key and query): one
-// wave streams 64 keys straight into MFMA B-operand registers (no LDS), four
-// waves per workgroup, many workgroups per request.  Top-k is a deterministic
-// radix select (11/11/10-bit digits, exact integer histograms) followed by an
-// index-ordered compaction with wave ballots.
+// wave streams 256 keys straight into MFMA B-operand registers (no LDS), four
+// waves per workgroup, many workgroups per request.  Top-k is an exact
+// selection spread over 4096-score segments (histogram, boundary bin, split,
+// final merge), so one query's selection runs on many compute units.
+#include <string.h>
+
 #include "launch.h"
 
 namespace dsv4 {
@@ -49,6 +51,15 @@ __global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, co
     if (lane == 0) wq[row] = (w ? w[row] : 1.0f) * scale;
 }
 
+// Order-preserving key of a score: larger score -> larger key; -0 == +0; NaN
+// below everything.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (f != f) return 0u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ---------------------------------------------------------------- decode scoring
 // grid: (ceil(Nmax / kKeysPerWG), n_queries); block 256 = 4 waves, each
 // streaming kKeysPerWave keys as 16-key sub-blocks, loads for the next group of
@@ -63,7 +74,7 @@ template <int HB, bool FULL>
 __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C, const uint8_t *q8,
                                                             const float *wq, const int32_t *req,
                                                             const int32_t *pos, float *scores,
-                                                            int64_t ld) {
+                                                            int64_t ld, uint2 *wr, int nwr) {
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);    // wave-uniform (scalar)
@@ -125,6 +136,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
         sk = okb ? s : 0.0f;
     };
     float *srow = scores + (int64_t)q * ld;
+    uint32_t kmn = 0xffffffffu, kmx = 0u;          // key range of the finite scores this lane writes
     auto score_sb = [&](int kb, const i32x8 &Bk, float sk) {
         f32x4 acc[HB];
 #pragma unroll
@@ -138,7 +150,15 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
             for (int i = 0; i < 4; ++i) part = part + fmaxf(acc[hb][i], 0.0f) * wl[hb][i];
         part = part + __shfl_xor(part, 16);
         part = part + __shfl_xor(part, 32);
-        if (g == 0 && kb + c16 < N) srow[kb + c16] = sk * part;
+        if (g == 0 && kb + c16 < N) {
+            const float v = sk * part;
+            srow[kb + c16] = v;
+            if (fabsf(v) < INFINITY) {
+                const uint32_t u = score_key(v);
+                kmn = min(kmn, u);
+                kmx = max(kmx, u);
+            }
+        }
     };
     constexpr int GS = 2;                          // sub-blocks per pipeline group
     constexpr int NG = kKeysPerWave / 16 / GS;
@@ -163,261 +183,750 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
 #pragma unroll
         for (int i = 0; i < GS; ++i) score_sb(kh + 16 * i, B1[i], s1[i]);
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o));
+        kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o));
+    }
+    // every wave with keys records its extremes (kmx == 0: no finite score)
+    if (lane == 0) wr[(int64_t)q * nwr + k0 / kKeysPerWave] = make_uint2(kmn, kmx);
 }
 
 // ---------------------------------------------------------------- top-k
-// Order-preserving key of a score: larger score -> larger key; -0 == +0; NaN
-// below everything.
-__device__ __forceinline__ uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (f != f) return 0u;
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+// Exact selection of the min(k, N) largest scores of a query by (score desc,
+// index asc), emitted in ascending index order.  The score row is cut into
+// segments of kTkSeg scores and the selection runs in four launches, each
+// independent of how many queries share it:
+//   hist   per segment, a kTkBins histogram of its scores mapped linearly onto
+//          the query's finite score range (the scorer records each wave's
+//          extremes).  The map is monotone, so bins are ordered by score; NaN
+//          lies below every bin and +-inf fall into the end bins;
+//   bin    per query, the bin b* holding the k-th largest score, how many
+//          elements lie above it (all selected: "sure") and how many remain to
+//          be taken from inside it, plus each segment's output offsets;
+//   split  per segment, its sure indices and its candidates (elements of b*:
+//          key and index) written in index order at those offsets;
+//   final  per query, the exact threshold among the candidates (the rem-th
+//          largest key; ties go to the lower index) and a merge of the sure
+//          list with the chosen candidates.  When b* holds more than
+//          kTkCandMax elements the threshold is refined by radix passes over
+//          the query's whole score row instead, and the row is compacted
+//          directly.
+// Every count is an exact integer and every order is fixed, so the result is
+// unique.
+constexpr int kTkThreads = 256;
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkVec = kTkSeg / (kTkThreads * 4);    // float4 loads per thread and segment
+static_assert(kTkVec * kTkThreads * 4 == kTkSeg, "segment = whole float4 rows");
+static_assert(kTkBins == kTkThreads * 8, "eight bins per thread");
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-
-// Exclusive scan of one value per thread over the workgroup (fixed order).
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sh_w, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) sh_w[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t s = 0;
-        for (int w = 0; w < kTopkWaves; ++w) {
-            uint32_t c = sh_w[w];
-            sh_w[w] = s;
-            s += c;
-        }
-        *total = s;
-    }
-    __syncthreads();
-    uint32_t r = sh_w[wave] + x - v;
-    __syncthreads();
-    return r;
-}
-
-struct TopkShared {
-    uint32_t hist[2048];
-    uint32_t sh_w[kTopkWaves];
-    uint32_t wave_gt[kTopkWaves], wave_eq[kTopkWaves];
-    uint32_t wave_sel_base[kTopkWaves], wave_eq_base[kTopkWaves];
-    uint32_t total;
-    uint32_t found_bin, found_before;
+struct TkArgs {
+    Lay L;
+    const int32_t *req, *pos;
+    int n_req;
+    int64_t max_tokens;
+    IndexWs ws;
+    int32_t *out;
+    const int32_t *nvis;    // explicit row lengths (rows of given scores), else from req / pos
+    int64_t nvis_max;
 };
 
-// Select from keys[0..n) (LDS) the k largest by (key desc, position asc);
-// out_pos(i, p) is called for the i-th selected element (ascending position p).
-// Returns the number selected (min(k, n)).  Called by all threads.
-template <typename Out>
-__device__ int select_topk(const uint32_t *keys, int n, int k, TopkShared &S, Out out_pos) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (n <= k) {
-        for (int p = tid; p < n; p += kTopkThreads) out_pos(p, p);
-        return n;
+// Elements of row q: the visible compressed entries of query q, or the given
+// row length (0 for an invalid request / position / length).  Split in two so
+// that a kernel can issue the two loads together with its others and wait once.
+struct TkRowLen {
+    int32_t a, b;
+};
+__device__ __forceinline__ TkRowLen tk_fetch(const TkArgs &A, int q) {
+    const int32_t *pa = A.nvis ? A.nvis : A.req;
+    const int32_t *pb = A.nvis ? A.nvis : A.pos;
+    return TkRowLen{pa[q], pb[q]};
+}
+__device__ __forceinline__ int64_t tk_count(const TkArgs &A, TkRowLen v) {
+    if (A.nvis) return (v.a < 0 || (int64_t)v.a > A.nvis_max) ? 0 : v.a;
+    const int r = v.a;
+    const int64_t t = v.b;
+    if (r < 0 || r >= A.n_req || t < 0 || t >= A.max_tokens) return 0;
+    return (t + 1) / A.L.m;
+}
+__device__ __forceinline__ int64_t tk_visible(const TkArgs &A, int q) { return tk_count(A, tk_fetch(A, q)); }
+
+__device__ __forceinline__ int bit_length(uint32_t x) { return x ? 32 - __clz(x) : 0; }
+
+// Float value of an order-preserving key (key 0, the NaN key, is excluded by callers).
+__device__ __forceinline__ float key_value(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Linear map of [fmin, fmax] onto bins 0 .. kTkBins-1 (scale 0 when the range
+// is empty, a single value or not finite: every score then lands in bin 0).
+__device__ __forceinline__ void tk_map(uint32_t kmin, uint32_t kmax, float &fmin, float &scale) {
+    fmin = 0.0f;
+    scale = 0.0f;
+    if (kmax == 0u || kmin > kmax) return;
+    fmin = key_value(kmin);
+    const float range = key_value(kmax) - fmin;
+    if (range > 0.0f && range < INFINITY) scale = (float)(kTkBins - 1) / range;
+}
+
+// Bin of key u: -1 for NaN, else monotone non-decreasing in u.
+// (Selects only, no branches.)
+__device__ __forceinline__ int tk_digit(uint32_t u, float fmin, float scale) {
+    const float y = (key_value(u) - fmin) * scale;
+    // y <= 0 also catches -inf and the NaN products of scale 0
+    const float yc = y > 0.0f ? (y < (float)(kTkBins - 1) ? y : (float)(kTkBins - 1)) : 0.0f;
+    return u == 0u ? -1 : (int)yc;
+}
+
+// Wave-wide inclusive scan under an associative op with identity id, on the
+// DPP cross-lane paths (no LDS round trips): prefix within each row of 16
+// lanes by shifts of 1, 2, 4, 8, then the row totals carried into the rows
+// above (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op) {
+    const int i = (int)id;
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(i, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(i, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(i, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(i, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(i, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(i, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return x;
+}
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) { return wave_scan(x, 0u, OpAdd()); }
+__device__ __forceinline__ uint32_t wave_last(uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 63); }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) { return wave_last(wave_incl_scan(x)); }
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) { return wave_last(wave_scan(x, 0xffffffffu, OpMin())); }
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) { return wave_last(wave_scan(x, 0u, OpMax())); }
+
+// Exclusive prefix (thread order) of NV values per thread at once, and their
+// block totals.  wt: LDS scratch of NV * kTkWaves words.  Contains barriers.
+template <int NV>
+__device__ __forceinline__ void block_excl(uint32_t (&x)[NV], uint32_t (&tot)[NV], uint32_t *wt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        incl[v] = wave_incl_scan(x[v]);
+        if (lane == 63) wt[v * kTkWaves + wave] = incl[v];
     }
-    // radix select of the k-th largest key
-    uint32_t prefix = 0, pmask = 0, rem = (uint32_t)k;
-    const int shifts[3] = {21, 10, 0};
-    const int bitsv[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-        const int sh = shifts[pass], nb = 1 << bitsv[pass];
-        for (int b = tid; b < nb; b += kTopkThreads) S.hist[b] = 0;
-        __syncthreads();
-        for (int p = tid; p < n; p += kTopkThreads) {
-            uint32_t u = keys[p];
-            if ((u & pmask) == prefix) atomicAdd(&S.hist[(u >> sh) & (nb - 1)], 1u);
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        uint32_t base = 0, t = 0;
+#pragma unroll
+        for (int w = 0; w < kTkWaves; ++w) {
+            const uint32_t c = wt[v * kTkWaves + w];
+            base += w < wave ? c : 0u;
+            t += c;
         }
-        __syncthreads();
-        // counts from the top bin down: thread owns reversed bins [2*tid, 2*tid+2)
-        uint32_t c0 = 0, c1 = 0;
-        const int rb0 = 2 * tid, rb1 = 2 * tid + 1;
-        if (rb0 < nb) c0 = S.hist[nb - 1 - rb0];
-        if (rb1 < nb) c1 = S.hist[nb - 1 - rb1];
-        uint32_t before = block_exclusive_scan(c0 + c1, S.sh_w, &S.total);
-        if (rb0 < nb && before < rem && rem <= before + c0) {
-            S.found_bin = nb - 1 - rb0;
-            S.found_before = before;
-        }
-        if (rb1 < nb && before + c0 < rem && rem <= before + c0 + c1) {
-            S.found_bin = nb - 1 - rb1;
-            S.found_before = before + c0;
-        }
-        __syncthreads();
-        prefix |= S.found_bin << sh;
-        pmask |= (uint32_t)(nb - 1) << sh;
-        rem -= S.found_before;
-        __syncthreads();
+        x[v] = base + incl[v] - x[v];
+        tot[v] = t;
     }
-    const uint32_t T = prefix;
-    const uint32_t need_eq = rem;
-    // compaction in position order: each wave owns a contiguous chunk
-    const int chunk = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
-    const int lo = wave * chunk, hi = min(n, lo + chunk);
-    uint32_t gt = 0, eq = 0;
-    for (int base = lo; base < hi; base += 64) {
-        int p = base + lane;
-        uint32_t u = p < hi ? keys[p] : 0u;
-        bool vg = p < hi && u > T, ve = p < hi && u == T;
-        gt += __popcll(__ballot(vg));
-        eq += __popcll(__ballot(ve));
-    }
+    __syncthreads();
+}
+
+// Min / max over the block (all threads get the result).  Contains barriers.
+__device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, uint32_t *wt) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    mn = wave_umin(mn);
+    mx = wave_umax(mx);
     if (lane == 0) {
-        S.wave_gt[wave] = gt;
-        S.wave_eq[wave] = eq;
+        wt[wave] = mn;
+        wt[kTkWaves + wave] = mx;
     }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t sb = 0, eb = 0;
-        for (int w = 0; w < kTopkWaves; ++w) {
-            S.wave_sel_base[w] = sb;
-            S.wave_eq_base[w] = eb;
-            uint32_t take = eb >= need_eq ? 0u : min(S.wave_eq[w], need_eq - eb);
-            sb += S.wave_gt[w] + take;
-            eb += S.wave_eq[w];
-        }
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        mn = min(mn, wt[w]);
+        mx = max(mx, wt[kTkWaves + w]);
     }
     __syncthreads();
-    uint32_t sb = S.wave_sel_base[wave], eb = S.wave_eq_base[wave];
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = lo; base < hi; base += 64) {
-        int p = base + lane;
-        uint32_t u = p < hi ? keys[p] : 0u;
-        bool vg = p < hi && u > T, ve = p < hi && u == T;
-        uint64_t me = __ballot(ve);
-        uint32_t rank = eb + __popcll(me & below);
-        bool sel = vg || (ve && rank < need_eq);
-        uint64_t ms = __ballot(sel);
-        if (sel) out_pos((int)(sb + __popcll(ms & below)), p);
-        sb += __popcll(ms);
-        eb += __popcll(me);
-    }
-    return k;
 }
 
-// Segment pass: grid (S_max, n_queries).  Each workgroup stages one segment of
-// a query's scores as keys in LDS and selects its local top-k.  A query with a
-// single segment writes its final (ascending, -1 padded) list directly;
-// otherwise the segment's candidates go to the workspace for the merge pass.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_segment(Lay L, const int32_t *req,
-                                                               const int32_t *pos, int n_req_cache,
-                                                               int64_t max_tokens, const float *scores, int64_t ld,
-                                                               int seg, int k, int32_t *out,
-                                                               int32_t *cand_idx, uint32_t *cand_key,
-                                                               int s_max) {
-    extern __shared__ uint32_t dyn[];
-    __shared__ TopkShared S;
+// Over hist[0..nb) (nb <= kTkBins, bins ordered by value), the bin holding the
+// rem-th largest element and how many elements lie in higher bins.  bin = -1
+// (and before = the total) when fewer than rem elements were counted.
+// Contains barriers.
+__device__ __forceinline__ void tk_find_bin(const uint32_t *hist, int nb, uint32_t rem, uint32_t *wt,
+                                            int *bin_out, uint32_t *before_out) {
+    __shared__ int s_bin;
+    __shared__ uint32_t s_before;
+    const int tid = threadIdx.x;
+    uint32_t c[8], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {                    // reversed bins: largest first
+        const int rb = tid * 8 + j;
+        c[j] = rb < nb ? hist[nb - 1 - rb] : 0u;
+        sum += c[j];
+    }
+    uint32_t x[1] = {sum}, tot[1];
+    block_excl<1>(x, tot, wt);
+    if (tid == 0 && tot[0] < rem) {
+        s_bin = -1;
+        s_before = tot[0];
+    }
+    uint32_t run = x[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (run < rem && rem <= run + c[j]) {
+            s_bin = nb - 1 - (tid * 8 + j);
+            s_before = run;
+        }
+        run += c[j];
+    }
+    __syncthreads();
+    *bin_out = s_bin;
+    *before_out = s_before;
+    __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t shr32(uint32_t v, int s) { return s >= 32 ? 0u : v >> s; }
+
+// Exact rem-th largest among the keys get(p), p < n, that satisfy in(u); all
+// such keys lie in [lo_key, hi_key].  Radix passes of up to 11 bits over
+// u - lo_key.  Returns the key; *need receives how many keys equal to it are
+// among the rem largest.  Contains barriers.
+template <typename Get, typename In>
+__device__ uint32_t tk_refine(Get get, int64_t n, In in, uint32_t lo_key, uint32_t hi_key, uint32_t rem,
+                              uint32_t *hist, uint32_t *wt, uint32_t *need) {
+    int hs = bit_length(hi_key - lo_key);
+    uint32_t hv = 0;
+    while (hs > 0) {
+        const int lo = hs > 11 ? hs - 11 : 0;
+        const int nb = 1 << (hs - lo);
+        for (int b = threadIdx.x; b < kTkBins; b += kTkThreads) hist[b] = 0;
+        __syncthreads();
+        for (int64_t p = threadIdx.x; p < n; p += kTkThreads) {
+            const uint32_t u = get(p);
+            if (!in(u)) continue;
+            const uint32_t v = u - lo_key;
+            if (shr32(v, hs) == hv) atomicAdd(&hist[(v >> lo) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        int fb;
+        uint32_t before;
+        tk_find_bin(hist, nb, rem, wt, &fb, &before);
+        hv = (hv << (hs - lo)) | (uint32_t)fb;       // fb >= 0: the keys in range number >= rem
+        rem -= before;
+        hs = lo;
+    }
+    *need = rem;
+    return lo_key + hv;
+}
+
+// Rows of given scores: grid (nwr / 4, n), one wave per 256 scores records
+// the extremes of its finite scores, as the scoring kernel does.
+__global__ __launch_bounds__(256) void k_tk_extremes(TkArgs A) {
+    const int q = blockIdx.y, lane = threadIdx.x & 63;
+    const int64_t k0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kKeysPerWave;
+    const int64_t N = tk_visible(A, q);
+    if (k0 >= N) return;
+    const float4 x = *(const float4 *)(A.ws.scores + (int64_t)q * A.ws.ld + k0 + 4 * lane);
+    const float e[4] = {x.x, x.y, x.z, x.w};
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (k0 + 4 * lane + c < N && fabsf(e[c]) < INFINITY) {
+            const uint32_t u = score_key(e[c]);
+            mn = min(mn, u);
+            mx = max(mx, u);
+        }
+    }
+    mn = wave_umin(mn);
+    mx = wave_umax(mx);
+    if (lane == 0) A.ws.wr[(int64_t)q * A.ws.nwr + k0 / kKeysPerWave] = make_uint2(mn, mx);
+}
+
+// Histograms are stored as 16-bit counts (a segment holds at most 4096
+// scores): thread t of a pass owns bins [8t, 8t+8), one 16-byte word.
+__device__ __forceinline__ void tk_unpack8(const uint4 &h, uint32_t (&c)[8]) {
+    c[0] = h.x & 0xffffu; c[1] = h.x >> 16;
+    c[2] = h.y & 0xffffu; c[3] = h.y >> 16;
+    c[4] = h.z & 0xffffu; c[5] = h.z >> 16;
+    c[6] = h.w & 0xffffu; c[7] = h.w >> 16;
+}
+
+// Pass 1: grid (s_max, n).  Histogram of one segment.  Every load whose
+// address is known up front is issued before the row length is read (rows and
+// per-wave extremes are always in bounds), so the kernel waits on memory once.
+__global__ __launch_bounds__(kTkThreads) void k_tk_hist(TkArgs A) {
+    __shared__ uint32_t hist[kTkBins];
+    __shared__ uint32_t wt[2 * kTkWaves];
     const int q = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
-    const int r = req[q];
-    const int64_t t = pos[q];
-    const bool okq = !(r < 0 || r >= n_req_cache || t < 0 || t >= max_tokens);
-    const int64_t N = okq ? (t + 1) / L.m : 0;
-    const int nseg = N <= seg ? 1 : (int)((N + seg - 1) / seg);
-    if (s >= nseg) return;
-    const int64_t lo = (int64_t)s * seg;
-    const int n = (int)min((int64_t)seg, N - lo);
-    const float *src = scores + (int64_t)q * ld + lo;
-    uint32_t *keys = dyn;
-    for (int p = tid; p < n; p += kTopkThreads) keys[p] = score_key(src[p]);
+    const IndexWs &W = A.ws;
+    const float *row = W.scores + (int64_t)q * W.ld + (int64_t)s * kTkSeg;
+    float4 x[kTkVec];
+#pragma unroll
+    for (int v = 0; v < kTkVec; ++v) x[v] = *(const float4 *)(row + v * kTkThreads * 4 + 4 * tid);
+    // (clamped indices keep every load unconditional: no branch between them)
+    const uint2 e0 = W.wr[(int64_t)q * W.nwr + min(tid, W.nwr - 1)];
+    const TkRowLen rl = tk_fetch(A, q);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t N = tk_count(A, rl);
+    const int k = A.L.topk;
+    if (N <= k || (int64_t)s * kTkSeg >= N) return;
+    const int n = (int)min((int64_t)kTkSeg, N - (int64_t)s * kTkSeg);
+    // the query's finite score range, from the scoring waves' extremes
+    const int nw = (int)((N + kKeysPerWave - 1) / kKeysPerWave);
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    if (tid < nw && e0.y != 0u) {
+        mn = e0.x;
+        mx = e0.y;
+    }
+    for (int i = tid + kTkThreads; i < nw; i += kTkThreads) {
+        const uint2 e = W.wr[(int64_t)q * W.nwr + i];
+        if (e.y != 0u) {
+            mn = min(mn, e.x);
+            mx = max(mx, e.y);
+        }
+    }
+    for (int b = tid; b < kTkBins; b += kTkThreads) hist[b] = 0;
+    block_minmax(mn, mx, wt);
+    float fmin, scale;
+    tk_map(mn, mx, fmin, scale);
+#pragma unroll
+    for (int v = 0; v < kTkVec; ++v) {
+        const int p = v * kTkThreads * 4 + 4 * tid;
+        const float e[4] = {x[v].x, x[v].y, x[v].z, x[v].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int d = p + c < n ? tk_digit(score_key(e[c]), fmin, scale) : -1;
+            if (d >= 0) atomicAdd(&hist[d], 1u);
+        }
+    }
     __syncthreads();
-    if (nseg == 1) {
-        int32_t *o = out + (int64_t)q * k;
-        int got = select_topk(keys, n, k, S, [&](int i, int p) { o[i] = p; });
-        for (int i = got + tid; i < k; i += kTopkThreads) o[i] = -1;
-    } else {
-        int32_t *ci = cand_idx + ((int64_t)q * s_max + s) * k;
-        uint32_t *ck = cand_key + ((int64_t)q * s_max + s) * k;
-        select_topk(keys, n, k, S, [&](int i, int p) {
-            ci[i] = (int32_t)(lo + p);
-            ck[i] = keys[p];
-        });
+    const uint32_t *h = hist + 8 * tid;
+    *(uint4 *)(W.hist + ((int64_t)q * W.s_max + s) * kTkBins + 8 * tid) =
+        make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    if (s == 0 && tid == 0) {
+        W.qm[q].fmin = fmin;
+        W.qm[q].scale = scale;
     }
 }
 
-// Merge pass: one workgroup per query with more than one segment.  Candidates
-// of all segments, concatenated in segment order (ascending entry index), are
-// staged and the same selection is run over them.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_merge(Lay L, const int32_t *req,
-                                                             const int32_t *pos, int n_req_cache,
-                                                             int64_t max_tokens, int seg, int k, int32_t *out,
-                                                             const int32_t *cand_idx,
-                                                             const uint32_t *cand_key, int s_max) {
-    extern __shared__ uint32_t dyn[];
-    __shared__ TopkShared S;
-    const int q = blockIdx.x, tid = threadIdx.x;
-    const int r = req[q];
-    const int64_t t = pos[q];
-    if (r < 0 || r >= n_req_cache || t < 0 || t >= max_tokens) return;
-    const int64_t N = (t + 1) / L.m;
-    if (N <= seg) return;
-    const int nseg = (int)((N + seg - 1) / seg);
-    uint32_t *keys = dyn;
-    int32_t *cidx = (int32_t *)(dyn + s_max * k);
-    int n = 0;
-    for (int s = 0; s < nseg; ++s) {
-        const int ns = (int)min((int64_t)k, min((int64_t)seg, N - (int64_t)s * seg));
-        const int64_t base = ((int64_t)q * s_max + s) * k;
-        for (int i = tid; i < ns; i += kTopkThreads) {
-            keys[n + i] = cand_key[base + i];
-            cidx[n + i] = cand_idx[base + i];
+// Query histogram over segments [0, S) (c) and over segments [0, s_lim) (p),
+// bins [8t, 8t+8) of thread t; eight segments' loads in flight at a time.
+template <bool PREFIX>
+__device__ __forceinline__ void tk_sum_hists(const uint16_t *gh, int S, int s_lim, uint32_t (&c)[8],
+                                             uint32_t (&p)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = p[j] = 0;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        uint4 h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            h[i] = s0 + i < S ? *(const uint4 *)(gh + (int64_t)(s0 + i) * kTkBins + 8 * threadIdx.x)
+                              : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t e[8];
+            tk_unpack8(h[i], e);
+            const bool before = PREFIX && s0 + i < s_lim;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                c[j] += e[j];
+                p[j] += before ? e[j] : 0u;
+            }
         }
-        n += ns;
+    }
+}
+
+// Pass 2 (rows of more than kTkFuseSeg segments): grid (n).  Boundary bin of
+// the query and every segment's output offsets.  (With fewer segments the
+// split pass derives them itself.)
+__global__ __launch_bounds__(kTkThreads) void k_tk_bin(TkArgs A) {
+    __shared__ uint32_t hist[kTkBins];
+    __shared__ uint32_t wt[3 * kTkWaves];
+    __shared__ uint32_t seg_sure[kTkMaxSeg], seg_cand[kTkMaxSeg];
+    const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t N = tk_visible(A, q);
+    const uint32_t k = (uint32_t)A.L.topk;
+    if (N <= (int64_t)k) return;
+    const IndexWs &W = A.ws;
+    const int S = (int)((N + kTkSeg - 1) / kTkSeg);
+    const uint16_t *gh = W.hist + (int64_t)q * W.s_max * kTkBins;
+    uint32_t c[8], p[8];
+    tk_sum_hists<false>(gh, S, 0, c, p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hist[8 * tid + j] = c[j];
+    __syncthreads();
+    int bstar;
+    uint32_t above;
+    tk_find_bin(hist, kTkBins, k, wt, &bstar, &above);
+    // per segment: elements above b* and inside b* (NaN scores form the bin
+    // below bin 0); wave w takes segments w, w + 4, ...
+    for (int s = wave; s < S; s += kTkWaves) {
+        const uint16_t *h = gh + (int64_t)s * kTkBins + 32 * lane;
+        uint32_t sure = 0, all = 0, inb = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t e[8];
+            tk_unpack8(*(const uint4 *)(h + 8 * j), e);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int b = 32 * lane + 8 * j + i;
+                all += e[i];
+                sure += b > bstar ? e[i] : 0u;
+                inb += b == bstar ? e[i] : 0u;
+            }
+        }
+        sure = wave_sum(sure);
+        all = wave_sum(all);
+        inb = wave_sum(inb);
+        if (lane == 0) {
+            const uint32_t ns = (uint32_t)min((int64_t)kTkSeg, N - (int64_t)s * kTkSeg);
+            seg_sure[s] = sure;
+            seg_cand[s] = bstar >= 0 ? inb : ns - all;
+        }
     }
     __syncthreads();
-    int32_t *o = out + (int64_t)q * k;
-    int got = select_topk(keys, n, k, S, [&](int i, int p) { o[i] = cidx[p]; });
-    for (int i = got + tid; i < k; i += kTopkThreads) o[i] = -1;
+    uint32_t base_s = 0, base_c = 0;
+    for (int s0 = 0; s0 < S; s0 += kTkThreads) {
+        const int s = s0 + tid;
+        uint32_t x[2] = {s < S ? seg_sure[s] : 0u, s < S ? seg_cand[s] : 0u}, tot[2];
+        block_excl<2>(x, tot, wt);
+        if (s < S) W.segoff[(int64_t)q * W.s_max + s] = make_int2((int)(base_s + x[0]), (int)(base_c + x[1]));
+        base_s += tot[0];
+        base_c += tot[1];
+    }
+    if (tid == 0) {
+        W.qm[q].bstar = bstar;
+        W.qm[q].rem = (int32_t)(k - base_s);
+        W.qm[q].n_sure = (int32_t)base_s;
+        W.qm[q].n_cand = (int32_t)base_c;
+    }
+}
+
+// Pass 3: grid (s_max, n).  Sure indices and candidates of one segment, in
+// index order.  FUSED (s_max <= kTkFuseSeg): the boundary bin and this
+// segment's offsets come from the histograms directly (every workgroup of the
+// query derives the same values; segment 0 records them for the final pass).
+// All loads are issued before the row length is known.
+template <bool FUSED>
+__global__ __launch_bounds__(kTkThreads) void k_tk_split(TkArgs A) {
+    __shared__ uint32_t wt[2 * kTkVec * kTkWaves];
+    const int q = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+    const IndexWs &W = A.ws;
+    const float *row = W.scores + (int64_t)q * W.ld + (int64_t)s * kTkSeg;
+    float4 x[kTkVec];
+#pragma unroll
+    for (int v = 0; v < kTkVec; ++v) x[v] = *(const float4 *)(row + v * kTkThreads * 4 + 4 * tid);
+    const float2 map = *(const float2 *)&W.qm[q].fmin;
+    uint4 hw[FUSED ? kTkFuseSeg : 1];
+    int2 off = make_int2(0, 0);
+    int32_t q_bstar = 0, q_ncand = 0;
+    if constexpr (FUSED) {
+        const uint16_t *gh = W.hist + (int64_t)q * W.s_max * kTkBins + 8 * tid;
+        // (clamped indices keep every load unconditional: no branch between them)
+#pragma unroll
+        for (int i = 0; i < kTkFuseSeg; ++i) hw[i] = *(const uint4 *)(gh + (int64_t)min(i, W.s_max - 1) * kTkBins);
+    } else {
+        off = W.segoff[(int64_t)q * W.s_max + s];
+        q_bstar = W.qm[q].bstar;
+        q_ncand = W.qm[q].n_cand;
+    }
+    const TkRowLen rl = tk_fetch(A, q);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t N = tk_count(A, rl);
+    const int k = A.L.topk;
+    if (N <= k || (int64_t)s * kTkSeg >= N) return;
+    const int n = (int)min((int64_t)kTkSeg, N - (int64_t)s * kTkSeg);
+    const float fmin = map.x, scale = map.y;
+    int bstar;
+    uint32_t sure_off, cand_off, above = 0, n_cand;
+    if constexpr (FUSED) {
+        __shared__ uint32_t hist[kTkBins];
+        const int S = (int)((N + kTkSeg - 1) / kTkSeg);
+        uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0}, p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < kTkFuseSeg; ++i) {
+            uint32_t e[8];
+            tk_unpack8(hw[i], e);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                c[j] += i < S ? e[j] : 0u;
+                p[j] += i < s ? e[j] : 0u;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hist[8 * tid + j] = c[j];
+        __syncthreads();
+        tk_find_bin(hist, kTkBins, (uint32_t)k, wt, &bstar, &above);
+        uint32_t r[4] = {0, 0, 0, 0}, tot[4];       // prefix above b*, prefix all, prefix in b*, query all
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int b = 8 * tid + j;
+            r[0] += b > bstar ? p[j] : 0u;
+            r[1] += p[j];
+            r[2] += b == bstar ? p[j] : 0u;
+            r[3] += c[j];
+        }
+        block_excl<4>(r, tot, wt);
+        sure_off = tot[0];
+        cand_off = bstar >= 0 ? tot[2] : (uint32_t)s * kTkSeg - tot[1];
+        n_cand = bstar >= 0 ? hist[bstar] : (uint32_t)N - tot[3];
+    } else {
+        bstar = q_bstar;
+        n_cand = (uint32_t)q_ncand;
+        sure_off = (uint32_t)off.x;
+        cand_off = (uint32_t)off.y;
+    }
+    const bool keep = n_cand <= (uint32_t)kTkCandMax;
+    uint32_t key[kTkVec][4];
+    int dg[kTkVec][4];
+    uint32_t cnt[2 * kTkVec];
+#pragma unroll
+    for (int v = 0; v < kTkVec; ++v) {
+        const float e[4] = {x[v].x, x[v].y, x[v].z, x[v].w};
+        uint32_t ns = 0, nc = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int p = v * kTkThreads * 4 + 4 * tid + c;
+            key[v][c] = score_key(e[c]);
+            // beyond the row's end: a bin below every other (never chosen)
+            dg[v][c] = p < n ? tk_digit(key[v][c], fmin, scale) : -2;
+            ns += dg[v][c] > bstar;
+            nc += dg[v][c] == bstar;
+        }
+        cnt[v] = ns;
+        cnt[kTkVec + v] = nc;
+    }
+    uint32_t tot[2 * kTkVec];
+    block_excl<2 * kTkVec>(cnt, tot, wt);
+    uint32_t bs = sure_off, bc = cand_off;
+    int32_t *sure = W.sure + (int64_t)q * k;
+    uint32_t *ck = W.ckey + (int64_t)q * kTkCandMax;
+    int32_t *cp = W.cpos + (int64_t)q * kTkCandMax;
+    int32_t *cr = W.crank + (int64_t)q * kTkCandMax;
+#pragma unroll
+    for (int v = 0; v < kTkVec; ++v) {
+        uint32_t is = bs + cnt[v], ic = bc + cnt[kTkVec + v];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int32_t idx = (int32_t)((int64_t)s * kTkSeg + v * kTkThreads * 4 + 4 * tid + c);
+            if (dg[v][c] > bstar) sure[is++] = idx;
+            if (dg[v][c] == bstar && keep) {
+                ck[ic] = key[v][c];
+                cp[ic] = idx;
+                cr[ic] = (int32_t)is;                // sure elements before it
+                ++ic;
+            }
+        }
+        bs += tot[v];
+        bc += tot[kTkVec + v];
+    }
+    if (FUSED && s == 0 && tid == 0) {
+        W.qm[q].bstar = bstar;
+        W.qm[q].rem = (int32_t)((uint32_t)k - above);
+        W.qm[q].n_sure = (int32_t)above;
+        W.qm[q].n_cand = (int32_t)n_cand;
+    }
+}
+
+// Pass 4: grid (n).  Exact threshold and the ascending output list.
+__global__ __launch_bounds__(kTkThreads) void k_tk_final(TkArgs A) {
+    constexpr int kMaxK = 2048;
+    __shared__ uint32_t ckey[kTkCandMax];
+    __shared__ int32_t cpos[kTkCandMax];
+    __shared__ int32_t crk[kTkCandMax];
+    __shared__ int32_t sure[kMaxK], slotv[kMaxK];
+    __shared__ uint32_t hist[kTkBins];
+    __shared__ uint32_t wt[4 * kTkWaves];
+    __shared__ uint32_t s_thr, s_need;
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int k = A.L.topk;
+    const IndexWs &W = A.ws;
+    // the first candidates, the sure list and the query's counts, all read
+    // before the row length (the workspace rows are always that long)
+    const uint32_t ck0 = W.ckey[(int64_t)q * kTkCandMax + tid];
+    const int32_t cp0 = W.cpos[(int64_t)q * kTkCandMax + tid];
+    const int32_t cr0 = W.crank[(int64_t)q * kTkCandMax + tid];
+    int32_t su[kMaxK / kTkThreads];
+#pragma unroll
+    for (int j = 0; j < kMaxK / kTkThreads; ++j) su[j] = W.sure[(int64_t)q * k + min(tid + j * kTkThreads, k - 1)];
+    const TkQuery M = W.qm[q];
+    const TkRowLen rl = tk_fetch(A, q);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t N = tk_count(A, rl);
+    int32_t *out = A.out + (int64_t)q * k;
+    if (N <= k) {                                    // everything visible, ascending, then padding
+        for (int i = tid; i < k; i += kTkThreads) out[i] = i < N ? i : -1;
+        return;
+    }
+    const uint32_t rem = (uint32_t)M.rem;
+    const int D = M.n_sure;
+    const float *row = W.scores + (int64_t)q * W.ld;
+    const int bstar = M.bstar;
+    auto in_b = [&](uint32_t u) { return tk_digit(u, M.fmin, M.scale) == bstar; };
+    uint32_t T, need;
+    if (M.n_cand <= kTkCandMax) {
+        const int C = M.n_cand;
+        if (tid < C) {
+            ckey[tid] = ck0;
+            cpos[tid] = cp0;
+            crk[tid] = cr0;
+        }
+        for (int i = kTkThreads + tid; i < C; i += kTkThreads) {
+            ckey[i] = W.ckey[(int64_t)q * kTkCandMax + i];
+            cpos[i] = W.cpos[(int64_t)q * kTkCandMax + i];
+            crk[i] = W.crank[(int64_t)q * kTkCandMax + i];
+        }
+        for (int i = tid; i < k; i += kTkThreads) slotv[i] = -1;
+#pragma unroll
+        for (int j = 0; j < kMaxK / kTkThreads; ++j)
+            if (tid + j * kTkThreads < D) sure[tid + j * kTkThreads] = su[j];
+        __syncthreads();
+        if (C <= kTkThreads) {
+            // rank the candidates: the rem-th largest has fewer than rem
+            // candidates above it and at least rem at or above it
+            if (tid < C) {
+                const uint32_t mine = ck0;
+                uint32_t gt = 0, ge = 0;
+                for (int j = 0; j < C; ++j) {
+                    const uint32_t c = ckey[j];
+                    gt += c > mine;
+                    ge += c >= mine;
+                }
+                if (gt < rem && rem <= ge) {         // equal candidates write equal values
+                    s_thr = mine;
+                    s_need = rem - gt;
+                }
+            }
+            __syncthreads();
+            T = s_thr;
+            need = s_need;
+        } else {
+            uint32_t lo = 0xffffffffu, hi = 0u;
+            for (int i = tid; i < C; i += kTkThreads) {
+                lo = min(lo, ckey[i]);
+                hi = max(hi, ckey[i]);
+            }
+            block_minmax(lo, hi, wt);
+            T = tk_refine([&](int64_t p) { return ckey[p]; }, C, [](uint32_t) { return true; }, lo, hi, rem, hist,
+                          wt, &need);
+        }
+        // chosen candidates in index order: above T, then the first `need`
+        // equal to T.  The j-th chosen one, with r sure elements before it,
+        // takes output slot j + r; the sure elements fill the other slots in order.
+        uint32_t ngt = 0, neq = 0;                   // candidates above / equal to T so far
+        for (int i0 = 0; i0 < C; i0 += kTkThreads) {
+            const int i = i0 + tid;
+            const uint32_t u = i < C ? ckey[i] : 0u;
+            const bool gt = i < C && u > T, isq = i < C && u == T;
+            uint32_t x[2] = {gt ? 1u : 0u, isq ? 1u : 0u}, tx[2];
+            block_excl<2>(x, tx, wt);
+            const uint32_t eq_before = neq + x[1];
+            // chosen ones before i: all above T, and the first `need` equal to T
+            const uint32_t j = ngt + x[0] + min(eq_before, need);
+            if (gt || (isq && eq_before < need)) slotv[j + crk[i]] = cpos[i];
+            ngt += tx[0];
+            neq += tx[1];
+        }
+        __syncthreads();
+        uint32_t fr[1] = {0}, tf[1];
+        int32_t sv[kMaxK / kTkThreads];
+        constexpr int SPT = kMaxK / kTkThreads;      // output slots per thread
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int slot = SPT * tid + j;
+            sv[j] = slot < k ? slotv[slot] : 0;
+            fr[0] += (slot < k && sv[j] < 0) ? 1u : 0u;
+        }
+        block_excl<1>(fr, tf, wt);
+        uint32_t f = fr[0];
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int slot = SPT * tid + j;
+            if (slot < k) out[slot] = sv[j] >= 0 ? sv[j] : sure[f++];
+        }
+        return;
+    }
+    // crowded boundary bin: refine over the whole row, then compact it
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int64_t p = tid; p < N; p += kTkThreads) {
+        const uint32_t u = score_key(row[p]);
+        if (in_b(u)) {
+            lo = min(lo, u);
+            hi = max(hi, u);
+        }
+    }
+    block_minmax(lo, hi, wt);
+    T = tk_refine([&](int64_t p) { return score_key(row[p]); }, N, in_b, lo, hi, rem, hist, wt, &need);
+    uint32_t nsel = 0, neq = 0;
+    for (int64_t p0 = 0; p0 < N; p0 += 4 * kTkThreads) {
+        uint32_t u[4], e = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t p = p0 + 4 * tid + c;
+            u[c] = p < N ? score_key(row[p]) : 0u;
+            e += (p < N && u[c] == T) ? 1u : 0u;
+        }
+        uint32_t x[1] = {e}, tx[1];
+        block_excl<1>(x, tx, wt);
+        bool pick[4];
+        uint32_t np = 0, eq = neq + x[0];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t p = p0 + 4 * tid + c;
+            const bool isq = p < N && u[c] == T;
+            pick[c] = p < N && (u[c] > T || (isq && eq < need));
+            eq += isq ? 1u : 0u;
+            np += pick[c] ? 1u : 0u;
+        }
+        uint32_t y[1] = {np}, ty[1];
+        block_excl<1>(y, ty, wt);
+        uint32_t o = nsel + y[0];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (pick[c]) out[o++] = (int32_t)(p0 + 4 * tid + c);
+        nsel += ty[0];
+        neq += tx[0];
+    }
 }
 
 // ---------------------------------------------------------------- launchers
-// Workspace layout for n queries, Nmax entries: q8 [n][HI][128] | wq [n][HI] |
-// scores [n][Nmax] | cand_idx [n][S][k] | cand_key [n][S][k].
-
-
+// Workspace layout for n queries whose rows hold ld = Nmax rounded up to whole
+// segments: q8 [n][HI][128] | wq [n][HI] | wave extremes [n][ld/256] |
+// scores [n][ld] | 16-bit histograms [n][S][2048] | query results [n] |
+// segment offsets [n][S] | sure lists [n][k] | candidate keys, indices and
+// sure-ranks [n][kTkCandMax] each.
 static inline int64_t al256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-int topk_segment_len(int k, int64_t nmax, int nq, int cus) {
-    // One workgroup per segment; a query with more than one segment is merged
-    // from its segments' candidates (s_max * k <= 16384 keys in LDS).  Small
-    // batches use shorter segments so that the selection spreads over the CUs.
-    int64_t want = nq > 0 ? (cus + nq - 1) / nq : 1;
-    int64_t cap = 16384 / k;
-    if (want > cap) want = cap;
-    if (want < 1) want = 1;
-    int64_t seg = (nmax + want - 1) / want;
-    seg = (seg + 1023) / 1024 * 1024;
-    if (seg < 4096) seg = 4096;
-    while ((nmax + seg - 1) / seg * (int64_t)k > 16384) seg += 1024;
-    return (int)seg;
-}
-
 int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base) {
-    const int seg = topk_segment_len(L.topk, nmax, n, 256);
-    const int s_max = nmax <= seg ? 1 : (int)((nmax + seg - 1) / seg);
+    const int64_t ld = (nmax + kTkSeg - 1) / kTkSeg * kTkSeg;
+    const int s_max = (int)(ld / kTkSeg);
+    const int nwr = (int)(ld / kKeysPerWave);
     int64_t off = 0;
-    int64_t o_q8 = off; off = al256(off + (int64_t)n * L.HI * 128);
-    int64_t o_wq = off; off = al256(off + (int64_t)n * L.HI * 4);
-    int64_t o_sc = off; off = al256(off + (int64_t)n * nmax * 4);
-    int64_t o_ci = off, o_ck = off;
-    if (s_max > 1) {
-        o_ci = off; off = al256(off + (int64_t)n * s_max * L.topk * 4);
-        o_ck = off; off = al256(off + (int64_t)n * s_max * L.topk * 4);
-    }
+    const int64_t o_q8 = off; off = al256(off + (int64_t)n * L.HI * 128);
+    const int64_t o_wq = off; off = al256(off + (int64_t)n * L.HI * 4);
+    const int64_t o_wr = off; off = al256(off + (int64_t)n * nwr * 8);
+    const int64_t o_sc = off; off = al256(off + (int64_t)n * ld * 4);
+    const int64_t o_hi = off; off = al256(off + (int64_t)n * s_max * kTkBins * 2);
+    const int64_t o_qm = off; off = al256(off + (int64_t)n * (int64_t)sizeof(TkQuery));
+    const int64_t o_sm = off; off = al256(off + (int64_t)n * s_max * 8);
+    const int64_t o_su = off; off = al256(off + (int64_t)n * L.topk * 4);
+    const int64_t o_ck = off; off = al256(off + (int64_t)n * kTkCandMax * 4);
+    const int64_t o_cp = off; off = al256(off + (int64_t)n * kTkCandMax * 4);
+    const int64_t o_cr = off; off = al256(off + (int64_t)n * kTkCandMax * 4);
     if (w) {
         w->q8 = base + o_q8;
         w->wq = (float *)(base + o_wq);
+        w->wr = (uint2 *)(base + o_wr);
         w->scores = (float *)(base + o_sc);
-        w->cand_idx = (int32_t *)(base + o_ci);
-        w->cand_key = (uint32_t *)(base + o_ck);
-        w->ld = nmax;
-        w->seg = seg;
+        w->hist = (uint16_t *)(base + o_hi);
+        w->qm = (TkQuery *)(base + o_qm);
+        w->segoff = (int2 *)(base + o_sm);
+        w->sure = (int32_t *)(base + o_su);
+        w->ckey = (uint32_t *)(base + o_ck);
+        w->cpos = (int32_t *)(base + o_cp);
+        w->crank = (int32_t *)(base + o_cr);
+        w->ld = ld;
+        w->nwr = nwr;
         w->s_max = s_max;
     }
     return off;
@@ -458,7 +967,8 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
     const int hb = (L.HI + 15) / 16;
     const bool full = L.dI == 128;
 #define DSV4_SCORE(HBV, FV) \
-    hipLaunchKernelGGL((k_index_score_decode<HBV, FV>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, ws.ld)
+    hipLaunchKernelGGL((k_index_score_decode<HBV, FV>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, ws.ld, \
+                       ws.wr, ws.nwr)
     if (full) {
         if (hb == 4) DSV4_SCORE(4, true);
         else if (hb == 3) DSV4_SCORE(3, true);
@@ -474,26 +984,43 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
     return hipGetLastError();
 }
 
+// n <= 65535 (grid y).  With no segments (empty rows) only the final pass
+// runs: it writes the padding.
+static void launch_tk_passes(const TkArgs &A, int n, hipStream_t s) {
+    const IndexWs &ws = A.ws;
+    if (ws.s_max > 0) {
+        hipLaunchKernelGGL(k_tk_hist, dim3(ws.s_max, n), dim3(kTkThreads), 0, s, A);
+        if (ws.s_max <= kTkFuseSeg) {
+            hipLaunchKernelGGL(k_tk_split<true>, dim3(ws.s_max, n), dim3(kTkThreads), 0, s, A);
+        } else {
+            hipLaunchKernelGGL(k_tk_bin, dim3(n), dim3(kTkThreads), 0, s, A);
+            hipLaunchKernelGGL(k_tk_split<false>, dim3(ws.s_max, n), dim3(kTkThreads), 0, s, A);
+        }
+    }
+    hipLaunchKernelGGL(k_tk_final, dim3(n), dim3(kTkThreads), 0, s, A);
+}
+
 hipError_t launch_topk(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos, int n,
                        const IndexWs &ws, int32_t *out, hipStream_t s) {
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_topk_segment, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           32768 * 4);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void *)k_topk_merge, hipFuncAttributeMaxDynamicSharedMemorySize, 16384 * 8);
+    const TkArgs A{L, req, pos, C.n_req, (int64_t)C.max_blocks * kBlockTokens, ws, out, nullptr, 0};
+    launch_tk_passes(A, n, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *nvis, int n, int64_t max_n, int k,
+                            const IndexWs &ws, int32_t *out, hipStream_t s) {
+    Lay L;
+    memset(&L, 0, sizeof(L));
+    L.topk = k;
+    L.m = 1;
+    const TkArgs A{L, nullptr, nullptr, 0, 0, ws, out, nvis, max_n};
+    if (max_n > 0) {
+        hipError_t e = hipMemcpy2DAsync(ws.scores, (size_t)ws.ld * 4, scores, (size_t)ld * 4, (size_t)max_n * 4,
+                                        n, hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return e;
-        attr_done = true;
+        hipLaunchKernelGGL(k_tk_extremes, dim3((unsigned)(ws.nwr / 4), n), dim3(256), 0, s, A);
     }
-    size_t lds = (size_t)ws.seg * 4;
-    hipLaunchKernelGGL(k_topk_segment, dim3(ws.s_max, n), dim3(kTopkThreads), lds, s, L, req, pos, C.n_req,
-                       (int64_t)C.max_blocks * kBlockTokens, ws.scores, ws.ld, ws.seg, L.topk, out, ws.cand_idx, ws.cand_key, ws.s_max);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || ws.s_max <= 1) return e;
-    size_t lds2 = (size_t)ws.s_max * L.topk * 8;
-    hipLaunchKernelGGL(k_topk_merge, dim3(n), dim3(kTopkThreads), lds2, s, L, req, pos, C.n_req,
-                       (int64_t)C.max_blocks * kBlockTokens, ws.seg,
-                       L.topk, out, ws.cand_idx, ws.cand_key, ws.s_max);
+    launch_tk_passes(A, n, s);
     return hipGetLastError();
 }
 

@@ -17,16 +17,42 @@ hipError_t launch_state_tokens(const Lay &L, const dsv4_cache &C, int r, int64_t
                                const void *kv, const void *gate, const void *kI, const void *gI,
                                hipStream_t s);
 
+// Top-k: scores are selected in segments of kTkSeg; a query's boundary bin
+// keeps at most kTkCandMax candidates in the workspace (more take a slower
+// exact path); a score row spans at most kTkMaxSeg segments.
+constexpr int kTkSeg = 4096;
+constexpr int kTkBins = 2048;
+constexpr int kTkCandMax = 4096;
+constexpr int kTkMaxSeg = 1024;
+// Rows of at most this many segments skip the separate boundary-bin pass:
+// each split workgroup sums the (few) segment histograms itself.
+constexpr int kTkFuseSeg = 16;
+// Queries (or rows) one indexer / top-k launch takes: the grid's y extent.
+constexpr int kMaxGridRows = 65535;
+// Per-query outcome of the boundary-bin pass.
+struct TkQuery {
+    float fmin, scale;      // linear map of the finite scores onto the bins
+    int32_t bstar;          // bin holding the k-th largest score (-1: the NaN scores)
+    int32_t rem;            // elements still to take from bin bstar
+    int32_t n_sure;         // elements above bin bstar (all selected)
+    int32_t n_cand;         // elements inside bin bstar
+    int32_t pad[2];
+};
 struct IndexWs {
     uint8_t *q8;
     float *wq;
-    float *scores;
-    int32_t *cand_idx;
-    uint32_t *cand_key;
+    uint2 *wr;              // [n][nwr]: per scoring wave, min / max key of its finite scores
+    float *scores;          // [n][ld]
+    uint16_t *hist;         // [n][s_max][kTkBins] per-segment counts
+    TkQuery *qm;            // [n]
+    int2 *segoff;           // [n][s_max]: output offsets of a segment's sure / candidate elements
+    int32_t *sure;          // [n][k]
+    uint32_t *ckey;         // [n][kTkCandMax]
+    int32_t *cpos;          // [n][kTkCandMax]
+    int32_t *crank;         // [n][kTkCandMax]: sure elements before each candidate
     int64_t ld;
-    int seg, s_max;
+    int nwr, s_max;
 };
-int topk_segment_len(int k, int64_t nmax, int nq, int cus);
 int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base);
 hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows, const IndexWs &ws,
                           hipStream_t s);
@@ -34,6 +60,8 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
                                int n, const IndexWs &ws, hipStream_t s);
 hipError_t launch_topk(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos, int n,
                        const IndexWs &ws, int32_t *out, hipStream_t s);
+hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *nvis, int n, int64_t max_n, int k,
+                            const IndexWs &ws, int32_t *out, hipStream_t s);
 hipError_t launch_expand_queries(const int32_t *cu, const int32_t *req, const int32_t *pos0, int n_seq,
                                  int total, int32_t *req_q, int32_t *pos_q, hipStream_t s);
 

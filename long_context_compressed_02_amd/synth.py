@@ -152,3 +152,41 @@ def tiny_hidden(w: Workload = TINY_CSA, steps: int = 16):
 
 def permutation(wid: int, n: int, sub: int = 0) -> np.ndarray:
     return rng(wid, T_PERM, sub).permutation(n)
+
+
+T_SCORE = 20
+SCORE_KINDS = ("normal", "ties", "crowded", "constant", "special", "allnan", "wide", "huge")
+
+
+def score_row(kind: str, n: int, seed: int) -> np.ndarray:
+    """A float32 row of n scores for the selection tests: 'normal' N(0,1);
+    'ties' integers 0..49; 'crowded' integers 0..2; 'constant' all 1.5;
+    'special' N(0,1) with NaN, +-inf and +-0 sprinkled in; 'allnan';
+    'wide' log-normal with sigma 10 (a huge dynamic range); 'huge' values near
+    +-3e38 (their range overflows fp32)."""
+    g = np.random.default_rng([0, T_SCORE, SCORE_KINDS.index(kind), seed])
+    if kind == "normal":
+        x = g.standard_normal(n)
+    elif kind == "ties":
+        x = g.integers(0, 50, n).astype(np.float64)
+    elif kind == "crowded":
+        x = g.integers(0, 3, n).astype(np.float64)
+    elif kind == "constant":
+        x = np.full(n, 1.5)
+    elif kind == "special":
+        x = g.standard_normal(n)
+        u = g.random(n)
+        x[u < 0.10] = np.nan
+        x[(u >= 0.10) & (u < 0.12)] = np.inf
+        x[(u >= 0.12) & (u < 0.14)] = -np.inf
+        x[(u >= 0.14) & (u < 0.17)] = 0.0
+        x[(u >= 0.17) & (u < 0.20)] = -0.0
+    elif kind == "allnan":
+        x = np.full(n, np.nan)
+    elif kind == "wide":
+        x = g.lognormal(0.0, 10.0, n) * np.where(g.random(n) < 0.3, -1.0, 1.0)
+    elif kind == "huge":
+        x = np.where(g.random(n) < 0.5, -3e38, 3e38) * g.uniform(0.5, 1.0, n)
+    else:
+        raise ValueError(kind)
+    return x.astype(np.float32)

@@ -125,7 +125,7 @@ def test_compress_decode_equals_prefill_and_oracle(shape, kind):
 @pytest.mark.parametrize("k", [256, 1024])
 def test_index_topk_decode(k):
     cfg, oc = Hh.cfgs(PROD, topk=k)
-    ctx = [3, 1000, 4099, 20001, 4000]       # query position t = ctx - 1
+    ctx = [3, 1000, 4099, 20001, 4000, 160004]   # query position t = ctx - 1 (the last: two top-k segments)
     cache, bth = _new_cache(cfg, B.DSV4_CSA, ctx, seed=2)
     nq = len(ctx)
     keys = []

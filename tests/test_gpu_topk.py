@@ -1,0 +1,82 @@
+"""Exact top-k selection on given fp32 rows (dsv4_topk_rows) against the
+oracle's stable sort, element for element.  Selection is index work, so the
+bar is bit-exact: the same fp32 values go to both sides (the oracle widens
+them to fp64 exactly), and the pages' rule -- the k largest, ties to the lower
+index, ascending output padded with -1 -- leaves exactly one correct answer.
+The row kinds drive every path of the kernel: spread-out scores (boundary bin
+of a few candidates), many ties (hundreds of candidates, radix refinement
+inside the candidate list), crowded or constant rows (more candidates than the
+workspace keeps: refinement over the whole row), NaN / +-inf / +-0, all-NaN
+rows, huge dynamic ranges and a range that overflows fp32."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_compressed_02_amd import binding as B
+from long_context_compressed_02_amd import synth
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(rows, k, max_n=None, ld_pad=3, n_override=None):
+    max_n = max_n if max_n is not None else max([len(r) for r in rows] + [0])
+    ld = max_n + ld_pad
+    sc = np.zeros((len(rows), ld), dtype=np.float32)
+    for i, r in enumerate(rows):
+        sc[i, :len(r)] = r
+    n = np.array([len(r) for r in rows] if n_override is None else n_override, dtype=np.int32)
+    st = torch.from_numpy(sc).to(DEV)
+    nt = torch.from_numpy(n).to(DEV)
+    out = torch.full((len(rows), k), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(B.dsv4_topk_rows_ws_bytes(len(rows), max_n, k), dtype=torch.uint8, device=DEV)
+    B.dsv4_topk_rows(st, nt, max_n, k, out, ws)
+    return out.cpu().numpy()
+
+
+def _check(got, rows, k):
+    for i, r in enumerate(rows):
+        want = O.topk(r.astype(np.float64), k)
+        if not np.array_equal(got[i], want):
+            bad = np.nonzero(got[i] != want)[0]
+            raise AssertionError(f"row {i} (n={len(r)}): first mismatch at {bad[0]}: "
+                                 f"got {got[i][bad[:5]]} want {want[bad[:5]]}")
+
+
+@pytest.mark.parametrize("kind", synth.SCORE_KINDS)
+@pytest.mark.parametrize("k", [512, 1024])
+def test_topk_rows_exact(kind, k):
+    lens = [0, 1, k - 1, k, k + 1, 4095, 4096, 4097, 9000, 40001]
+    rows = [synth.score_row(kind, n, seed) for seed, n in enumerate(lens)]
+    print(f"topk_rows kind={kind} k={k} lens={lens}", flush=True)
+    _check(_run(rows, k), rows, k)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special"])
+def test_topk_rows_one_million_context(kind):
+    # 1M-token context at stride 4: 262144 entries, 64 segments
+    rows = [synth.score_row(kind, 262144, 7), synth.score_row(kind, 131071, 8)]
+    print(f"topk_rows 1M kind={kind}", flush=True)
+    _check(_run(rows, 1024), rows, 1024)
+
+
+def test_topk_rows_k_limits_and_invalid_lengths():
+    rows = [synth.score_row("normal", n, 30 + n) for n in (5000, 2048, 3000)]
+    print("topk_rows k=2048 / k=1", flush=True)
+    _check(_run(rows, 2048), rows, 2048)
+    _check(_run(rows, 1), rows, 1)
+    # lengths outside [0, max_n] select nothing
+    got = _run(rows, 64, max_n=5000, n_override=[-1, 5001, 3000])
+    assert (got[0] == -1).all() and (got[1] == -1).all()
+    _check(got[2:], rows[2:], 64)
+
+
+def test_topk_rows_more_rows_than_one_launch():
+    # 70000 rows: the library splits them into launches of at most 65535 rows
+    g = np.random.default_rng(5)
+    n = g.integers(0, 17, 70000)
+    rows = [synth.score_row("ties", int(m), int(i % 97)) for i, m in enumerate(n)]
+    print("topk_rows 70000 rows", flush=True)
+    got = _run(rows, 4, max_n=16)
+    _check(got, rows, 4)
