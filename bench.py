@@ -16,8 +16,10 @@ starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -179,7 +181,8 @@ def main():
     achieved = pl["work"] / avg_s / (1e9 if pl["unit"] == "GB/s" else 1e12)
     roof = {"kernel": {"index_score": "k_index_score_decode", "attend": "k_attend"}[dom], "bound": pl["bound"],
             "achieved": round(achieved, 2), "peak": pl["peak"], "unit": pl["unit"],
-            "frac": round(achieved / pl["peak"], 4), "traffic": None}
+            "frac": round(achieved / pl["peak"], 4),
+            "traffic": measured_traffic() if dom == "attend" and (Bsz, ctx) == (32, 131072) else None}
     step_bytes = score_bytes + attend_bytes_step
     value = Bsz / (ms_step * 1e-3)
 
@@ -205,6 +208,27 @@ def main():
         "setup_s": round(t_setup, 1),
     }
     print(json.dumps(res), flush=True)
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "k_attend_decode_128k_b32_hbm_traffic.txt")
+ATTEND_SRC = os.path.join(HERE, "long_context_compressed_02_amd", "csrc", "k_attend.hip")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, calibrated on a
+    plain copy) from the committed rocprofv3 summary of this workload -- only
+    if the summary was taken on the attention source as it is now."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = open(ATTEND_SRC, "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"k_attend_src_sha256: ([0-9a-f]+)", text)
+    if not m or not h or hashlib.sha256(src).hexdigest() != h.group(1):
+        return None
+    return int(m.group(1))
 
 
 def cpu_baseline(w, nq, t):
