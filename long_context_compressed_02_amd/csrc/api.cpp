@@ -78,13 +78,12 @@ int num_cus() {
 }
 
 bool pick_hi(int policy, int nq, int nhg) {
-    // HI needs whole 64-head workgroups; otherwise LO runs (same results)
-    if (nhg % 4 != 0) return false;
     if (policy == DSV4_POLICY_HI) return true;
     if (policy == DSV4_POLICY_LO) return false;
-    // a HI workgroup (64 heads of one query) occupies a CU; while there are
-    // fewer of them than CUs, LO spreads each query over nhg workgroups instead
-    return (int64_t)nq * (nhg / 4) >= num_cus();
+    // LO gives each (query, head group) workgroup 16 waves; once there are
+    // enough workgroups to give every compute unit several, HI's 4-wave
+    // workgroups keep the same number of waves busy with less LDS each
+    return (int64_t)nq * nhg >= 2 * (int64_t)num_cus();
 }
 
 }  // namespace
@@ -378,7 +377,7 @@ static dsv4_status attend_common(const dsv4_cfg *cfg, const dsv4_cache *cache, i
     A.out = out;
     A.nq = nq;
     A.nhg = (L.H + 15) / 16;
-    if (attend_list_max(L, *cache, kind == DSV4_CSA) * 4 > kAttendMaxLocBytes) return DSV4_ERR_UNSUPPORTED;
+    if (attend_lds_max(L, attend_list_max(L, *cache, kind == DSV4_CSA)) > kLdsMax) return DSV4_ERR_UNSUPPORTED;
     const bool hi = pick_hi(policy, nq, A.nhg);
     Timed tm(DSV4_K_ATTEND, S(stream));
     return hip_status(launch_attend(A, kind == DSV4_CSA, prefill, hi, S(stream)));

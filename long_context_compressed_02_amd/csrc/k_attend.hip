@@ -11,35 +11,34 @@
 // with each stored record v_i serving as key and value, qrot the query rotated
 // at t on its last d_rope dims.
 //
-// Design (MI355X): records are staged 64 at a time in LDS exactly as they sit
-// in HBM (640 B rows, padded by 16 B against bank conflicts).  A wave owns a
-// 16-head group; both contractions run on v_mfma_f32_16x16x32_bf16:
-//   S^T = K . Q^T  (A = 16 records x 32 dims read with ds_read_b64 and
-//                   converted fp8 -> bf16 exactly; B = the rotated query held
-//                   in registers for the whole kernel)
+// Design (MI355X): both contractions run on v_mfma_f32_16x16x32_bf16:
+//   S^T = K . Q^T  (A = 16 records x 32 dims: E4M3 codes read from LDS and
+//                   converted to bf16 exactly; B = the rotated query, held in
+//                   registers for the whole kernel)
 //   O^T += V^T . P^T (A = 16 dims x 32 records read with the gfx950 LDS
 //                   transpose loads ds_read_b64_tr_b8 / _tr_b16 straight from
 //                   the row-major records; B = P from the S^T registers)
 // The FP8 scale stays outside the MFMA: logits use s_i * (q_n . c_i) + q_r . r_i,
-// and the P operand of the non-RoPE columns carries p_i * s_i.
+// and the P operand of the non-RoPE columns carries p_i * s_i.  Records are
+// gathered 32 at a time (whole 128-byte lines per load) into LDS rows padded
+// and shifted against bank conflicts.
 //
 // Batch invariance and the two kernels (m.youleyou.com, "what was sacrificed";
-// hwcomputing.csdn.net section 四): there is no split over records -- every
-// head's reduction runs over its query's record list in one fixed order with
-// a fixed tile of 64 records.  HI (for a saturated GPU) runs one workgroup per
-// (query, 64 heads): each of its 4 waves owns a 16-head group end to end (all
-// 4 record blocks of S, all 32 dim blocks of O), so a staged tile feeds 64
-// heads.  LO (for an unsaturated GPU) runs one workgroup per (query, 16-head
-// group): its 4 waves split the group's work (wave w does record block w of S
-// and dim blocks [8w, 8w+8) of O) and exchange logits through LDS, giving 8
-// workgroups per query; those 8 sit on one XCD so the gathered records are
-// fetched into one L2.  Every head sees the same MFMA instructions on the same
-// operands and the same scalar code in the same order, so HI and LO agree bit
-// for bit, whatever the batch.
+// hwcomputing.csdn.net section 四): nothing is split across workgroups -- each
+// (query, 16-head group) is reduced by one workgroup in a fixed order that
+// depends on nothing but the query (see the decomposition below), so a
+// query's output is bitwise the same whatever the batch.  LO (for an
+// unsaturated GPU) gives that workgroup 16 waves; HI (for a saturated GPU)
+// gives it 4 waves that do the same work in sequence, so that several
+// workgroups share a compute unit.  They agree bit for bit.  The 8 workgroups
+// of a query are placed on one XCD, so its gathered records are fetched into
+// one L2.
 //
 // Latency: all record addresses of a query (top-k index -> block table ->
-// record) are resolved once into an LDS locator array before the tile loop,
-// and tiles are prefetched two deep into registers.
+// record) are resolved once into an LDS locator array before the chunk loop,
+// and the next chunk's loads are in flight while the current one is computed.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace dsv4 {
@@ -48,11 +47,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x2 *lds_i32x2_p;
 typedef __attribute__((address_space(3))) i16x4 *lds_i16x4_p;
 
-constexpr int kTile = 64;   // records per online-softmax step (fixed: part of the reduction order)
+
 
 
 
@@ -155,319 +155,501 @@ __device__ __forceinline__ const uint8_t *loc_addr(const AttnArgs &A, const Quer
     return (const uint8_t *)A.C.state + (int64_t)Q.r * L.state_bytes + w * L.rec_bytes;
 }
 
-// G head groups per workgroup, R waves per head group: HI = (4, 2), LO = (1, 4).
-template <int D, int DR, int G, int R, bool CSA, bool PREFILL>
-__global__ __launch_bounds__(64 * G * R) void k_attend(AttnArgs A) {
-    constexpr int NT = 64 * G * R;
-    constexpr bool HI = G > 1;
-    constexpr int RBW = 4 / R;                   // record blocks of S per wave
-    constexpr int DN = D - DR;
-    constexpr int REC = ((DN + 2 * DR + 4) + 63) / 64 * 64;   // stored record stride in HBM
-    // LDS row: the record dequantised to bf16 codes (E4M3 -> bf16 is exact; the
-    // scale stays separate): [DN bf16 | DR bf16 | fp32 scale | pad]
-    constexpr int ROPE_OFF = 2 * DN, SCALE_OFF = 2 * D;
-    constexpr int RS = (2 * D + 4 + 15) / 16 * 16 + 16;     // 16 B pad against bank conflicts
-    constexpr int NCH = DN / 16;                 // HBM chunks of E4M3 codes
-    constexpr int RCH = DR / 8;                  // HBM chunks of bf16 RoPE dims
-    constexpr int LCH = NCH + RCH + 1;           // chunks loaded per record (codes, RoPE, scale)
-    constexpr int SCALE_OFF_HBM = DN + 2 * DR;   // 16-byte aligned: DN, DR multiples of 16
-    static_assert(SCALE_OFF_HBM % 16 == 0, "scale chunk alignment");
-    constexpr int KN = (DN + 31) / 32, KR = (DR + 31) / 32;
-    constexpr int DBN = DN / 16, DBR = DR / 16, DB = DBN + DBR;
-    constexpr int TPR = NT / kTile;              // loader threads per record
-    constexpr int CPT = (LCH + TPR - 1) / TPR;   // 16-byte chunks per thread per tile
-    constexpr int DBW = (DB + R - 1) / R;        // dim blocks of O held per wave
+// ---------------------------------------------------------------- the kernel
+// Decomposition of one (query, 16-head group).  The record list is cut into
+// chunks of 32 records; chunk c belongs to subset c mod 4, and each subset is
+// reduced on its own (online softmax over its chunks in increasing order).
+// The dims are cut into 2 parts: part dq owns MFMA code pairs
+// [QPP*dq, QPP*dq + QPP) of the logits and dim blocks [DBQ*dq, DBQ*dq + DBQ)
+// of the output; the last part also owns the RoPE part of the logits.  A
+// chunk's logits are the fixed-order sum of the parts' partial dot products:
+//     l = tau * (s * (a0 + a1) + r)
+// (a_q: code dims of part q, s: the record's scale, r: RoPE dims).  The four
+// subset states are then folded left to right:
+//     acc = s0;  acc = fold(acc, s1);  acc = fold(acc, s2);  acc = fold(acc, s3)
+// LO (8 waves: 4 subsets x 2 parts) runs the subsets at once and folds
+// through LDS; HI (2 waves: the parts) runs the subsets one after another and
+// folds in registers.  Same operations in the same order: HI and LO agree bit
+// for bit.  A wave holds half of the output accumulators, so two waves share
+// a SIMD and hide each other's LDS and memory latency.
+constexpr int kChunk = 32;     // records per chunk (the k of one PV MFMA)
+constexpr int kSubsets = 4;
+constexpr int kParts = 2;     // dim parts (each wave holds one part of the output)
 
-    __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * RS];
-    __shared__ float sS[G][4][16][17];            // logits exchanged between a group's waves
+template <int N>
+struct AttnState {
+    float m, l;                // running max / sum of the lane's head (base-2 logits)
+    f32x4 O[N];                // O^T of this quarter's dim blocks: dims 16*db + 4g + i
+};
+
+template <int N>
+__device__ __forceinline__ void state_clear(AttnState<N> &s) {
+    s.m = -INFINITY;
+    s.l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) s.O[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// fold(a, b): the two partial softmaxes rescaled to their common max.
+__device__ __forceinline__ void fold_scales(float ma, float la, float mb, float lb, float &m, float &l,
+                                            float &fa, float &fb) {
+    m = fmaxf(ma, mb);
+    fa = ma == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ma - m);
+    fb = mb == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - m);
+    l = la * fa + lb * fb;
+}
+__device__ __forceinline__ f32x4 fold_o(const f32x4 &a, float fa, const f32x4 &b, float fb) {
+    return a * fa + b * fb;
+}
+
+// Max / sum over the four lanes of a head (lanes c16, c16+16, c16+32, c16+48)
+// with the gfx950 row-swap permutes (VALU, no LDS).
+__device__ __forceinline__ float head_max(float v) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float head_sum(float v) {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Shapes shared by the kernel and its launcher.
+template <int D, int DR>
+struct AttnShape {
+    static constexpr int DN = D - DR;
+    static constexpr int NCH = DN / 16;                 // 16-byte pieces of E4M3 codes (16 dims each)
+    static constexpr int RCH = DR / 8;                  // 16-byte pieces of BF16 RoPE dims (8 dims each)
+    static constexpr int CREC = NCH + RCH + 1;          // + the piece holding the fp32 scale
+    static constexpr int REC = (DN + 2 * DR + 4 + 63) / 64 * 64;   // stored record stride in HBM
+    static constexpr int PPR = REC / 16;                // pieces per stored record (padding included)
+    static constexpr int LW = REC % 128 == 0 ? 8 : 4;   // lanes per record in one load: a 128 (64)-byte line
+    static constexpr int RPI = 64 / LW;                 // records per load instruction
+    static constexpr int NLD = kChunk * PPR / 64;       // load instructions per chunk
+    static constexpr int RS = PPR + 1;                  // LDS row stride in pieces (odd)
+    static constexpr int SWZ = 4;                       // records 16..31 shifted by SWZ pieces
+    static constexpr int BUF = (kChunk * RS + SWZ) * 16;   // LDS bytes of one chunk buffer
+    static constexpr int KP = (NCH + 3) / 4;            // logits: MFMA pairs over the code pieces
+    static constexpr int KR = (RCH + 3) / 4;            // logits: MFMAs over the RoPE pieces
+    static constexpr int QPP = (KP + kParts - 1) / kParts;   // code pairs per dim part
+    static constexpr int NDB = NCH + DR / 16;           // 16-dim blocks of the output
+    static constexpr int DBQ = (NDB + kParts - 1) / kParts;  // output dim blocks per dim part
+    static constexpr int XW = 2 * 4 * 64;               // floats of one part's partial logits
+    static_assert(DN % 16 == 0 && DR % 16 == 0, "dims in whole 16-dim blocks");
+    static_assert(NLD % kParts == 0, "a chunk's loads split evenly over the dim parts");
+};
+
+// NSW subset waves per dim part: LO = 4 (8 waves), HI = 1 (2 waves).
+template <int D, int DR, int NSW, bool CSA, bool PREFILL>
+__global__ __launch_bounds__(64 * kParts * NSW) void k_attend(AttnArgs A) {
+    using Sh = AttnShape<D, DR>;
+    constexpr int NT = 64 * kParts * NSW;
+    constexpr int NCH = Sh::NCH, RCH = Sh::RCH, CREC = Sh::CREC, PPR = Sh::PPR, LW = Sh::LW, RPI = Sh::RPI;
+    constexpr int NLD = Sh::NLD, LDQ = NLD / kParts, RS = Sh::RS, SWZ = Sh::SWZ, BUF = Sh::BUF;
+    constexpr int KP = Sh::KP, KR = Sh::KR, QPP = Sh::QPP, NDB = Sh::NDB, DBQ = Sh::DBQ, XW = Sh::XW;
+    constexpr int DN = Sh::DN;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ float2 rope_tab[DR / 2];
     __shared__ int32_t safe_sh;
-    __shared__ float2 rope_tab[DR / 2];          // cos/sin of this query's position per RoPE pair
-    extern __shared__ int32_t locs[];            // [n_list] record locators of this query
 
     const Lay &L = A.L;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar registers)
+    const int dq = wave % kParts, sw = wave / kParts;   // dim part, subset wave
 
-    // ---- which query and head group (the workgroups of one query share an
-    // XCD: workgroups are dealt round-robin over the 8 XCDs)
+    // ---- which query and head group (the 8 workgroups of a query are dealt
+    // onto one XCD: workgroup ids go round-robin over the 8 XCDs)
     const int lin = blockIdx.x, x8 = lin & 7, u8 = lin >> 3;
-    const int parts = A.nhg / G;                 // workgroups per query
-    const int qi = (u8 / parts) * 8 + x8;
-    const int gl = wave / R, role = wave % R;    // head group within the workgroup, role in it
-    const int hg = (u8 % parts) * G + gl;
+    const int qi = (u8 / A.nhg) * 8 + x8;
+    const int hg = u8 % A.nhg;
     if (qi >= A.nq) return;
     const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
     if (!Q.ok) return;
     const int head = hg * 16 + c16;
-    const bool head_ok = hg < A.nhg && head < L.H;
+    const bool head_ok = head < L.H;
 
-    // ---- resolve every record of the list once
-    for (int64_t p = tid; p < Q.n_list; p += NT) locs[p] = record_loc<CSA, PREFILL>(A, Q, p);
+    // LDS: record locators, NSW chunk buffers, NSW partial-logit exchanges.
+    // LO's final fold reuses the same bytes.
+    int32_t *locs = (int32_t *)smem;
+    const int loc_bytes = ((int)Q.n_list * 4 + 15) / 16 * 16;
+    uint32_t *vmask = (uint32_t *)(smem + loc_bytes);   // [chunk]: bit r = record r usable
+    const int head_bytes = loc_bytes + (((int)Q.n_list + kChunk - 1) / kChunk * 4 + 15) / 16 * 16;
+    uint8_t *buf = smem + head_bytes + sw * BUF;
+    float *xch = (float *)(smem + head_bytes + NSW * BUF) + sw * (kParts + 1) * XW;
+
+    // ---- resolve every record of the list once; any valid record stands in
+    // for masked ones (its bytes are loaded, its weight is 0)
+    if (tid == 0) safe_sh = -1;
     __syncthreads();
+    int32_t last_ok = -1;
+    for (int64_t p0 = (int64_t)wave * 64; p0 < Q.n_list; p0 += NT) {   // wave-uniform: 64 consecutive records
+        const int64_t p = p0 + lane;
+        const int32_t lc = p < Q.n_list ? record_loc<CSA, PREFILL>(A, Q, p) : kMasked;
+        if (p < Q.n_list) locs[p] = lc;
+        if (lc != kMasked) last_ok = (int32_t)p;
+        const uint64_t vb = __builtin_amdgcn_ballot_w64(lc != kMasked);
+        if (lane == 0) {
+            vmask[p0 / kChunk] = (uint32_t)vb;
+            if (p0 + kChunk < Q.n_list) vmask[p0 / kChunk + 1] = (uint32_t)(vb >> 32);
+        }
+    }
+    if (last_ok >= 0) atomicMax(&safe_sh, last_ok);
     if (tid < DR / 2) {
         float c, sn;
         rope_cs(L, Q.t, tid, c, sn);
         rope_tab[tid] = make_float2(c, sn);
     }
-    if (tid == 0) {
-        int32_t sf = kMasked;
-        for (int64_t p = Q.n_list - 1; p >= 0; --p)
-            if (locs[p] != kMasked) {
-                sf = locs[p];
-                break;
-            }
-        safe_sh = sf;
-    }
-
     __syncthreads();
-    // ---- query fragments (B operand of S^T = K Q^T): lane = head, items = 8 dims
-    bf16x8 Qn[KN], Qr[KR];
-    {
-        const int64_t qbase = ((int64_t)Q.qrow * L.H + head) * D;
-        // 8 consecutive dims of this lane's head as fp32 (one or two 16-byte loads)
-        auto q8 = [&](int dd, float (&v)[8]) {
-            if (L.act == DSV4_DT_BF16) {
-                const uint4 u = *(const uint4 *)((const uint16_t *)A.q + qbase + dd);
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[2 * j] = __uint_as_float(w[j] << 16);
-                    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    const int32_t safe = safe_sh >= 0 ? locs[safe_sh] : kMasked;
+    const int n_list = (int)Q.n_list;                // (lists are far below 2^31 records)
+    const int nchunks = safe == kMasked ? 0 : (n_list + kChunk - 1) / kChunk;
+
+    static_assert(kParts == 2, "the part dispatch below covers two parts");
+    // Everything below is compiled once per dim part (DQ), so that every LDS
+    // and register index is a compile-time offset from a few lane bases.
+    auto part_body = [&](auto dqc) {
+        constexpr int DQ = decltype(dqc)::value;
+        // ---- query fragments of this dim part (B operand of S^T = K Q^T), lane
+        // (head c16, group g): code pair kp reads piece 4kp+g, dims 16(4kp+g) +
+        // [0,8) and [8,16); RoPE step ks reads RoPE piece 4ks+g, rotated at t.
+        bf16x8 Qn[QPP][2], Qr[KR];
+        {
+            const int64_t qbase = ((int64_t)Q.qrow * L.H + head) * D;
+            auto q8 = [&](int dd, float (&v)[8]) {
+                if (L.act == DSV4_DT_BF16) {
+                    const uint4 u = *(const uint4 *)((const uint16_t *)A.q + qbase + dd);
+                    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[2 * j] = __uint_as_float(w[j] << 16);
+                        v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                    }
+                } else {
+                    const float4 a = *(const float4 *)((const float *)A.q + qbase + dd);
+                    const float4 b = *(const float4 *)((const float *)A.q + qbase + dd + 4);
+                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
                 }
-            } else {
-                const float4 a = *(const float4 *)((const float *)A.q + qbase + dd);
-                const float4 b = *(const float4 *)((const float *)A.q + qbase + dd + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-            }
-        };
-#pragma unroll
-        for (int ks = 0; ks < KN; ++ks) {
-            const int dd = ks * 32 + 8 * g;
-            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (head_ok && dd < DN) q8(dd, v);
-            bf16x8 f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[j] = f2bf(v[j]);
-            Qn[ks] = f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < KR; ++ks) {
-            const int uu = ks * 32 + 8 * g;
-            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (head_ok && uu < DR) q8(DN + uu, v);
-            bf16x8 f;
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                float a = 0.0f, b = 0.0f;
-                if (uu + j < DR) {
-                    const float2 cs = rope_tab[(uu + j) / 2];
-                    a = v[j] * cs.x - v[j + 1] * cs.y;
-                    b = v[j] * cs.y + v[j + 1] * cs.x;
+            };
+    #pragma unroll
+            for (int e = 0; e < QPP; ++e) {
+                const int kp = QPP * DQ + e, ch = 4 * kp + g;
+    #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (head_ok && kp < KP && ch < NCH) q8(16 * ch + 8 * h, v);
+                    bf16x8 f;
+    #pragma unroll
+                    for (int j = 0; j < 8; ++j) f[j] = f2bf(v[j]);
+                    Qn[e][h] = f;
                 }
-                f[j] = f2bf(a);
-                f[j + 1] = f2bf(b);
             }
-            Qr[ks] = f;
-        }
-    }
-    const int32_t safe = safe_sh;
-
-    // ---- running softmax state (lane's head) and output accumulators O^T
-    // softmax in base 2: logits carry tau*log2(e), exp is v_exp_f32
-    const float tau2 = L.tau * 1.4426950408889634f;
-    float m_run = -INFINITY, l_run = 0.0f;
-    f32x4 O[DBW];
-#pragma unroll
-    for (int i = 0; i < DBW; ++i) O[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    const int db0 = role * DBW;
-    const int64_t ntiles = (Q.n_list + kTile - 1) / kTile;
-
-    // loader: thread tid fetches chunks (tid % TPR) + TPR*i of record tid / TPR
-    const int ld_rec = tid / TPR, ld_c0 = tid % TPR;
-    auto load = [&](uint4 (&pre)[CPT], int64_t tl) {
-        const int64_t p = tl * kTile + ld_rec;
-        int32_t lc = p < Q.n_list ? locs[p] : kMasked;
-        if (lc == kMasked) lc = safe;
-        if (lc == kMasked) {
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) pre[i] = make_uint4(0, 0, 0, 0);
-            return;
-        }
-        const uint4 *src = (const uint4 *)loc_addr<PREFILL>(A, Q, lc);
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = ld_c0 + i * TPR;
-            if (c < LCH) pre[i] = src[c < NCH + RCH ? c : (SCALE_OFF_HBM / 16)];
-        }
-    };
-
-    auto compute = [&](int64_t tl) {
-        auto valid = [&](int rr) {
-            const int64_t p = tl * kTile + rr;
-            return p < Q.n_list && locs[p] != kMasked;
-        };
-        // ---- S^T = K Q^T for the record blocks this wave owns
-        float lg[4][4];
-        auto qk_block = [&](int rb, float (&out)[4]) {
-            const int rec = rb * 16 + c16;                 // A-operand row: record
-            const uint8_t *row = tile + rec * RS;
-            f32x4 an = {0.0f, 0.0f, 0.0f, 0.0f}, ar = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KN; ++ks) {
-                const int d0 = ks * 32 + 8 * g;
-                bf16x8 a = as_bf16x8(make_uint4(0, 0, 0, 0));
-                if (d0 < DN) a = *(const bf16x8 *)(row + 2 * d0);
-                an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, Qn[ks], an, 0, 0, 0);
-            }
-#pragma unroll
+    #pragma unroll
             for (int ks = 0; ks < KR; ++ks) {
-                const int u0 = ks * 32 + 8 * g;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (u0 < DR) v = *(const uint4 *)(row + ROPE_OFF + 2 * u0);
-                ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v), Qr[ks], ar, 0, 0, 0);
+                const int ch = 4 * ks + g;
+                float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (head_ok && DQ == kParts - 1 && ch < RCH) q8(DN + 8 * ch, v);
+                bf16x8 f;
+    #pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    float a = 0.0f, b = 0.0f;
+                    if (ch < RCH) {
+                        const float2 cs = rope_tab[(8 * ch + j) / 2];
+                        a = v[j] * cs.x - v[j + 1] * cs.y;
+                        b = v[j] * cs.y + v[j + 1] * cs.x;
+                    }
+                    f[j] = f2bf(a);
+                    f[j + 1] = f2bf(b);
+                }
+                Qr[ks] = f;
             }
-            // output lane = head, items = records rb*16 + 4g + i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = rb * 16 + 4 * g + i;
-                const float sc = *(const float *)(tile + rr * RS + SCALE_OFF);
-                const float z = tau2 * (sc * an[i] + ar[i]);
-                out[i] = valid(rr) ? z : -INFINITY;
+        }
+        const float tau2 = L.tau * 1.4426950408889634f;   // logits in base 2
+
+        // ---- chunk loads: the chunk's NLD loads are split over its part waves; in load i, lane l fetches piece LW*(i mod PPR/LW) + l%LW of record
+        // RPI*(i / (PPR/LW)) + l/LW, so every load reads whole lines of RPI
+        // records.  In LDS piece c of record r sits at r*RS + c (+SWZ for records
+        // 16..31), which keeps the MFMA operand reads free of bank conflicts.
+        const int ld_a = lane / LW, ld_b = lane % LW;
+        auto slot = [&](int c, int r) { return buf + (r * RS + c + (r >> 4) * SWZ) * 16; };
+        auto issue = [&](u32x4 (&pre)[LDQ], int ck) {
+    #pragma unroll
+            for (int e = 0; e < LDQ; ++e) {
+                const int i = LDQ * DQ + e;
+                const int r = RPI * (i / (PPR / LW)) + ld_a, c = LW * (i % (PPR / LW)) + ld_b;
+                const int p = ck * kChunk + r;
+                int32_t lc = locs[p < n_list ? p : n_list - 1];   // (no branch around the LDS read)
+                if (p >= n_list || lc == kMasked) lc = safe;
+                pre[e] = *(const u32x4 *)(loc_addr<PREFILL>(A, Q, lc) + 16 * c);
             }
         };
-#pragma unroll
-        for (int i = 0; i < RBW; ++i) {
-            const int rb = role * RBW + i;
-            float mine[4];
-            qk_block(rb, mine);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sS[gl][rb][4 * g + e][c16] = mine[e];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lg[rb][i] = sS[gl][rb][4 * g + i][c16];
+        auto stage = [&](const u32x4 (&pre)[LDQ]) {
+    #pragma unroll
+            for (int e = 0; e < LDQ; ++e) {
+                const int i = LDQ * DQ + e;
+                const int r = RPI * (i / (PPR / LW)) + ld_a, c = LW * (i % (PPR / LW)) + ld_b;
+                *(u32x4 *)slot(c, r) = pre[e];
+            }
+        };
 
-        // ---- online softmax for the lane's head (identical code in HI and LO)
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, lg[rb][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.0f;
-        float p[4][4];
-        if (m_new == -INFINITY) {
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p[rb][i] = 0.0f;
-        } else {
-            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p[rb][i] = __builtin_amdgcn_exp2f(lg[rb][i] - m_new);
-        }
-        float ps = 0.0f;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ps = ps + p[rb][i];
-        ps = ps + __shfl_xor(ps, 16);
-        ps = ps + __shfl_xor(ps, 32);
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < DBW; ++i) O[i] = O[i] * alpha;
+        // ---- this part's partial logits of a staged chunk: code dims of its
+        // pairs (raw, scale not applied) and, in the last part, the RoPE dims;
+        // rows = records 16rb + 4g + i, lane column = head c16
+        auto partial = [&](float (&an)[2][4], float (&ar)[2][4]) {
+    #pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, b = {0.0f, 0.0f, 0.0f, 0.0f};
+    #pragma unroll
+                for (int e = 0; e < QPP; ++e) {
+                    const int kp = QPP * DQ + e, ch = 4 * kp + g;
+                    if (kp < KP) {
+                        u32x4 u = {0, 0, 0, 0};
+                        if (NCH % 4 == 0 || ch < NCH) u = *(const u32x4 *)slot(ch, 16 * rb + c16);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8(u[0], u[1]), Qn[e][0], a, 0, 0, 0);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8(u[2], u[3]), Qn[e][1], a, 0, 0, 0);
+                    }
+                }
+                if (DQ == kParts - 1) {
+    #pragma unroll
+                    for (int ks = 0; ks < KR; ++ks) {
+                        const int ch = 4 * ks + g;
+                        u32x4 u = {0, 0, 0, 0};
+                        if (RCH % 4 == 0 || ch < RCH) u = *(const u32x4 *)slot(NCH + ch, 16 * rb + c16);
+                        union { u32x4 v; bf16x8 b; } cv;
+                        cv.v = u;
+                        b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Qr[ks], b, 0, 0, 0);
+                    }
+                }
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    an[rb][i] = a[i];
+                    ar[rb][i] = b[i];
+                }
+                __builtin_amdgcn_sched_barrier(0);   // one record block's operands at a time
+            }
+        };
 
-        // ---- O^T += V^T P^T, two k-steps of 32 records
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            // B operand: lane = head, items j <-> record ks*32 + (j<4 ? 4g+j : 16+4g+j-4)
+        // ---- the rest of a chunk step, after the partials are exchanged: logits,
+        // online softmax, O^T += V^T P^T on this part's dim blocks
+        auto finish = [&](auto &S, int ck) {
+            constexpr int NO = sizeof(S.O) / sizeof(S.O[0]);
+            float lg[2][4], sc[2][4];
+            const uint32_t vm = vmask[ck];
+    #pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * g + i, k = (rb * 4 + i) * 64 + lane;
+                    const bool ok = (vm >> r) & 1u;
+                    sc[rb][i] = *(const float *)slot(CREC - 1, r);
+                    float a = xch[k];
+    #pragma unroll
+                    for (int q = 1; q < kParts; ++q) a = a + xch[q * XW + k];
+                    lg[rb][i] = ok ? tau2 * (sc[rb][i] * a + xch[kParts * XW + k]) : -INFINITY;
+                }
+            float cmax = -INFINITY;
+    #pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, lg[rb][i]);
+            cmax = head_max(cmax);
+            const float m_new = fmaxf(S.m, cmax);
+            float p[2][4];
+            float alpha = 1.0f;
+            if (m_new == -INFINITY) {
+    #pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) p[rb][i] = 0.0f;
+            } else {
+                alpha = __builtin_amdgcn_exp2f(S.m - m_new);
+    #pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) p[rb][i] = __builtin_amdgcn_exp2f(lg[rb][i] - m_new);
+            }
+            float ps = 0.0f;
+    #pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) ps = ps + p[rb][i];
+            ps = head_sum(ps);
+            S.l = S.l * alpha + ps;
+            S.m = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // alpha == 1 leaves O as it is
+    #pragma unroll
+                for (int i = 0; i < NO; ++i) S.O[i] = S.O[i] * alpha;
+            }
+            // k-slot j of lane group g is record 4g+j (j < 4) or 16+4g+(j-4): the
+            // S^T rows this lane holds
             bf16x8 Pn, Pr;
-#pragma unroll
+    #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int rb = 2 * ks + (j >> 2), i = j & 3;
-                const int rr = rb * 16 + 4 * g + i;
-                const float sc = *(const float *)(tile + rr * RS + SCALE_OFF);
-                Pn[j] = f2bf(p[rb][i] * sc);
+                const int rb = j >> 2, i = j & 3;
+                Pn[j] = f2bf(p[rb][i] * sc[rb][i]);
                 Pr[j] = f2bf(p[rb][i]);
             }
-            // transpose-read addresses: lanes 4r..4r+3 of group g -> record of row r
+            // code dims: ds_read_b64_tr_b8 -- lanes 2j, 2j+1 of the group address
+            // row j (the record of k-slot j), 8 bytes each; lane c16 receives dim
+            // c16 of the 8 records.  RoPE dims (bf16): ds_read_b64_tr_b16 -- lanes
+            // 4r..4r+3 address row r (record 4g+r, resp. 16+4g+r), 4 dims each.
+            const int trow = c16 >> 1, thalf = c16 & 1;
+            const int trec = (trow < 4 ? 0 : 16) + 4 * g + (trow & 3);
             const int r16 = c16 >> 2, q16 = c16 & 3;
-            const int rec16a = ks * 32 + 4 * g + r16;
-            const int rec16b = ks * 32 + 16 + 4 * g + r16;
-#pragma unroll
-            for (int ii = 0; ii < DBW; ++ii) {
-                const int db = db0 + ii;
-                if (db >= DB) break;
-                // dims db*16 .. db*16+15 of the bf16 row (non-RoPE dims first, then RoPE)
-                const int cb = db * 16 + 4 * q16;
-                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(tile + rec16a * RS + 2 * cb));
-                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(tile + rec16b * RS + 2 * cb));
-                union { i16x4 s[2]; bf16x8 b; } cv;
-                cv.s[0] = lo;
-                cv.s[1] = hi;
-                O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, db < DBN ? Pn : Pr, O[ii], 0, 0, 0);
+    #pragma unroll
+            for (int ii = 0; ii < NO; ++ii) {
+                if (ii % 4 == 0) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+                const int db = DBQ * DQ + ii;
+                if (db < NCH) {
+                    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_p)(slot(db, trec) + 8 * thalf));
+                    S.O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8((uint32_t)v[0], (uint32_t)v[1]), Pn, S.O[ii], 0,
+                                                                      0, 0);
+                } else if (db < NDB) {
+                    const int ch = NCH + 2 * (db - NCH) + (q16 >> 1);
+                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(slot(ch, 4 * g + r16) + 8 * (q16 & 1)));
+                    i16x4 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(slot(ch, 16 + 4 * g + r16) + 8 * (q16 & 1)));
+                    union { i16x4 s[2]; bf16x8 b; } cv;
+                    cv.s[0] = lo;
+                    cv.s[1] = hi;
+                    S.O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Pr, S.O[ii], 0, 0, 0);
+                }
             }
-        }
-    };
+        };
 
-    auto step = [&](uint4 (&pre)[CPT], int64_t tl) {
-        __syncthreads();                                   // previous tile fully consumed
-        uint8_t *row = tile + ld_rec * RS;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = ld_c0 + i * TPR;
-            if (c < NCH) {                       // 16 codes -> 16 bf16
-                const bf16x8 lo8 = cvt8(pre[i].x, pre[i].y), hi8 = cvt8(pre[i].z, pre[i].w);
-                *(bf16x8 *)(row + 32 * c) = lo8;
-                *(bf16x8 *)(row + 32 * c + 16) = hi8;
-            } else if (c < NCH + RCH) {          // RoPE dims, already bf16
-                *(uint4 *)(row + ROPE_OFF + 16 * (c - NCH)) = pre[i];
-            } else if (c == NCH + RCH) {         // scale
-                *(float *)(row + SCALE_OFF) = __uint_as_float(pre[i].x);
+        // ---- one chunk step of every subset wave: stage, exchange partials, finish.
+        // ck < 0: this subset has no chunk at this step (the wave still takes part
+        // in the workgroup barriers).
+        auto step = [&](auto &S, int ck, u32x4 (&pre)[LDQ], int next) {
+            __syncthreads();                             // the buffer's previous chunk is consumed
+            if (ck >= 0) stage(pre);
+            if (next >= 0) issue(pre, next);             // in flight during this step's compute
+            __syncthreads();                             // staged chunk visible
+            if (ck >= 0) {
+                float an[2][4], ar[2][4];
+                partial(an, ar);
+    #pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int k = (rb * 4 + i) * 64 + lane;
+                        xch[DQ * XW + k] = an[rb][i];
+                        if (DQ == kParts - 1) xch[kParts * XW + k] = ar[rb][i];
+                    }
             }
-        }
-        __syncthreads();                                   // tile visible
-        if (tl + 2 < ntiles) load(pre, tl + 2);            // two tiles in flight during compute
-        compute(tl);
-    };
+            __syncthreads();                             // partials visible
+            if (ck >= 0) finish(S, ck);
+        };
 
-    uint4 pre0[CPT], pre1[CPT];
-    if (ntiles > 0) load(pre0, 0);
-    if (ntiles > 1) load(pre1, 1);
-    for (int64_t tl = 0; tl < ntiles; tl += 2) {
-        step(pre0, tl);
-        if (tl + 1 < ntiles) step(pre1, tl + 1);
-    }
+        // ---- output rows d = 16db + 4g + i of head `head`, with the sink:
+        // out = O * f / (l * f + 2^(z - M)),  f = 2^(m - M),  M = max(m, z)
+        const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
+        auto emit = [&](float m, float l, int db, const f32x4 &o) {
+            const float z = A.sinks[head] * 1.4426950408889634f;
+            const float M = fmaxf(m, z);
+            const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            const float den = l * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
+            const float cf = den > 0.0f ? f / den : 0.0f;
+            const int dd = db * 16 + 4 * g;
+            if (L.act == DSV4_DT_BF16) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 v = {f2bf(o[0] * cf), f2bf(o[1] * cf), f2bf(o[2] * cf), f2bf(o[3] * cf)};
+                *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
+            } else {
+                *(float4 *)((float *)A.out + obase + dd) = make_float4(o[0] * cf, o[1] * cf, o[2] * cf, o[3] * cf);
+            }
+        };
 
-    // ---- sink and normalisation; output rows d = db*16 + 4g + i of head `head`
-    if (!head_ok) return;
-    const float z = A.sinks[head] * 1.4426950408889634f;
-    const float M = fmaxf(m_run, z);
-    const float f = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
-    const float den = l_run * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
-    const float cf = den > 0.0f ? f / den : 0.0f;
-    const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
-#pragma unroll
-    for (int ii = 0; ii < DBW; ++ii) {
-        const int db = db0 + ii;
-        if (db >= DB) break;
-        const int dd = db * 16 + 4 * g;
-        if (L.act == DSV4_DT_BF16) {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            const bf16x4 v = {f2bf(O[ii][0] * cf), f2bf(O[ii][1] * cf), f2bf(O[ii][2] * cf), f2bf(O[ii][3] * cf)};
-            *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
+        u32x4 pre[LDQ];
+        if constexpr (NSW == 1) {
+            // HI: the subsets one after another on the same 2 waves
+            AttnState<DBQ> acc, cur;
+            state_clear(acc);
+            int first = -1;                              // first chunk in processing order
+            for (int s = 0; s < kSubsets && first < 0; ++s)
+                if (s < nchunks) first = s;
+            if (first >= 0) issue(pre, first);
+    #pragma unroll 1
+            for (int s = 0; s < kSubsets; ++s) {
+                state_clear(cur);
+    #pragma unroll 1
+                for (int ck = s; ck < nchunks; ck += kSubsets) {
+                    int next = ck + kSubsets;
+                    if (next >= nchunks) {               // the next subset's first chunk
+                        next = -1;
+                        for (int s2 = s + 1; s2 < kSubsets && next < 0; ++s2)
+                            if (s2 < nchunks) next = s2;
+                    }
+                    step(cur, ck, pre, next);
+                }
+                if (s == 0) {
+                    acc = cur;
+                } else {
+                    float m, l, fa, fb;
+                    fold_scales(acc.m, acc.l, cur.m, cur.l, m, l, fa, fb);
+    #pragma unroll
+                    for (int i = 0; i < DBQ; ++i) acc.O[i] = fold_o(acc.O[i], fa, cur.O[i], fb);
+                    acc.m = m;
+                    acc.l = l;
+                }
+            }
+            if (head_ok) {
+    #pragma unroll
+                for (int i = 0; i < DBQ; ++i)
+                    if (DBQ * DQ + i < NDB) emit(acc.m, acc.l, DBQ * DQ + i, acc.O[i]);
+            }
         } else {
-            *(float4 *)((float *)A.out + obase + dd) =
-                make_float4(O[ii][0] * cf, O[ii][1] * cf, O[ii][2] * cf, O[ii][3] * cf);
+            // LO: subset sw on this wave; all subsets advance together, one chunk
+            // each per step
+            AttnState<DBQ> S;
+            state_clear(S);
+            const int nsteps = (nchunks + kSubsets - 1) / kSubsets;
+            if (sw < nchunks) issue(pre, sw);
+    #pragma unroll 1
+            for (int t = 0; t < nsteps; ++t) {
+                const int ck = kSubsets * t + sw;
+                const int nx = ck + kSubsets;
+                step(S, ck < nchunks ? ck : -1, pre, nx < nchunks ? nx : -1);
+            }
+            // fold the four subsets' states (per dim part) through LDS
+            __syncthreads();
+            constexpr int NWV = kParts * NSW;
+            float2 *ml = (float2 *)smem;                 // [wave][64]
+            f32x4 *ob = (f32x4 *)(smem + NWV * 64 * 8);  // [wave][DBQ][64]
+            ml[wave * 64 + lane] = make_float2(S.m, S.l);
+    #pragma unroll
+            for (int b = 0; b < DBQ; ++b) ob[(wave * DBQ + b) * 64 + lane] = S.O[b];
+            __syncthreads();
+            // wave (sw, DQ) finishes dim blocks sw, sw+4, ... of part DQ
+            float m = ml[(0 * kParts + DQ) * 64 + lane].x, l = ml[(0 * kParts + DQ) * 64 + lane].y;
+            float fw[kSubsets][2];                       // fold s: factors of the folded part and of state s
+    #pragma unroll
+            for (int s = 1; s < kSubsets; ++s) {
+                const float2 b = ml[(s * kParts + DQ) * 64 + lane];
+                float mm, ll, fa, fb;
+                fold_scales(m, l, b.x, b.y, mm, ll, fa, fb);
+                fw[s][0] = fa;
+                fw[s][1] = fb;
+                m = mm;
+                l = ll;
+            }
+    #pragma unroll
+            for (int b = sw; b < DBQ; b += kSubsets) {
+                f32x4 o = ob[((0 * kParts + DQ) * DBQ + b) * 64 + lane];
+    #pragma unroll
+                for (int s = 1; s < kSubsets; ++s)
+                    o = fold_o(o, fw[s][0], ob[((s * kParts + DQ) * DBQ + b) * 64 + lane], fw[s][1]);
+                if (head_ok && DBQ * DQ + b < NDB) emit(m, l, DBQ * DQ + b, o);
+            }
         }
-    }
+    };
+    if (dq == 0) part_body(std::integral_constant<int, 0>());
+    else part_body(std::integral_constant<int, kParts - 1>());
+
 }
 
 // ---------------------------------------------------------------- launchers
@@ -475,25 +657,41 @@ int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa) {
     return (csa ? (int64_t)L.topk : (int64_t)C.max_blocks * L.epb) + L.W;
 }
 
-template <int D, int DR, int G, int R, bool CSA, bool PREFILL>
+template <int D, int DR, int NSW>
+int64_t attend_lds_bytes(int64_t list_max) {
+    using Sh = AttnShape<D, DR>;
+    const int64_t stream = (list_max * 4 + 15) / 16 * 16 + ((list_max + kChunk - 1) / kChunk * 4 + 15) / 16 * 16 +
+                           (int64_t)NSW * Sh::BUF + (int64_t)NSW * (kParts + 1) * Sh::XW * 4;
+    constexpr int NWV = kParts * NSW;
+    const int64_t fold = NSW == 1 ? 0 : NWV * 64 * 8 + (int64_t)NWV * Sh::DBQ * 64 * 16;
+    return stream > fold ? stream : fold;
+}
+
+int64_t attend_lds_max(const Lay &L, int64_t list_max) {
+    const int64_t lo = L.d == 512 ? attend_lds_bytes<512, 64, 4>(list_max) : attend_lds_bytes<64, 16, 4>(list_max);
+    const int64_t hi = L.d == 512 ? attend_lds_bytes<512, 64, 1>(list_max) : attend_lds_bytes<64, 16, 1>(list_max);
+    return lo > hi ? lo : hi;
+}
+
+template <int D, int DR, int NSW, bool CSA, bool PREFILL>
 static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_attend<D, DR, G, R, CSA, PREFILL>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kAttendMaxLocBytes);
+    const int64_t lds = attend_lds_bytes<D, DR, NSW>(attend_list_max(A.L, A.C, CSA));
+    static int64_t attr = -1;
+    if (attr < lds) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_attend<D, DR, NSW, CSA, PREFILL>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr = true;
+        attr = lds;
     }
-    const size_t lds = (size_t)attend_list_max(A.L, A.C, CSA) * 4;
     const int groups = (A.nq + 7) / 8;
-    hipLaunchKernelGGL((k_attend<D, DR, G, R, CSA, PREFILL>), dim3(groups * 8 * (A.nhg / G)), dim3(64 * G * R), lds,
-                       s, A);
+    hipLaunchKernelGGL((k_attend<D, DR, NSW, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kParts * NSW),
+                       (size_t)lds, s, A);
     return hipGetLastError();
 }
 
 template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_t(const AttnArgs &A, bool hi, hipStream_t s) {
-    return hi ? launch_gr<D, DR, 4, 2, CSA, PREFILL>(A, s) : launch_gr<D, DR, 1, 4, CSA, PREFILL>(A, s);
+    return hi ? launch_gr<D, DR, 1, CSA, PREFILL>(A, s) : launch_gr<D, DR, 4, CSA, PREFILL>(A, s);
 }
 
 hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s) {

@@ -82,8 +82,10 @@ struct AttnArgs {
     int nhg;                // head groups (ceil(H/16))
 };
 hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s);
-// Longest record list one attention query can have (sizes the per-query locator array in LDS).
-constexpr int kAttendMaxLocBytes = 64 * 1024;
+// Longest record list one attention query can have, and the LDS the attention
+// kernels need for it (the per-query locators live in LDS).
 int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa);
+int64_t attend_lds_max(const Lay &L, int64_t list_max);
+constexpr int64_t kLdsMax = 160 * 1024;   // LDS of one gfx950 workgroup
 
 }  // namespace dsv4
