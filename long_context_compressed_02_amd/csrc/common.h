@@ -78,12 +78,23 @@ __device__ __forceinline__ void rope_cs(const Lay &L, int64_t pos, int i, float 
     sincosf((float)r, &s, &c);
 }
 
-// Wave-wide max over the 64 lanes (exact, so the order of the butterfly does
-// not matter).
+// Wave-wide max over the 64 lanes, returned to every lane.  Max is exact and
+// ignores NaN operands whatever the order, so any reduction tree gives the same
+// value; this one runs on the DPP cross-lane paths (no LDS round trips):
+// within rows of 16 lanes by shifts of 1, 2, 4, 8, then across rows.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x) {
+    const int ninf = (int)0xff800000u;
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(ninf, __float_as_int(x), CTRL, ROW_MASK, 0xf, false)));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = dpp_max_step<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_max_step<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_max_step<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_max_step<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_max_step<0x142, 0xa>(v);   // row_bcast:15
+    v = dpp_max_step<0x143, 0xc>(v);   // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // ------------------------------------------------------------------ cache addressing

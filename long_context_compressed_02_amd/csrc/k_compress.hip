@@ -22,9 +22,11 @@ namespace dsv4 {
 
 // ---------------------------------------------------------------- stored vectors
 // Store a record held by one wave (lane l owns dims [l*VPL, (l+1)*VPL)).
+// cs: cos/sin of the position per RoPE pair if already computed (LDS), else
+// computed here.
 template <int D, int DR>
 __device__ void store_record(const Lay &L, float (&x)[(D / 64) > 0 ? D / 64 : 1], int64_t pos,
-                             uint8_t *dst) {
+                             uint8_t *dst, const float2 *cs = nullptr) {
     constexpr int VPL = D / 64;
     constexpr int DN = D - DR;
     const int lane = threadIdx.x & 63;
@@ -36,7 +38,12 @@ __device__ void store_record(const Lay &L, float (&x)[(D / 64) > 0 ? D / 64 : 1]
             int dd = d0 + v;
             if (dd >= DN) {
                 float c, s;
-                rope_cs(L, pos, (dd - DN) / 2, c, s);
+                if (cs) {
+                    c = cs[(dd - DN) / 2].x;
+                    s = cs[(dd - DN) / 2].y;
+                } else {
+                    rope_cs(L, pos, (dd - DN) / 2, c, s);
+                }
                 float a = x[v], b = x[v + 1];
                 x[v] = a * c - b * s;
                 x[v + 1] = a * s + b * c;
@@ -137,14 +144,26 @@ __device__ __forceinline__ uint8_t *state_ptr(const Lay &L, const dsv4_cache &C,
 }
 
 // ---------------------------------------------------------------- decode
-// One workgroup (256 threads) per request.
+// One workgroup (256 threads) per request.  Everything the step reads -- the
+// new token's kv / gate / kI / gI and, when a block completes and its window
+// is short (CSA: 8 tokens), the window's older tokens from the pending ring --
+// is loaded into LDS in one batch of loads, so the step waits on memory once;
+// the pooled entry, the window record and the ring push are then formed from
+// LDS.  (A long window -- HCA, 128 tokens, one entry per 128 steps -- is pooled
+// straight from the ring.)
+constexpr int kStageWin = 8;           // window tokens staged in LDS
+constexpr int kStageFloats = 2 * 512 + 2 * 128;   // floats of one staged token (d <= 512, idx_dim <= 128)
+
+
 template <int D, int DR>
 __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, const void *kv,
                                                          const void *gate, const void *kI,
                                                          const void *gI, const int32_t *req,
                                                          const int32_t *pos) {
     constexpr int VPL = D / 64 > 0 ? D / 64 : 1;
+    __shared__ float tokbuf[kStageWin][kStageFloats];
     __shared__ float pooled[D + 128];
+    __shared__ float2 cs_tab[DR / 2];                // cos/sin of position t (window record and entry)
     const int b = blockIdx.x;
     const int r = req[b];
     const int64_t t = pos[b];
@@ -154,63 +173,112 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
     const int dI = csa ? L.dI : 0;
     uint8_t *st = state_ptr(L, C, r);
     float *pend = (float *)(st + L.pend_off);
-    const int ptf = L.pend_tok_floats;
+    const int ptf = L.pend_tok_floats;               // [kv D][gate D][kI dI][gI dI]
     const bool emit = ((t + 1) % L.m) == 0;
     const int64_t j = (t + 1) / L.m - 1;
     const int64_t s0 = emit ? (j * L.m - (L.wc - L.m) > 0 ? j * L.m - (L.wc - L.m) : 0) : 0;
-    const int n = (int)(t - s0 + 1);
+    const int n = emit ? (int)(t - s0 + 1) : 1;
+    const bool staged = emit && n <= kStageWin;
+    float *newtok = tokbuf[staged ? n - 1 : 0];      // the new token, in ring layout
 
-    // 1. pool the completed block (reads older tokens from the pending ring)
+    // 1. cos/sin of position t (the window record and the entry both sit
+    // there), on the last wave while the others start their loads
+    if (tid >= 192 && tid - 192 < DR / 2) {
+        float c, sn;
+        rope_cs(L, t, tid - 192, c, sn);
+        cs_tab[tid - 192] = make_float2(c, sn);
+    }
+    // 2. one batch of loads into LDS: token slot s of the window (the new one
+    // last), channel c = tid + 256u
+    auto in_tok = [&](int c) {
+        if (c < D) return load_act(kv, (int64_t)b * D + c, L.act);
+        if (c < 2 * D) return load_act(gate, (int64_t)b * D + c - D, L.act);
+        if (c < 2 * D + dI) return load_act(kI, (int64_t)b * dI + c - 2 * D, L.act);
+        return load_act(gI, (int64_t)b * dI + c - 2 * D - dI, L.act);
+    };
+    constexpr int U = (kStageFloats + 255) / 256;
+    {
+        const int nold = staged ? n - 1 : 0;         // older window tokens staged
+        float v[kStageWin][U];
+#pragma unroll
+        for (int s = 0; s < kStageWin; ++s) {
+            if (s < nold) {                          // (wave-uniform)
+                const float *src = pend + ((s0 + s) % L.pend_slots) * ptf;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = tid + 256 * u;
+                    v[s][u] = c < ptf ? src[c] : 0.0f;
+                }
+            }
+        }
+        float vn[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = tid + 256 * u;
+            vn[u] = c < ptf ? in_tok(c) : 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < kStageWin; ++s)
+            if (s < nold) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (tid + 256 * u < ptf) tokbuf[s][tid + 256 * u] = v[s][u];
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (tid + 256 * u < ptf) newtok[tid + 256 * u] = vn[u];
+    }
+    __syncthreads();
+
+    // 2. pool the completed block (per channel: softmax over the window's gate
+    // logits, weighted sum of kv)
     if (emit) {
         for (int c = tid; c < D + dI; c += 256) {
             const bool isk = c >= D;
             const int cc = isk ? c - D : c;
-            const void *vin = isk ? kI : kv;
-            const void *gin = isk ? gI : gate;
-            const int dim = isk ? dI : D;
             const int voff = isk ? 2 * D + cc : cc;
             const int goff = isk ? 2 * D + dI + cc : D + cc;
-            pooled[c] = pool_channel(n, [&](int s, float &v, float &g) {
-                int64_t p = s0 + s;
-                if (p == t) {
-                    v = load_act(vin, (int64_t)b * dim + cc, L.act);
-                    g = load_act(gin, (int64_t)b * dim + cc, L.act);
-                } else {
-                    const float *tok = pend + (p % L.pend_slots) * ptf;
-                    v = tok[voff];
-                    g = tok[goff];
-                }
-            });
+            if (staged) {
+                pooled[c] = pool_channel(n, [&](int s, float &v, float &g) {
+                    v = tokbuf[s][voff];
+                    g = tokbuf[s][goff];
+                });
+            } else {
+                pooled[c] = pool_channel(n, [&](int s, float &v, float &g) {
+                    const int64_t p = s0 + s;
+                    if (p == t) {
+                        v = newtok[voff];
+                        g = newtok[goff];
+                    } else {
+                        const float *tok = pend + (p % L.pend_slots) * ptf;
+                        v = tok[voff];
+                        g = tok[goff];
+                    }
+                });
+            }
         }
     }
     __syncthreads();
-    // 2. push the raw token into the pending ring
+    // 3. push the raw token into the pending ring
     {
         float *tok = pend + (t % L.pend_slots) * ptf;
-        for (int c = tid; c < ptf; c += 256) {
-            float v;
-            if (c < D) v = load_act(kv, (int64_t)b * D + c, L.act);
-            else if (c < 2 * D) v = load_act(gate, (int64_t)b * D + c - D, L.act);
-            else if (c < 2 * D + dI) v = load_act(kI, (int64_t)b * dI + c - 2 * D, L.act);
-            else v = load_act(gI, (int64_t)b * dI + c - 2 * D - dI, L.act);
-            tok[c] = v;
-        }
+        for (int c = tid; c < ptf; c += 256) tok[c] = newtok[c];
     }
-    // 3. window record of the new token (wave 0)
+    // 4. window record of the new token (wave 0)
     if (wave == 0 && L.W > 0) {
         float x[VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) x[v] = load_act(kv, (int64_t)b * D + lane * VPL + v, L.act);
-        store_record<D, DR>(L, x, t, st + (t % L.W) * L.rec_bytes);
+        for (int v = 0; v < VPL; ++v) x[v] = newtok[lane * VPL + v];
+        store_record<D, DR>(L, x, t, st + (t % L.W) * L.rec_bytes, cs_tab);
     }
-    // 4. the completed entry (wave 1) and its index key (wave 2)
+    // 5. the completed entry (wave 1) and its index key (wave 2)
     if (emit && wave == 1) {
         uint8_t *dst = entry_ptr(L, C, r, j);
         if (dst) {
             float x[VPL];
 #pragma unroll
             for (int v = 0; v < VPL; ++v) x[v] = pooled[lane * VPL + v];
-            store_record<D, DR>(L, x, t, dst);
+            store_record<D, DR>(L, x, t, dst, cs_tab);   // entry position m*j+m-1 = t
         }
     }
     if (emit && csa && wave == 2) {
