@@ -30,9 +30,16 @@ FLAGS = [
 ]
 
 
+# Per-file code-generation options.  Attention: MFMA accumulators in
+# ordinary VGPRs (the online-softmax rescale is VALU work on them; with the
+# accumulators in AGPRs the compiler copies all of them back and forth on
+# every chunk).
+FILE_FLAGS = {"k_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

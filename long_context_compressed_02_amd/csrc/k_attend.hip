@@ -27,12 +27,14 @@
 // hwcomputing.csdn.net section 四): nothing is split across workgroups -- each
 // (query, 16-head group) is reduced by one workgroup in a fixed order that
 // depends on nothing but the query (see the decomposition below), so a
-// query's output is bitwise the same whatever the batch.  LO (for an
-// unsaturated GPU) gives that workgroup 16 waves; HI (for a saturated GPU)
-// gives it 4 waves that do the same work in sequence, so that several
-// workgroups share a compute unit.  They agree bit for bit.  The 8 workgroups
-// of a query are placed on one XCD, so its gathered records are fetched into
-// one L2.
+// query's output is bitwise the same whatever the batch.  Two kernels run
+// that decomposition: k_attend_lo (for an unsaturated GPU) gives the
+// workgroup 4 waves, one per subset, each over all dims; k_attend (HI, for a
+// saturated GPU) gives it 2 waves, one per dim part, that take the subsets one
+// after another, so that several workgroups share a compute unit.  Both sum
+// every logit from the same partial dot products and fold the subsets in the
+// same order: they agree bit for bit.  The 8 workgroups of a query are placed
+// on one XCD, so its gathered records are fetched into one L2.
 //
 // Latency: all record addresses of a query (top-k index -> block table ->
 // record) are resolved once into an LDS locator array before the chunk loop,
@@ -167,11 +169,8 @@ __device__ __forceinline__ const uint8_t *loc_addr(const AttnArgs &A, const Quer
 // (a_q: code dims of part q, s: the record's scale, r: RoPE dims).  The four
 // subset states are then folded left to right:
 //     acc = s0;  acc = fold(acc, s1);  acc = fold(acc, s2);  acc = fold(acc, s3)
-// LO (8 waves: 4 subsets x 2 parts) runs the subsets at once and folds
-// through LDS; HI (2 waves: the parts) runs the subsets one after another and
-// folds in registers.  Same operations in the same order: HI and LO agree bit
-// for bit.  A wave holds half of the output accumulators, so two waves share
-// a SIMD and hide each other's LDS and memory latency.
+// HI (2 waves: the parts) runs the subsets one after another and folds in
+// registers; k_attend_lo below runs them at once and folds through LDS.
 constexpr int kChunk = 32;     // records per chunk (the k of one PV MFMA)
 constexpr int kSubsets = 4;
 constexpr int kParts = 2;     // dim parts (each wave holds one part of the output)
@@ -242,7 +241,7 @@ struct AttnShape {
     static_assert(NLD % kParts == 0, "a chunk's loads split evenly over the dim parts");
 };
 
-// NSW subset waves per dim part: LO = 4 (8 waves), HI = 1 (2 waves).
+// NSW subset waves per dim part (1: the HI kernel, 2 waves).
 template <int D, int DR, int NSW, bool CSA, bool PREFILL>
 __global__ __launch_bounds__(64 * kParts * NSW) void k_attend(AttnArgs A) {
     using Sh = AttnShape<D, DR>;
@@ -565,8 +564,8 @@ __global__ __launch_bounds__(64 * kParts * NSW) void k_attend(AttnArgs A) {
         };
 
         u32x4 pre[LDQ];
-        if constexpr (NSW == 1) {
-            // HI: the subsets one after another on the same 2 waves
+        {
+            // the subsets one after another on the same 2 waves
             AttnState<DBQ> acc, cur;
             state_clear(acc);
             int first = -1;                              // first chunk in processing order
@@ -602,54 +601,424 @@ __global__ __launch_bounds__(64 * kParts * NSW) void k_attend(AttnArgs A) {
                 for (int i = 0; i < DBQ; ++i)
                     if (DBQ * DQ + i < NDB) emit(acc.m, acc.l, DBQ * DQ + i, acc.O[i]);
             }
-        } else {
-            // LO: subset sw on this wave; all subsets advance together, one chunk
-            // each per step
-            AttnState<DBQ> S;
-            state_clear(S);
-            const int nsteps = (nchunks + kSubsets - 1) / kSubsets;
-            if (sw < nchunks) issue(pre, sw);
-    #pragma unroll 1
-            for (int t = 0; t < nsteps; ++t) {
-                const int ck = kSubsets * t + sw;
-                const int nx = ck + kSubsets;
-                step(S, ck < nchunks ? ck : -1, pre, nx < nchunks ? nx : -1);
-            }
-            // fold the four subsets' states (per dim part) through LDS
-            __syncthreads();
-            constexpr int NWV = kParts * NSW;
-            float2 *ml = (float2 *)smem;                 // [wave][64]
-            f32x4 *ob = (f32x4 *)(smem + NWV * 64 * 8);  // [wave][DBQ][64]
-            ml[wave * 64 + lane] = make_float2(S.m, S.l);
-    #pragma unroll
-            for (int b = 0; b < DBQ; ++b) ob[(wave * DBQ + b) * 64 + lane] = S.O[b];
-            __syncthreads();
-            // wave (sw, DQ) finishes dim blocks sw, sw+4, ... of part DQ
-            float m = ml[(0 * kParts + DQ) * 64 + lane].x, l = ml[(0 * kParts + DQ) * 64 + lane].y;
-            float fw[kSubsets][2];                       // fold s: factors of the folded part and of state s
-    #pragma unroll
-            for (int s = 1; s < kSubsets; ++s) {
-                const float2 b = ml[(s * kParts + DQ) * 64 + lane];
-                float mm, ll, fa, fb;
-                fold_scales(m, l, b.x, b.y, mm, ll, fa, fb);
-                fw[s][0] = fa;
-                fw[s][1] = fb;
-                m = mm;
-                l = ll;
-            }
-    #pragma unroll
-            for (int b = sw; b < DBQ; b += kSubsets) {
-                f32x4 o = ob[((0 * kParts + DQ) * DBQ + b) * 64 + lane];
-    #pragma unroll
-                for (int s = 1; s < kSubsets; ++s)
-                    o = fold_o(o, fw[s][0], ob[((s * kParts + DQ) * DBQ + b) * 64 + lane], fw[s][1]);
-                if (head_ok && DBQ * DQ + b < NDB) emit(m, l, DBQ * DQ + b, o);
-            }
         }
     };
     if (dq == 0) part_body(std::integral_constant<int, 0>());
     else part_body(std::integral_constant<int, kParts - 1>());
 
+}
+
+// ---------------------------------------------------------------- the LO kernel
+// Same decomposition and the same operations as k_attend, laid out for an
+// unsaturated GPU: one workgroup of four waves per (query, 16-head group),
+// wave s reducing subset s over all dims.  A wave stages its chunks through
+// its own LDS buffer and exchanges nothing with the other waves until the
+// final fold, so its chunk loop has no workgroup barrier, and it keeps the
+// loads of its next two chunks in flight.  Its logits are summed from the
+// same partial dot products as k_attend's dim parts (chain q over the code
+// pairs [QPP*q, QPP*q + QPP), then a0 + a1, then the scale and the RoPE
+// chain), so the two kernels agree bit for bit.
+template <int D, int DR>
+struct LoShape {
+    using Sh = AttnShape<D, DR>;
+    // per-wave LDS: locators [cpw][32] | valid masks [cpw] | RoPE table | chunk buffer
+    static __host__ __device__ int wave_bytes(int cpw) {
+        return cpw * kChunk * 4 + (cpw * 4 + 15) / 16 * 16 + (DR / 2 * 8 + 15) / 16 * 16 + Sh::BUF;
+    }
+    static constexpr int FOLD = kSubsets * 64 * 8 + kSubsets * Sh::NDB * 64 * 16;
+};
+
+constexpr int kLoPrefetch = 2;
+
+__device__ __forceinline__ void wave_lds_fence() {
+    // the wave's LDS accesses are performed in order; this keeps the compiler
+    // from moving one lane's LDS reads above another lane's writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int DR, bool CSA, bool PREFILL>
+__global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
+    using Sh = AttnShape<D, DR>;
+    constexpr int NCH = Sh::NCH, RCH = Sh::RCH, CREC = Sh::CREC, PPR = Sh::PPR, LW = Sh::LW, RPI = Sh::RPI;
+    constexpr int NLD = Sh::NLD, RS = Sh::RS, SWZ = Sh::SWZ;
+    constexpr int KP = Sh::KP, KR = Sh::KR, QPP = Sh::QPP, NDB = Sh::NDB, DN = Sh::DN;
+    constexpr int RES = 8;                               // locators per lane per resolution batch
+    constexpr int PFD = kLoPrefetch;                     // chunks of loads in flight per wave
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const Lay &L = A.L;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int sw = __builtin_amdgcn_readfirstlane(tid >> 6);   // subset of this wave
+
+    const int lin = blockIdx.x, x8 = lin & 7, u8 = lin >> 3;
+    const int qi = (u8 / A.nhg) * 8 + x8;
+    const int hg = u8 % A.nhg;
+    if (qi >= A.nq) return;
+    const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
+    if (!Q.ok) return;
+    const int head = hg * 16 + c16;
+    const bool head_ok = head < L.H;
+    const int n_list = (int)Q.n_list;
+    const int nchunks = (n_list + kChunk - 1) / kChunk;
+    const int cpw = (nchunks + kSubsets - 1) / kSubsets;                    // chunks of wave 0 (the most)
+    int mine = sw < nchunks ? (nchunks - 1 - sw) / kSubsets + 1 : 0;        // chunks sw, sw+4, ...
+    uint8_t *wb = smem + sw * LoShape<D, DR>::wave_bytes(cpw);
+    int32_t *locs = (int32_t *)wb;                                          // [t][32]: chunk sw + 4t
+    uint32_t *vmask = (uint32_t *)(wb + cpw * kChunk * 4);
+    float2 *rtab = (float2 *)(wb + cpw * kChunk * 4 + (cpw * 4 + 15) / 16 * 16);
+    uint8_t *buf = (uint8_t *)rtab + (DR / 2 * 8 + 15) / 16 * 16;
+
+    // ---- the query: raw bf16/fp32 values of this lane's fragments (loaded
+    // first, so they travel with the locator reads)
+    const int64_t qbase = ((int64_t)Q.qrow * L.H + head) * D;
+    auto q8 = [&](int dd, float (&v)[8]) {
+        if (L.act == DSV4_DT_BF16) {
+            const uint4 u = *(const uint4 *)((const uint16_t *)A.q + qbase + dd);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = __uint_as_float(w[j] << 16);
+                v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        } else {
+            const float4 a = *(const float4 *)((const float *)A.q + qbase + dd);
+            const float4 b = *(const float4 *)((const float *)A.q + qbase + dd + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+    };
+    // code pieces: bf16 queries are the MFMA operand bits as they are
+    bf16x8 Qn[KP][2];
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ch = 4 * kp + g;
+            bf16x8 f;
+            if (L.act == DSV4_DT_BF16) {
+                uint4 u = make_uint4(0, 0, 0, 0);
+                if (head_ok && ch < NCH) u = *(const uint4 *)((const uint16_t *)A.q + qbase + 16 * ch + 8 * h);
+                f = as_bf16x8(u);
+            } else {
+                float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (head_ok && ch < NCH) q8(16 * ch + 8 * h, v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) f[j] = f2bf(v[j]);
+            }
+            Qn[kp][h] = f;
+        }
+    // RoPE pieces: raw bits now (8 bf16, or 8 fp32 in two halves), rotated
+    // further down, so that no wait on these loads holds up the locator reads
+    u32x4 qrr[KR][2];
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks) {
+        const int ch = 4 * ks + g;
+        qrr[ks][0] = qrr[ks][1] = (u32x4){0, 0, 0, 0};
+        if (head_ok && ch < RCH) {
+            if (L.act == DSV4_DT_BF16) {
+                qrr[ks][0] = *(const u32x4 *)((const uint16_t *)A.q + qbase + DN + 8 * ch);
+            } else {
+                qrr[ks][0] = *(const u32x4 *)((const float *)A.q + qbase + DN + 8 * ch);
+                qrr[ks][1] = *(const u32x4 *)((const float *)A.q + qbase + DN + 8 * ch + 4);
+            }
+        }
+    }
+
+    // ---- locators of this wave's records, RES per lane per batch: the top-k
+    // reads of a batch, then its block-table reads, each all in flight at
+    // once (indices are clamped instead of branched around).  A masked record
+    // is replaced by a stand-in that is always valid and finite -- the
+    // query's own window record -- and keeps weight 0 through the valid mask.
+    const int64_t n_ent = Q.n_ent;
+    const int32_t own = Q.n_win > 0 ? record_loc<CSA, PREFILL>(A, Q, Q.n_list - 1) : kMasked;
+    int32_t first_ok = -1;                               // (no window: the wave's first valid record stands in)
+    for (int e0 = 0; e0 < mine * kChunk; e0 += 64 * RES) {
+        int64_t p[RES], j[RES];
+#pragma unroll
+        for (int u = 0; u < RES; ++u) {
+            const int e = e0 + 64 * u + lane;
+            p[u] = (int64_t)(sw + kSubsets * (e >> 5)) * kChunk + (e & 31);
+            if (e >= mine * kChunk) p[u] = Q.n_list;   // past the list: masked
+            j[u] = p[u];
+            if constexpr (CSA) {
+                const int64_t pc = p[u] < n_ent ? p[u] : (n_ent > 0 ? n_ent - 1 : 0);
+                j[u] = A.topk[(int64_t)Q.qrow * L.topk + pc];
+            }
+        }
+        int32_t lc[RES];
+#pragma unroll
+        for (int u = 0; u < RES; ++u) {
+            const bool ent = p[u] < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+            const int64_t blk = ent ? (j[u] * L.m) / kBlockTokens : 0;
+            const int32_t bid = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
+            int32_t l_ent = (ent && bid >= 0 && bid < A.C.n_blocks) ? (int32_t)(bid * L.epb + j[u] % L.epb) : kMasked;
+            const int64_t w = p[u] - n_ent;
+            int32_t l_win = kMasked;
+            if (w >= 0 && w < Q.n_win) {
+                const int64_t ts = Q.t - Q.n_win + 1 + w;
+                if constexpr (PREFILL) l_win = (int32_t)(-1 - (Q.win_base + (ts - (Q.pos0 - L.W))));
+                else l_win = (int32_t)(-1 - (ts % L.W));
+            }
+            lc[u] = p[u] < n_ent ? l_ent : l_win;
+        }
+#pragma unroll
+        for (int u = 0; u < RES; ++u) {
+            const int e = e0 + 64 * u + lane;
+            const uint64_t vb = __builtin_amdgcn_ballot_w64(lc[u] != kMasked);
+            if (first_ok < 0 && vb != 0)
+                first_ok = __builtin_amdgcn_readlane(lc[u], (int)__builtin_ctzll(vb));
+            if (e < mine * kChunk) locs[e] = lc[u] != kMasked ? lc[u] : own;
+            const int t0 = (e0 + 64 * u) >> 5;
+            if (lane == 0) {
+                if (t0 < mine) vmask[t0] = (uint32_t)vb;
+                if (t0 + 1 < mine) vmask[t0 + 1] = (uint32_t)(vb >> 32);
+            }
+        }
+    }
+    if (own == kMasked) {                                // no window (W = 0)
+        if (first_ok < 0) mine = 0;                      // nothing valid: the subset contributes nothing
+        wave_lds_fence();
+        for (int e = lane; e < mine * kChunk; e += 64)
+            if (locs[e] == kMasked) locs[e] = first_ok;
+    }
+    if (lane < DR / 2) {
+        float c, sn;
+        rope_cs(L, Q.t, lane, c, sn);
+        rtab[lane] = make_float2(c, sn);
+    }
+    wave_lds_fence();
+
+    // ---- chunk loads (same line-wise pattern as k_attend, all NLD loads of a
+    // chunk on this wave)
+    const int ld_a = lane / LW, ld_b = lane % LW;
+    auto slot = [&](int c, int r) { return buf + (r * RS + c + (r >> 4) * SWZ) * 16; };
+    auto issue = [&](u32x4 (&pre)[NLD], int t) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int r = RPI * (i / (PPR / LW)) + ld_a, c = LW * (i % (PPR / LW)) + ld_b;
+            pre[i] = *(const u32x4 *)(loc_addr<PREFILL>(A, Q, locs[t * kChunk + r]) + 16 * c);
+        }
+    };
+    auto stage = [&](const u32x4 (&pre)[NLD]) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int r = RPI * (i / (PPR / LW)) + ld_a, c = LW * (i % (PPR / LW)) + ld_b;
+            *(u32x4 *)slot(c, r) = pre[i];
+        }
+    };
+    u32x4 R0[NLD], R1[PFD == 2 ? NLD : 1];
+    if (mine > 0) issue(R0, 0);
+    if constexpr (PFD == 2)
+        if (mine > 1) issue(R1, 1);
+
+    // ---- RoPE query fragments, rotated at t (the code fragments are above):
+    // code pair kp holds piece 4kp+g, RoPE step ks RoPE piece 4ks+g
+    bf16x8 Qr[KR];
+#pragma unroll
+    for (int ks = 0; ks < KR; ++ks) {
+        const int ch = 4 * ks + g;
+        float qr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (L.act == DSV4_DT_BF16) {
+                const uint32_t w = qrr[ks][0][j >> 1];
+                qr[j] = __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+            } else {
+                qr[j] = __uint_as_float(qrr[ks][j >> 2][j & 3]);
+            }
+        }
+        bf16x8 f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            float a = 0.0f, b = 0.0f;
+            if (ch < RCH) {
+                const float2 cs = rtab[(8 * ch + j) / 2];
+                a = qr[j] * cs.x - qr[j + 1] * cs.y;
+                b = qr[j] * cs.y + qr[j + 1] * cs.x;
+            }
+            f[j] = f2bf(a);
+            f[j + 1] = f2bf(b);
+        }
+        Qr[ks] = f;
+    }
+    const float tau2 = L.tau * 1.4426950408889634f;   // logits in base 2
+
+    // ---- one chunk: logits from the partial chains, online softmax, O^T += V^T P^T
+    AttnState<NDB> S;
+    state_clear(S);
+    auto compute = [&](int t) {
+        float lg[2][4], sc[2][4];
+        const uint32_t vm = vmask[t];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            // all of the block's operand pieces first (their LDS latencies overlap),
+            // then the chains interleaved: chain q keeps its pairs in order
+            u32x4 u[KP], ur[KR];
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp) {
+                const int ch = 4 * kp + g;
+                u[kp] = (u32x4){0, 0, 0, 0};
+                if (NCH % 4 == 0 || ch < NCH) u[kp] = *(const u32x4 *)slot(ch, 16 * rb + c16);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KR; ++ks) {
+                const int ch = 4 * ks + g;
+                ur[ks] = (u32x4){0, 0, 0, 0};
+                if (RCH % 4 == 0 || ch < RCH) ur[ks] = *(const u32x4 *)slot(NCH + ch, 16 * rb + c16);
+            }
+            f32x4 x[kParts], xr = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int q = 0; q < kParts; ++q) x[q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int e = 0; e < QPP; ++e)
+#pragma unroll
+                for (int q = 0; q < kParts; ++q) {
+                    const int kp = QPP * q + e;
+                    if (kp < KP) {
+                        x[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8(u[kp][0], u[kp][1]), Qn[kp][0], x[q], 0, 0, 0);
+                        x[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8(u[kp][2], u[kp][3]), Qn[kp][1], x[q], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+            for (int ks = 0; ks < KR; ++ks) {
+                union { u32x4 v; bf16x8 b; } cv;
+                cv.v = ur[ks];
+                xr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Qr[ks], xr, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rb + 4 * g + i;
+                const bool ok = (vm >> r) & 1u;
+                sc[rb][i] = *(const float *)slot(CREC - 1, r);
+                float a = x[0][i];
+#pragma unroll
+                for (int q = 1; q < kParts; ++q) a = a + x[q][i];
+                lg[rb][i] = ok ? tau2 * (sc[rb][i] * a + xr[i]) : -INFINITY;
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one record block's operands at a time
+        }
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, lg[rb][i]);
+        cmax = head_max(cmax);
+        const float m_new = fmaxf(S.m, cmax);
+        float p[2][4];
+        float alpha = 1.0f;
+        if (m_new == -INFINITY) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[rb][i] = 0.0f;
+        } else {
+            alpha = __builtin_amdgcn_exp2f(S.m - m_new);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[rb][i] = __builtin_amdgcn_exp2f(lg[rb][i] - m_new);
+        }
+        float ps = 0.0f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ps = ps + p[rb][i];
+        ps = head_sum(ps);
+        S.l = S.l * alpha + ps;
+        S.m = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) S.O[i] = S.O[i] * alpha;
+        }
+        bf16x8 Pn, Pr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int rb = j >> 2, i = j & 3;
+            Pn[j] = f2bf(p[rb][i] * sc[rb][i]);
+            Pr[j] = f2bf(p[rb][i]);
+        }
+        const int trow = c16 >> 1, thalf = c16 & 1;
+        const int trec = (trow < 4 ? 0 : 16) + 4 * g + (trow & 3);
+        const int r16 = c16 >> 2, q16 = c16 & 3;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            if (db % 4 == 0) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+            if (db < NCH) {
+                const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_p)(slot(db, trec) + 8 * thalf));
+                S.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8((uint32_t)v[0], (uint32_t)v[1]), Pn, S.O[db], 0,
+                                                                  0, 0);
+            } else {
+                const int ch = NCH + 2 * (db - NCH) + (q16 >> 1);
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(slot(ch, 4 * g + r16) + 8 * (q16 & 1)));
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(slot(ch, 16 + 4 * g + r16) + 8 * (q16 & 1)));
+                union { i16x4 s[2]; bf16x8 b; } cv;
+                cv.s[0] = lo;
+                cv.s[1] = hi;
+                S.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Pr, S.O[db], 0, 0, 0);
+            }
+        }
+    };
+    auto step = [&](u32x4 (&pre)[NLD], int t) {
+        wave_lds_fence();                    // the previous chunk's reads come first
+        stage(pre);
+        if (t + PFD < mine) issue(pre, t + PFD);
+        wave_lds_fence();                    // staged chunk visible to the whole wave
+        compute(t);
+    };
+    if constexpr (PFD == 2) {
+#pragma unroll 1
+        for (int t = 0; t < mine; t += 2) {
+            step(R0, t);
+            if (t + 1 < mine) step(R1, t + 1);
+        }
+    } else {
+#pragma unroll 1
+        for (int t = 0; t < mine; ++t) step(R0, t);
+    }
+
+    // ---- fold the four subset states left to right through LDS (the same
+    // operations as k_attend's sequential fold); wave s emits dim blocks s, s+4, ...
+    __syncthreads();
+    float2 *ml = (float2 *)smem;                                 // [subset][64]
+    f32x4 *ob = (f32x4 *)(smem + kSubsets * 64 * 8);             // [subset][NDB][64]
+    ml[sw * 64 + lane] = make_float2(S.m, S.l);
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) ob[(sw * NDB + b) * 64 + lane] = S.O[b];
+    __syncthreads();
+    float m = ml[lane].x, l = ml[lane].y;
+    float fw[kSubsets][2];
+#pragma unroll
+    for (int s = 1; s < kSubsets; ++s) {
+        const float2 b = ml[s * 64 + lane];
+        float mm, ll, fa, fb;
+        fold_scales(m, l, b.x, b.y, mm, ll, fa, fb);
+        fw[s][0] = fa;
+        fw[s][1] = fb;
+        m = mm;
+        l = ll;
+    }
+    if (!head_ok) return;
+    const float z = A.sinks[head] * 1.4426950408889634f;
+    const float M = fmaxf(m, z);
+    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    const float den = l * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
+    const float cf = den > 0.0f ? f / den : 0.0f;
+    const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
+#pragma unroll
+    for (int b = sw; b < NDB; b += kSubsets) {
+        f32x4 o = ob[b * 64 + lane];
+#pragma unroll
+        for (int s = 1; s < kSubsets; ++s) o = fold_o(o, fw[s][0], ob[(s * NDB + b) * 64 + lane], fw[s][1]);
+        const int dd = b * 16 + 4 * g;
+        if (L.act == DSV4_DT_BF16) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 v = {f2bf(o[0] * cf), f2bf(o[1] * cf), f2bf(o[2] * cf), f2bf(o[3] * cf)};
+            *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
+        } else {
+            *(float4 *)((float *)A.out + obase + dd) = make_float4(o[0] * cf, o[1] * cf, o[2] * cf, o[3] * cf);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -667,8 +1036,15 @@ int64_t attend_lds_bytes(int64_t list_max) {
     return stream > fold ? stream : fold;
 }
 
+template <int D, int DR>
+int64_t attend_lo_lds_bytes(int64_t list_max) {
+    const int64_t nch = (list_max + kChunk - 1) / kChunk, cpw = (nch + kSubsets - 1) / kSubsets;
+    const int64_t stream = kSubsets * (int64_t)LoShape<D, DR>::wave_bytes((int)cpw);
+    return stream > LoShape<D, DR>::FOLD ? stream : LoShape<D, DR>::FOLD;
+}
+
 int64_t attend_lds_max(const Lay &L, int64_t list_max) {
-    const int64_t lo = L.d == 512 ? attend_lds_bytes<512, 64, 4>(list_max) : attend_lds_bytes<64, 16, 4>(list_max);
+    const int64_t lo = L.d == 512 ? attend_lo_lds_bytes<512, 64>(list_max) : attend_lo_lds_bytes<64, 16>(list_max);
     const int64_t hi = L.d == 512 ? attend_lds_bytes<512, 64, 1>(list_max) : attend_lds_bytes<64, 16, 1>(list_max);
     return lo > hi ? lo : hi;
 }
@@ -690,8 +1066,24 @@ static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
 }
 
 template <int D, int DR, bool CSA, bool PREFILL>
+static hipError_t launch_lo(const AttnArgs &A, hipStream_t s) {
+    const int64_t lds = attend_lo_lds_bytes<D, DR>(attend_list_max(A.L, A.C, CSA));
+    static int64_t attr = -1;
+    if (attr < lds) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_attend_lo<D, DR, CSA, PREFILL>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = lds;
+    }
+    const int groups = (A.nq + 7) / 8;
+    hipLaunchKernelGGL((k_attend_lo<D, DR, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kSubsets), (size_t)lds,
+                       s, A);
+    return hipGetLastError();
+}
+
+template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_t(const AttnArgs &A, bool hi, hipStream_t s) {
-    return hi ? launch_gr<D, DR, 1, CSA, PREFILL>(A, s) : launch_gr<D, DR, 4, CSA, PREFILL>(A, s);
+    return hi ? launch_gr<D, DR, 1, CSA, PREFILL>(A, s) : launch_lo<D, DR, CSA, PREFILL>(A, s);
 }
 
 hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s) {
