@@ -626,6 +626,9 @@ struct LoShape {
         return cpw * kChunk * 4 + (cpw * 4 + 15) / 16 * 16 + (DR / 2 * 8 + 15) / 16 * 16 + Sh::BUF;
     }
     static constexpr int FOLD = kSubsets * 64 * 8 + kSubsets * Sh::NDB * 64 * 16;
+    // the workgroup's 16 query rows (fp32 at most), rows padded by one piece
+    static constexpr int QROW = D * 4 + 16;
+    static constexpr int QBYTES = 16 * QROW;
 };
 
 constexpr int kLoPrefetch = 2;
@@ -669,60 +672,23 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     float2 *rtab = (float2 *)(wb + cpw * kChunk * 4 + (cpw * 4 + 15) / 16 * 16);
     uint8_t *buf = (uint8_t *)rtab + (DR / 2 * 8 + 15) / 16 * 16;
 
-    // ---- the query: raw bf16/fp32 values of this lane's fragments (loaded
-    // first, so they travel with the locator reads)
-    const int64_t qbase = ((int64_t)Q.qrow * L.H + head) * D;
-    auto q8 = [&](int dd, float (&v)[8]) {
-        if (L.act == DSV4_DT_BF16) {
-            const uint4 u = *(const uint4 *)((const uint16_t *)A.q + qbase + dd);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    // ---- the query: the workgroup's 16 rows are fetched once (each thread a
+    // few 16-byte pieces, clamped to the last head) and parked in LDS after
+    // the locators resolve; rows are padded by one piece, so the fragment
+    // reads below hit distinct banks
+    const int ab = L.act == DSV4_DT_BF16 ? 2 : 4;
+    const int qrow_bytes = D * ab;                       // bytes of one query row
+    constexpr int QPT = (16 * D * 4 / 16 + 64 * kSubsets - 1) / (64 * kSubsets);   // pieces per thread (fp32 bound)
+    uint8_t *qlds = smem + kSubsets * LoShape<D, DR>::wave_bytes(cpw);
+    const int npc = qrow_bytes;                          // 16-byte pieces of the 16 rows
+    u32x4 qpc[QPT];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[2 * j] = __uint_as_float(w[j] << 16);
-                v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-            }
-        } else {
-            const float4 a = *(const float4 *)((const float *)A.q + qbase + dd);
-            const float4 b = *(const float4 *)((const float *)A.q + qbase + dd + 4);
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        }
-    };
-    // code pieces: bf16 queries are the MFMA operand bits as they are
-    bf16x8 Qn[KP][2];
-#pragma unroll
-    for (int kp = 0; kp < KP; ++kp)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ch = 4 * kp + g;
-            bf16x8 f;
-            if (L.act == DSV4_DT_BF16) {
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (head_ok && ch < NCH) u = *(const uint4 *)((const uint16_t *)A.q + qbase + 16 * ch + 8 * h);
-                f = as_bf16x8(u);
-            } else {
-                float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (head_ok && ch < NCH) q8(16 * ch + 8 * h, v);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) f[j] = f2bf(v[j]);
-            }
-            Qn[kp][h] = f;
-        }
-    // RoPE pieces: raw bits now (8 bf16, or 8 fp32 in two halves), rotated
-    // further down, so that no wait on these loads holds up the locator reads
-    u32x4 qrr[KR][2];
-#pragma unroll
-    for (int ks = 0; ks < KR; ++ks) {
-        const int ch = 4 * ks + g;
-        qrr[ks][0] = qrr[ks][1] = (u32x4){0, 0, 0, 0};
-        if (head_ok && ch < RCH) {
-            if (L.act == DSV4_DT_BF16) {
-                qrr[ks][0] = *(const u32x4 *)((const uint16_t *)A.q + qbase + DN + 8 * ch);
-            } else {
-                qrr[ks][0] = *(const u32x4 *)((const float *)A.q + qbase + DN + 8 * ch);
-                qrr[ks][1] = *(const u32x4 *)((const float *)A.q + qbase + DN + 8 * ch + 4);
-            }
-        }
+    for (int i = 0; i < QPT; ++i) {
+        const int pc = tid + 64 * kSubsets * i;          // piece index over the 16 rows
+        const int hr = pc / (qrow_bytes / 16), off = (pc % (qrow_bytes / 16)) * 16;
+        const int hq = hg * 16 + hr < L.H ? hg * 16 + hr : L.H - 1;
+        if (pc < npc)
+            qpc[i] = *(const u32x4 *)((const uint8_t *)A.q + ((int64_t)Q.qrow * L.H + hq) * qrow_bytes + off);
     }
 
     // ---- locators of this wave's records, RES per lane per batch: the top-k
@@ -733,61 +699,65 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     const int64_t n_ent = Q.n_ent;
     const int32_t own = Q.n_win > 0 ? record_loc<CSA, PREFILL>(A, Q, Q.n_list - 1) : kMasked;
     int32_t first_ok = -1;                               // (no window: the wave's first valid record stands in)
-    for (int e0 = 0; e0 < mine * kChunk; e0 += 64 * RES) {
-        int64_t p[RES], j[RES];
+    auto resolve = [&](int t_lo, int t_hi) {             // chunk ordinals [t_lo, t_hi) of this wave
+        for (int e0 = t_lo * kChunk; e0 < t_hi * kChunk; e0 += 64 * RES) {
+            // entries in this batch at all?  (wave-uniform: the window needs no reads)
+            const bool any_ent = (int64_t)(sw + kSubsets * (e0 >> 5)) * kChunk < n_ent;
+            int64_t p[RES], j[RES];
+            int32_t bid[RES];
 #pragma unroll
-        for (int u = 0; u < RES; ++u) {
-            const int e = e0 + 64 * u + lane;
-            p[u] = (int64_t)(sw + kSubsets * (e >> 5)) * kChunk + (e & 31);
-            if (e >= mine * kChunk) p[u] = Q.n_list;   // past the list: masked
-            j[u] = p[u];
-            if constexpr (CSA) {
-                const int64_t pc = p[u] < n_ent ? p[u] : (n_ent > 0 ? n_ent - 1 : 0);
-                j[u] = A.topk[(int64_t)Q.qrow * L.topk + pc];
+            for (int u = 0; u < RES; ++u) {
+                const int e = e0 + 64 * u + lane;
+                p[u] = (int64_t)(sw + kSubsets * (e >> 5)) * kChunk + (e & 31);
+                if (e >= t_hi * kChunk) p[u] = Q.n_list;   // past the range: masked
+                j[u] = p[u];
+                bid[u] = -1;
+            }
+            if (any_ent) {
+                if constexpr (CSA) {
+#pragma unroll
+                    for (int u = 0; u < RES; ++u) {
+                        const int64_t pc = p[u] < n_ent ? p[u] : (n_ent > 0 ? n_ent - 1 : 0);
+                        j[u] = A.topk[(int64_t)Q.qrow * L.topk + pc];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < RES; ++u) {
+                    const bool ent = p[u] < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+                    const int64_t blk = ent ? (j[u] * L.m) / kBlockTokens : 0;
+                    bid[u] = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
+                }
+            }
+            int32_t lc[RES];
+#pragma unroll
+            for (int u = 0; u < RES; ++u) {
+                const bool ent = p[u] < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+                const int32_t l_ent =
+                    (ent && bid[u] >= 0 && bid[u] < A.C.n_blocks) ? (int32_t)(bid[u] * L.epb + j[u] % L.epb) : kMasked;
+                const int64_t w = p[u] - n_ent;
+                int32_t l_win = kMasked;
+                if (w >= 0 && w < Q.n_win) {
+                    const int64_t ts = Q.t - Q.n_win + 1 + w;
+                    if constexpr (PREFILL) l_win = (int32_t)(-1 - (Q.win_base + (ts - (Q.pos0 - L.W))));
+                    else l_win = (int32_t)(-1 - (ts % L.W));
+                }
+                lc[u] = p[u] < n_ent ? l_ent : l_win;
+            }
+#pragma unroll
+            for (int u = 0; u < RES; ++u) {
+                const int e = e0 + 64 * u + lane;
+                const uint64_t vb = __builtin_amdgcn_ballot_w64(lc[u] != kMasked);
+                if (first_ok < 0 && vb != 0)
+                    first_ok = __builtin_amdgcn_readlane(lc[u], (int)__builtin_ctzll(vb));
+                if (e < t_hi * kChunk) locs[e] = lc[u] != kMasked ? lc[u] : own;
+                const int t0 = (e0 + 64 * u) >> 5;
+                if (lane == 0) {
+                    if (t0 < t_hi) vmask[t0] = (uint32_t)vb;
+                    if (t0 + 1 < t_hi) vmask[t0 + 1] = (uint32_t)(vb >> 32);
+                }
             }
         }
-        int32_t lc[RES];
-#pragma unroll
-        for (int u = 0; u < RES; ++u) {
-            const bool ent = p[u] < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
-            const int64_t blk = ent ? (j[u] * L.m) / kBlockTokens : 0;
-            const int32_t bid = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
-            int32_t l_ent = (ent && bid >= 0 && bid < A.C.n_blocks) ? (int32_t)(bid * L.epb + j[u] % L.epb) : kMasked;
-            const int64_t w = p[u] - n_ent;
-            int32_t l_win = kMasked;
-            if (w >= 0 && w < Q.n_win) {
-                const int64_t ts = Q.t - Q.n_win + 1 + w;
-                if constexpr (PREFILL) l_win = (int32_t)(-1 - (Q.win_base + (ts - (Q.pos0 - L.W))));
-                else l_win = (int32_t)(-1 - (ts % L.W));
-            }
-            lc[u] = p[u] < n_ent ? l_ent : l_win;
-        }
-#pragma unroll
-        for (int u = 0; u < RES; ++u) {
-            const int e = e0 + 64 * u + lane;
-            const uint64_t vb = __builtin_amdgcn_ballot_w64(lc[u] != kMasked);
-            if (first_ok < 0 && vb != 0)
-                first_ok = __builtin_amdgcn_readlane(lc[u], (int)__builtin_ctzll(vb));
-            if (e < mine * kChunk) locs[e] = lc[u] != kMasked ? lc[u] : own;
-            const int t0 = (e0 + 64 * u) >> 5;
-            if (lane == 0) {
-                if (t0 < mine) vmask[t0] = (uint32_t)vb;
-                if (t0 + 1 < mine) vmask[t0 + 1] = (uint32_t)(vb >> 32);
-            }
-        }
-    }
-    if (own == kMasked) {                                // no window (W = 0)
-        if (first_ok < 0) mine = 0;                      // nothing valid: the subset contributes nothing
-        wave_lds_fence();
-        for (int e = lane; e < mine * kChunk; e += 64)
-            if (locs[e] == kMasked) locs[e] = first_ok;
-    }
-    if (lane < DR / 2) {
-        float c, sn;
-        rope_cs(L, Q.t, lane, c, sn);
-        rtab[lane] = make_float2(c, sn);
-    }
-    wave_lds_fence();
+    };
 
     // ---- chunk loads (same line-wise pattern as k_attend, all NLD loads of a
     // chunk on this wave)
@@ -808,9 +778,70 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
         }
     };
     u32x4 R0[NLD], R1[PFD == 2 ? NLD : 1];
+    resolve(0, mine);
+    if (own == kMasked) {                                // no window (W = 0)
+        if (first_ok < 0) mine = 0;                      // nothing valid: the subset contributes nothing
+        wave_lds_fence();
+        for (int e = lane; e < mine * kChunk; e += 64)
+            if (locs[e] == kMasked) locs[e] = first_ok;
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int pc = tid + 64 * kSubsets * i;
+        const int hr = pc / (qrow_bytes / 16), off = (pc % (qrow_bytes / 16)) * 16;
+        if (pc < npc) *(u32x4 *)(qlds + hr * LoShape<D, DR>::QROW + off) = qpc[i];
+    }
+    __syncthreads();                                     // query rows and this wave's locators visible
     if (mine > 0) issue(R0, 0);
     if constexpr (PFD == 2)
         if (mine > 1) issue(R1, 1);
+    // query fragments of head c16 from LDS: code pair kp holds piece 4kp+g
+    // (bf16 queries are the MFMA operand bits as they are)
+    const uint8_t *qh = qlds + c16 * LoShape<D, DR>::QROW;
+    auto q8 = [&](int dd, float (&v)[8]) {               // 8 query values from dim dd
+        if (L.act == DSV4_DT_BF16) {
+            const u32x4 u = *(const u32x4 *)(qh + dd * 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = __uint_as_float(u[j] << 16);
+                v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+            }
+        } else {
+            const u32x4 a = *(const u32x4 *)(qh + dd * 4), b = *(const u32x4 *)(qh + dd * 4 + 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[j] = __uint_as_float(a[j]);
+                v[4 + j] = __uint_as_float(b[j]);
+            }
+        }
+    };
+    bf16x8 Qn[KP][2];
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ch = 4 * kp + g;
+            bf16x8 f;
+            if (L.act == DSV4_DT_BF16) {
+                u32x4 u = {0, 0, 0, 0};
+                if (NCH % 4 == 0 || ch < NCH) u = *(const u32x4 *)(qh + (16 * ch + 8 * h) * 2);
+                union { u32x4 v; bf16x8 b; } cv;
+                cv.v = u;
+                f = cv.b;
+            } else {
+                float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (NCH % 4 == 0 || ch < NCH) q8(16 * ch + 8 * h, v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) f[j] = f2bf(v[j]);
+            }
+            Qn[kp][h] = f;
+        }
+    if (lane < DR / 2) {
+        float c, sn;
+        rope_cs(L, Q.t, lane, c, sn);
+        rtab[lane] = make_float2(c, sn);
+    }
+    wave_lds_fence();
 
     // ---- RoPE query fragments, rotated at t (the code fragments are above):
     // code pair kp holds piece 4kp+g, RoPE step ks RoPE piece 4ks+g
@@ -818,16 +849,8 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
 #pragma unroll
     for (int ks = 0; ks < KR; ++ks) {
         const int ch = 4 * ks + g;
-        float qr[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (L.act == DSV4_DT_BF16) {
-                const uint32_t w = qrr[ks][0][j >> 1];
-                qr[j] = __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
-            } else {
-                qr[j] = __uint_as_float(qrr[ks][j >> 2][j & 3]);
-            }
-        }
+        float qr[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (RCH % 4 == 0 || ch < RCH) q8(DN + 8 * ch, qr);
         bf16x8 f;
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
@@ -1039,7 +1062,7 @@ int64_t attend_lds_bytes(int64_t list_max) {
 template <int D, int DR>
 int64_t attend_lo_lds_bytes(int64_t list_max) {
     const int64_t nch = (list_max + kChunk - 1) / kChunk, cpw = (nch + kSubsets - 1) / kSubsets;
-    const int64_t stream = kSubsets * (int64_t)LoShape<D, DR>::wave_bytes((int)cpw);
+    const int64_t stream = kSubsets * (int64_t)LoShape<D, DR>::wave_bytes((int)cpw) + LoShape<D, DR>::QBYTES;
     return stream > LoShape<D, DR>::FOLD ? stream : LoShape<D, DR>::FOLD;
 }
 
