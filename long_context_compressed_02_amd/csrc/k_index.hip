@@ -112,12 +112,19 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     const int32_t *btr = C.block_table + (int64_t)r * C.max_blocks;
     const int lane_off = c16 * L.key_bytes;
     const uint8_t *pool = (const uint8_t *)C.index_keys;
-    // B operands: 16-key sub-blocks, each inside one 128-token cache block, so
-    // its block lookup is a wave-uniform scalar load; lane = key (c16).  An
-    // unmapped block reads block 0 and is masked by its zero scale.
+    // the block ids of this wave's key range, one per lane, read once up front
+    // (a per-sub-block lookup would make every group of key loads wait for
+    // the previous one: loads complete in order)
+    const int blk0 = (k0 * L.m) / kBlockTokens;
+    const int btv = blk0 + lane < C.max_blocks ? btr[blk0 + lane] : -1;
+    // B operands: 16-key sub-blocks, each inside one 128-token cache block
+    // (lane = key c16).  An unmapped block reads block 0 and is masked by its
+    // zero scale.
     auto load_sb = [&](int kb, i32x8 &Bk, float &sk) {
         const int kc = kb < N ? kb : k0;                       // stay in mapped memory past the end
-        const int bid = __builtin_amdgcn_readfirstlane(btr[(kc * L.m) / kBlockTokens]);
+        const int bi = (kc * L.m) / kBlockTokens - blk0;       // wave-uniform
+        const int bid = bi < 64 ? __builtin_amdgcn_readlane(btv, bi)   // (ranges of 64+ blocks: strides >= 32)
+                                : __builtin_amdgcn_readfirstlane(btr[(kc * L.m) / kBlockTokens]);
         const bool okb = bid >= 0 && bid < C.n_blocks && kb < N;
         const uint8_t *base = pool + (int64_t)(okb ? bid : 0) * L.index_block_bytes;
         const int slot0 = kc % L.epb;
