@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=8, help="queries timed on the CPU oracle (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (traffic calibration under --pmc)")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"],
+                    help="decode: the CSA+HCA decode step (the headline); prefill: one 8192-token CSA chunk on "
+                         "a 256K-token prefix")
     return ap.parse_args()
 
 
@@ -50,6 +53,8 @@ def main():
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": a.gpus}))
         sys.exit(2)
+    if a.workload == "prefill":
+        return prefill_main(a)
     import torch
     from long_context_compressed_02_amd import binding as B
     from long_context_compressed_02_amd import synth
@@ -205,6 +210,113 @@ def main():
         "launches_per_step": {n_: v["launches"] / steps for n_, v in kern.items()},
         "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "attend_TFLOPs": round(attend_flops_step / (kern["attend"]["total_ms"] / steps * 1e-3) / 1e12, 1),
+        "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def prefill_main(a):
+    """One prefill chunk of a CSA layer: 8192 new tokens appended to a
+    262144-token prefix (65536 entries and index keys), top-512.  A step =
+    compress + indexer + top-k + sparse attend over the chunk.  Inputs are
+    synthetic N(0,1) values generated on the device before timing."""
+    import torch
+    from long_context_compressed_02_amd import binding as B
+    from long_context_compressed_02_amd import synth
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    w = synth.CSA_PREFILL_8K
+    cfg = B.make_cfg(**w.shape())
+    H, d, HI_, dI, k = w.n_heads, w.d, w.idx_heads, w.idx_dim, w.topk
+    P, C = w.ctx[0], w.chunk
+    T = P + C
+    steps, warm = a.steps, a.warmup
+    nb = (T + 127) // 128 + 1
+    perm = torch.from_numpy(synth.permutation(w.wid, nb)).to(dev).to(torch.int32)
+    bt = perm.view(1, nb).contiguous()
+    csa = B.LayerCache(cfg, B.DSV4_CSA, 1, nb, nb, bt)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    rn = lambda *s_: torch.randn(*s_, generator=g, device=dev, dtype=torch.float32)
+    zero = torch.zeros(1, dtype=torch.int32, device=dev)
+    t_setup = time.time()
+    n_csa = P // 4
+    for a0 in range(0, n_csa, 1 << 15):
+        nn = min(1 << 15, n_csa - a0)
+        idx = torch.arange(a0, a0 + nn, dtype=torch.int32, device=dev)
+        rr = torch.zeros(nn, dtype=torch.int32, device=dev)
+        B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_ENTRY, rr, idx, rn(nn, d))
+        B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_INDEX_KEY, rr, idx, rn(nn, dI))
+    bf = lambda *s_: rn(*s_).to(torch.bfloat16)
+    B.dsv4_state_write_tokens(cfg, csa, 0, P - 128, bf(128, d), bf(128, d), bf(128, dI), bf(128, dI))
+    x = dict(kv=bf(C, d), gate=bf(C, d), kI=bf(C, dI), gI=bf(C, dI), q=bf(C, H, d), qI=bf(C, HI_, dI),
+             w=rn(C, HI_) / 8.0)
+    sinks = torch.from_numpy(synth.sinks(w)).to(dev)
+    cu = torch.tensor([0, C], dtype=torch.int32, device=dev)
+    p0 = torch.tensor([P], dtype=torch.int32, device=dev)
+    lay = csa.layout
+    winc = torch.empty((C + 128) * lay.record_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.dsv4_workspace_bytes(cfg, C, nb * 32), dtype=torch.uint8, device=dev)
+    topk = torch.empty((C, k), dtype=torch.int32, device=dev)
+    out_c = torch.empty((C, H, d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.dsv4_compress_kv_prefill(cfg, csa, x["kv"], x["gate"], x["kI"], x["gI"], cu, zero, p0, C, winc, stream)
+        B.dsv4_index_topk_prefill(cfg, csa, x["qI"], x["w"], cu, zero, p0, C, topk, ws, stream)
+        B.dsv4_csa_attend_prefill(cfg, csa, x["q"], cu, zero, p0, C, topk, winc, sinks, out_c, stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    for kid in range(B.DSV4_K_COUNT):
+        B.dsv4_timer_enable(kid, True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    names = {B.DSV4_K_COMPRESS: "compress", B.DSV4_K_INDEX_SCORE: "index_score", B.DSV4_K_TOPK: "topk",
+             B.DSV4_K_ATTEND: "attend"}
+    for kid, nm in names.items():
+        ms, n = B.dsv4_timer_read(kid, True)
+        B.dsv4_timer_enable(kid, False)
+        kern[nm] = dict(total_ms=ms, launches=n, avg_us=1e3 * ms / max(n, 1))
+    # algorithmic work of the chunk: indexer flops over the visible keys of every
+    # query, attention flops over its records (top-512 + window)
+    n_vis = sum((P + i + 1) // 4 for i in range(C))
+    idx_flops = n_vis * HI_ * dI * 2
+    csa_recs = C * (min(k, n_csa) + 128)
+    att_flops = csa_recs * H * 4 * d
+    idx_ms = kern["index_score"]["total_ms"] / steps
+    att_ms = kern["attend"]["total_ms"] / steps
+    idx_tf = idx_flops / (idx_ms * 1e-3) / 1e12 if idx_ms > 0 else 0.0
+    att_tf = att_flops / (att_ms * 1e-3) / 1e12 if att_ms > 0 else 0.0
+    dom = "index_score" if kern["index_score"]["total_ms"] >= kern["attend"]["total_ms"] else "attend"
+    roof = ({"kernel": "k_index_score_decode", "bound": "mfma", "achieved": round(idx_tf, 2),
+             "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tf / FP8_PEAK_TFLOPS, 4), "traffic": None}
+            if dom == "index_score" else
+            {"kernel": "k_attend", "bound": "mfma", "achieved": round(att_tf, 2), "peak": BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4), "traffic": None})
+    res = {
+        "metric": "CSA prefill tokens/s (8192-token chunk on a 262144-token prefix)",
+        "value": round(C / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8/bf16", "data": "synthetic",
+        "config": {"workload": f"V4 CSA layer prefill, chunk {C} on a {P // 1024}K prefix, top-{k}, "
+                               f"{H} heads x d {d}", "chunk": C, "prefix": P, "topk": k},
+        "roofline": roof,
+        "breakdown_ms": {n_: round(v["total_ms"] / steps, 3) for n_, v in kern.items()},
+        "indexer_TFLOPs": round(idx_tf, 1), "attend_TFLOPs": round(att_tf, 1),
         "setup_s": round(t_setup, 1),
     }
     print(json.dumps(res), flush=True)

@@ -235,7 +235,7 @@ dsv4_status dsv4_compress_kv_prefill(const dsv4_cfg *cfg, const dsv4_cache *cach
 
 static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, const void *qI, const float *w,
                                      const int32_t *req_q, const int32_t *pos_q, int nq, int32_t *topk_dev,
-                                     uint8_t *ws, int64_t ws_bytes, hipStream_t s) {
+                                     uint8_t *ws, int64_t ws_bytes, hipStream_t s, bool prefill) {
     const int64_t nmax = (int64_t)cache->max_blocks * L.epb;
     IndexWs W;
     const int64_t need = index_ws_bytes(L, nq, nmax, &W, ws);
@@ -246,7 +246,8 @@ static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, cons
     if (e != hipSuccess) return DSV4_ERR_LAUNCH;
     {
         Timed tm(DSV4_K_INDEX_SCORE, s);
-        e = launch_score_decode(L, *cache, req_q, pos_q, nq, W, s);
+        e = prefill ? launch_score_prefill(L, *cache, req_q, pos_q, nq, W, s)
+                    : launch_score_decode(L, *cache, req_q, pos_q, nq, W, s);
     }
     if (e != hipSuccess) return DSV4_ERR_LAUNCH;
     Timed tm(DSV4_K_TOPK, s);
@@ -267,7 +268,7 @@ dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
     if (!qI || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
     if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
     return index_topk_common(L, cache, qI, w_dev, req_dev, pos_dev, B, topk_dev, (uint8_t *)ws_dev, ws_bytes,
-                             S(stream));
+                             S(stream), false);
 }
 
 dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *qI,
@@ -301,7 +302,7 @@ dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
         const int n = total_tokens - q0 < group ? total_tokens - q0 : group;
         st = index_topk_common(L, cache, (const uint8_t *)qI + q0 * qrow, w_dev ? w_dev + (int64_t)q0 * L.HI : nullptr,
                                req_q + q0, pos_q + q0, n, topk_dev + (int64_t)q0 * L.topk, ws + rows_bytes,
-                               ws_bytes - rows_bytes, s);
+                               ws_bytes - rows_bytes, s, true);
         if (st != DSV4_OK) return st;
     }
     return DSV4_OK;

@@ -51,6 +51,16 @@ __global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, co
     if (lane == 0) wq[row] = (w ? w[row] : 1.0f) * scale;
 }
 
+// p(l) + p(l^16) + p(l^32) + p(l^48) as (p(l) + p(l^16)) + (p(l^32) + p(l^48)):
+// the sum of a key's partial scores over the four lane groups, on the gfx950
+// row-swap permutes (VALU, no LDS).
+__device__ __forceinline__ float group_sum4(float v) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // Order-preserving key of a score: larger score -> larger key; -0 == +0; NaN
 // below everything.
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -66,6 +76,7 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // four sub-blocks in flight while the current group is on the MFMA.
 constexpr int kKeysPerWave = 256;
 constexpr int kKeysPerWG = 4 * kKeysPerWave;
+static_assert(kKeysPerWave % 64 == 0, "scoring ranges are whole pipeline groups");
 
 // HB: 16-row blocks of index heads (idx_heads <= 16*HB); FULL: idx_dim == 128
 // (no padded operand bytes).  Both are compile-time so that the loads and the
@@ -83,7 +94,6 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     if (r < 0 || r >= C.n_req || t < 0 || (int64_t)t >= (int64_t)C.max_blocks * kBlockTokens) return;
     const int N = (t + 1) / L.m;
     const int k0 = (blockIdx.x * 4 + wave) * kKeysPerWave;
-    if (k0 >= N) return;
     const int dI = L.dI;
     // k-order of the 16x16x128 operands: lane group g holds bytes [16g, 16g+16)
     // and [64+16g, 64+16g+16) of a row, so each 16-byte load instruction of a
@@ -93,7 +103,6 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     const i32x4 z4 = {0, 0, 0, 0};
     // A operand: query codes (zero-padded to 128 bytes per row), rows = index heads
     i32x8 A[HB];
-    float wl[HB][4];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         const int row = hb * 16 + c16;
@@ -103,12 +112,16 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
         a.lo = *(const i32x4 *)(p + o0);
         a.hi = *(const i32x4 *)(p + o1);
         A[hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = hb * 16 + 4 * g + i;
-            wl[hb][i] = h < L.HI ? wq[(int64_t)q * L.HI + h] : 0.0f;
-        }
     }
+    // head weights in LDS (registers are kept for the operands: at 96 VGPRs or
+    // fewer five waves share a SIMD, and a whole decode batch is resident at once)
+    __shared__ f32x4 wls[HB * 4];                  // [hb][g]: heads hb*16 + 4g + i
+    if (threadIdx.x < HB * 16) {
+        const int h = threadIdx.x;
+        ((float *)wls)[h] = h < L.HI ? wq[(int64_t)q * L.HI + h] : 0.0f;
+    }
+    __syncthreads();
+    if (k0 >= N) return;                           // (after the barrier: every wave takes part in it)
     const int32_t *btr = C.block_table + (int64_t)r * C.max_blocks;
     const int lane_off = c16 * L.key_bytes;
     const uint8_t *pool = (const uint8_t *)C.index_keys;
@@ -152,11 +165,12 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
                                                                        0, 0, 0, 127, 0, 127);
         float part = 0.0f;
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+        for (int hb = 0; hb < HB; ++hb) {
+            const f32x4 w4 = wls[hb * 4 + g];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part = part + fmaxf(acc[hb][i], 0.0f) * wl[hb][i];
-        part = part + __shfl_xor(part, 16);
-        part = part + __shfl_xor(part, 32);
+            for (int i = 0; i < 4; ++i) part = part + fmaxf(acc[hb][i], 0.0f) * w4[i];
+        }
+        part = group_sum4(part);
         if (g == 0 && kb + c16 < N) {
             const float v = sk * part;
             srow[kb + c16] = v;
@@ -197,6 +211,222 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     }
     // every wave with keys records its extremes (kmx == 0: no finite score)
     if (lane == 0) wr[(int64_t)q * nwr + k0 / kKeysPerWave] = make_uint2(kmn, kmx);
+}
+
+// ---------------------------------------------------------------- prefill scoring
+// The queries of a prefill chunk read the same keys.  A workgroup scores
+// kPfRows consecutive query rows (kPfWaveRows per wave) against kPfKeys keys,
+// staged kPfChunk keys at a time through two LDS tiles: the next tile's loads
+// are in flight while the current one is scored, and every staged key serves
+// all rows of the workgroup.  A (row, 16-key sub-block) score takes exactly
+// the decode scorer's operations, so a prefilled query scores bitwise like a
+// decode step.  Rows of several requests in one workgroup are taken one
+// request at a time.
+constexpr int kPfWaveRows = 2;
+constexpr int kPfRows = 4 * kPfWaveRows;
+constexpr int kPfKeys = 2048;
+constexpr int kPfChunk = kKeysPerWave;                 // keys per tile (one extremes record per row)
+constexpr int kPfRowBytes = 128 + 16;                  // LDS bytes per key: codes + one piece (bank shift)
+static_assert(kPfKeys % kPfChunk == 0, "whole tiles per workgroup");
+
+// LDS the prefill scorer needs beyond its static arrays: the block ids of its key range.
+int64_t score_prefill_dyn_lds(const Lay &L) { return ((int64_t)kPfKeys * L.m / kBlockTokens + 2) * 4; }
+
+template <int HB, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_index_score_prefill(Lay L, dsv4_cache C, const uint8_t *q8,
+                                                             const float *wq, const int32_t *req,
+                                                             const int32_t *pos, int n, float *scores,
+                                                             int64_t ld, uint2 *wr, int nwr) {
+    constexpr int QW = kPfWaveRows;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPfChunk * kPfRowBytes];
+    __shared__ float tsc[2][kPfChunk];
+    __shared__ f32x4 wls[kPfRows][HB * 4];             // [row][hb][g]: heads hb*16 + 4g + i
+    extern __shared__ int32_t btl[];                     // block ids of the key range
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // wave-uniform (scalar)
+    const int row0 = blockIdx.y * kPfRows;
+    const int kbeg = blockIdx.x * kPfKeys;
+    const int dI = L.dI;
+    for (int i = tid; i < kPfRows * HB * 16; i += 256) {
+        const int rr = i / (HB * 16), h = i % (HB * 16), qi = row0 + rr;
+        ((float *)wls[rr])[h] = (qi < n && h < L.HI) ? wq[(int64_t)qi * L.HI + h] : 0.0f;
+    }
+    if (!FULL) {                                         // code bytes past dI stay zero
+        for (int i = tid; i < 2 * kPfChunk * kPfRowBytes / 16; i += 256) ((i32x4 *)tile)[i] = (i32x4){0, 0, 0, 0};
+    }
+    // the rows' requests and visible key counts (0: nothing to score)
+    int rq[kPfRows], Nq[kPfRows];
+#pragma unroll
+    for (int i = 0; i < kPfRows; ++i) {
+        const int qi = row0 + i;
+        rq[i] = -1;
+        Nq[i] = 0;
+        if (qi < n) {
+            const int r = req[qi], t = pos[qi];
+            if (r >= 0 && r < C.n_req && t >= 0 && (int64_t)t < (int64_t)C.max_blocks * kBlockTokens) {
+                rq[i] = r;
+                Nq[i] = (t + 1) / L.m;
+            }
+        }
+    }
+    const int blk0 = (kbeg * L.m) / kBlockTokens;
+    const int nbl = (kPfKeys * L.m) / kBlockTokens + 2;
+    const uint8_t *pool = (const uint8_t *)C.index_keys;
+    constexpr int PKMAX = 8;                             // 16-byte pieces of a 128-byte key
+    const int PK = dI / 16;
+    int done = 0;
+#pragma unroll
+    for (int i = 0; i < kPfRows; ++i)
+        if (Nq[i] <= kbeg) done |= 1 << i;
+#pragma unroll 1
+    while (done != (1 << kPfRows) - 1) {                 // one request per pass (workgroup-uniform)
+        int R = -1;
+#pragma unroll
+        for (int i = kPfRows - 1; i >= 0; --i)
+            if (!((done >> i) & 1)) R = rq[i];
+        int act = 0, Nmax = 0;
+#pragma unroll
+        for (int i = 0; i < kPfRows; ++i)
+            if (!((done >> i) & 1) && rq[i] == R) {
+                act |= 1 << i;
+                Nmax = Nq[i] > Nmax ? Nq[i] : Nmax;
+            }
+        done |= act;
+        const int kend = kbeg + kPfKeys < Nmax ? kbeg + kPfKeys : Nmax;
+        const int nch = (kend - kbeg + kPfChunk - 1) / kPfChunk;
+        __syncthreads();                                 // the previous pass is done with the tiles and btl
+        const int32_t *btr = C.block_table + (int64_t)R * C.max_blocks;
+        for (int i = tid; i < nbl; i += 256) btl[i] = blk0 + i < C.max_blocks ? btr[blk0 + i] : -1;
+        __syncthreads();
+        // A operands of this wave's rows
+        const int wr0 = wave * QW;                       // first row (within the workgroup) of this wave
+        i32x8 A[QW][HB];
+#pragma unroll
+        for (int i = 0; i < QW; ++i)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                const int hrow = hb * 16 + c16;
+                const bool ok = ((act >> (wr0 + i)) & 1) && hrow < L.HI;
+                const uint8_t *p = q8 + ((int64_t)(ok ? row0 + wr0 + i : 0) * L.HI + (ok ? hrow : 0)) * 128;
+                i32x8 a;
+                a.lo = *(const i32x4 *)(p + 16 * g);
+                a.hi = *(const i32x4 *)(p + 64 + 16 * g);
+                A[i][hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        // one tile's loads: thread piece tid + 256u is piece (u mod PK) of key (tid + 256u) / PK;
+        // thread tid also fetches key tid's scale.  Keys past the end, or in
+        // unmapped blocks, read block 0 and get scale 0.
+        i32x4 stg[PKMAX];
+        float stg_s;
+        auto load_tile = [&](int kc0) {
+#pragma unroll
+            for (int u = 0; u < PKMAX; ++u) {
+                if (u >= PK) break;
+                const int pc = tid + 256 * u, kk = pc / PK, off = (pc % PK) * 16, k = kc0 + kk;
+                const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
+                const bool ok = bid >= 0 && bid < C.n_blocks;
+                const uint8_t *src = pool + (ok ? (int64_t)bid * L.index_block_bytes + (k % L.epb) * L.key_bytes + off : 0);
+                stg[u] = *(const i32x4 *)src;
+            }
+            const int k = kc0 + tid;
+            const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
+            const bool ok = bid >= 0 && bid < C.n_blocks;
+            const float sv = *(const float *)(pool + (ok ? (int64_t)bid * L.index_block_bytes + L.key_scale_off +
+                                                               (k % L.epb) * 4 : 0));
+            stg_s = ok ? sv : 0.0f;
+        };
+        auto store_tile = [&](int b) {
+#pragma unroll
+            for (int u = 0; u < PKMAX; ++u) {
+                if (u >= PK) break;
+                const int pc = tid + 256 * u, kk = pc / PK, off = (pc % PK) * 16;
+                *(i32x4 *)(tile[b] + kk * kPfRowBytes + off) = stg[u];
+            }
+            tsc[b][tid] = stg_s;
+        };
+        uint32_t kmn[QW], kmx[QW];
+        // rows two at a time with no branch between them (their MFMAs, weightings
+        // and cross-lane sums overlap); rows inactive or past their visible keys
+        // store nothing
+        auto score_sb = [&](int b, int sb, int kb) {
+            i32x8 Bk;
+            const uint8_t *kr = tile[b] + (sb * 16 + c16) * kPfRowBytes;
+            Bk.lo = *(const i32x4 *)(kr + 16 * g);
+            Bk.hi = *(const i32x4 *)(kr + 64 + 16 * g);
+            const float sk = tsc[b][sb * 16 + c16];
+#pragma unroll
+            for (int i0 = 0; i0 < QW; i0 += 2) {
+                f32x4 acc[2][HB];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb)
+                        acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            A[i0 + ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+                float part[2];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    part[ii] = 0.0f;
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) {
+                        const f32x4 w4 = wls[wr0 + i0 + ii][hb * 4 + g];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) part[ii] = part[ii] + fmaxf(acc[ii][hb][j], 0.0f) * w4[j];
+                    }
+                }
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) part[ii] = group_sum4(part[ii]);
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = i0 + ii, rw = wr0 + i;
+                    if (g == 0 && ((act >> rw) & 1) && kb + c16 < Nq[rw]) {
+                        const float v = sk * part[ii];
+                        scores[(int64_t)(row0 + rw) * ld + kb + c16] = v;
+                        if (fabsf(v) < INFINITY) {
+                            const uint32_t u = score_key(v);
+                            kmn[i] = min(kmn[i], u);
+                            kmx[i] = max(kmx[i], u);
+                        }
+                    }
+                }
+            }
+        };
+        load_tile(kbeg);
+        store_tile(0);
+        __syncthreads();
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            const int kc0 = kbeg + c * kPfChunk, b = c & 1;
+            if (c + 1 < nch) load_tile(kc0 + kPfChunk);  // in flight while this tile is scored
+#pragma unroll
+            for (int i = 0; i < QW; ++i) {
+                kmn[i] = 0xffffffffu;
+                kmx[i] = 0u;
+            }
+#pragma unroll 1
+            for (int sb = 0; sb < kPfChunk / 16; ++sb) {
+                const int kb = kc0 + sb * 16;
+                if (kb >= kend) break;                   // workgroup-uniform
+                score_sb(b, sb, kb);
+            }
+            // this tile's extremes per row (the record the decode scorer's wave
+            // for these keys writes)
+#pragma unroll
+            for (int i = 0; i < QW; ++i) {
+                const int rw = wr0 + i;
+                if (!((act >> rw) & 1) || kc0 >= Nq[rw]) continue;   // wave-uniform
+                uint32_t mn = kmn[i], mx = kmx[i];
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) {
+                    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+                    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+                }
+                if (lane == 0) wr[(int64_t)(row0 + rw) * nwr + kc0 / kKeysPerWave] = make_uint2(mn, mx);
+            }
+            if (c + 1 < nch) store_tile(b ^ 1);
+            __syncthreads();                             // next tile visible; this one free
+        }
+    }
 }
 
 // ---------------------------------------------------------------- top-k
@@ -976,6 +1206,30 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
 #define DSV4_SCORE(HBV, FV) \
     hipLaunchKernelGGL((k_index_score_decode<HBV, FV>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, ws.ld, \
                        ws.wr, ws.nwr)
+    if (full) {
+        if (hb == 4) DSV4_SCORE(4, true);
+        else if (hb == 3) DSV4_SCORE(3, true);
+        else if (hb == 2) DSV4_SCORE(2, true);
+        else DSV4_SCORE(1, true);
+    } else {
+        if (hb == 4) DSV4_SCORE(4, false);
+        else if (hb == 3) DSV4_SCORE(3, false);
+        else if (hb == 2) DSV4_SCORE(2, false);
+        else DSV4_SCORE(1, false);
+    }
+#undef DSV4_SCORE
+    return hipGetLastError();
+}
+
+hipError_t launch_score_prefill(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
+                                int n, const IndexWs &ws, hipStream_t s) {
+    dim3 g((unsigned)((ws.ld + kPfKeys - 1) / kPfKeys), (unsigned)((n + kPfRows - 1) / kPfRows));
+    const int hb = (L.HI + 15) / 16;
+    const bool full = L.dI == 128;
+    const size_t dyn = (size_t)score_prefill_dyn_lds(L);
+#define DSV4_SCORE(HBV, FV) \
+    hipLaunchKernelGGL((k_index_score_prefill<HBV, FV>), g, dim3(256), dyn, s, L, C, ws.q8, ws.wq, req, pos, n, \
+                       ws.scores, ws.ld, ws.wr, ws.nwr)
     if (full) {
         if (hb == 4) DSV4_SCORE(4, true);
         else if (hb == 3) DSV4_SCORE(3, true);

@@ -58,6 +58,10 @@ hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows
                           hipStream_t s);
 hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
                                int n, const IndexWs &ws, hipStream_t s);
+// The same scores for the packed rows of a prefill chunk (rows of one request
+// in index order share their key loads).
+hipError_t launch_score_prefill(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
+                                int n, const IndexWs &ws, hipStream_t s);
 hipError_t launch_topk(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos, int n,
                        const IndexWs &ws, int32_t *out, hipStream_t s);
 hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *nvis, int n, int64_t max_n, int k,
