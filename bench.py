@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=8, help="queries timed on the CPU oracle (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (traffic calibration under --pmc)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"],
-                    help="decode: the CSA+HCA decode step (the headline); prefill: one 8192-token CSA chunk on "
-                         "a 256K-token prefix")
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "hca_decode", "pair_1m"],
+                    help="decode: the CSA+HCA decode step, batch 32 at 128K (the headline); prefill: one "
+                         "8192-token CSA chunk on a 256K-token prefix; hca_decode: the HCA decode step, batch 16 at "
+                         "64K; pair_1m: the CSA+HCA decode step for 4 requests at 1M/512K/64K/4K")
     return ap.parse_args()
 
 
@@ -55,6 +56,8 @@ def main():
         sys.exit(2)
     if a.workload == "prefill":
         return prefill_main(a)
+    if a.workload in ("hca_decode", "pair_1m"):
+        return decode_mix_main(a)
     import torch
     from long_context_compressed_02_amd import binding as B
     from long_context_compressed_02_amd import synth
@@ -317,6 +320,153 @@ def prefill_main(a):
         "roofline": roof,
         "breakdown_ms": {n_: round(v["total_ms"] / steps, 3) for n_, v in kern.items()},
         "indexer_TFLOPs": round(idx_tf, 1), "attend_TFLOPs": round(att_tf, 1),
+        "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _timed_steps(step, steps, warm):
+    """Warm up, time `steps` steps with events on the current stream, then run
+    them again with the library's per-kernel timers on."""
+    import torch
+    from long_context_compressed_02_amd import binding as B
+    for s in range(warm):
+        step(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(warm, warm + steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    for kid in range(B.DSV4_K_COUNT):
+        B.dsv4_timer_enable(kid, True)
+    for s in range(warm, warm + steps):
+        step(s)
+    torch.cuda.synchronize()
+    names = {B.DSV4_K_COMPRESS: "compress", B.DSV4_K_INDEX_SCORE: "index_score", B.DSV4_K_TOPK: "topk",
+             B.DSV4_K_ATTEND: "attend"}
+    kern = {}
+    for kid, nm in names.items():
+        ms, n = B.dsv4_timer_read(kid, True)
+        B.dsv4_timer_enable(kid, False)
+        kern[nm] = dict(total_ms=ms, launches=n, avg_us=1e3 * ms / max(n, 1))
+    return ms_step, kern
+
+
+def decode_mix_main(a):
+    """Decode steps of the other two decode workloads.  hca_decode: an HCA layer,
+    16 requests at 65536 tokens (512 entries each); a step = append/compress +
+    dense attention.  pair_1m: a CSA+HCA layer pair for 4 requests at
+    1048576 / 524288 / 65536 / 4096 tokens; a step = the whole decode path of
+    both layers.  Entries, keys and window tokens are N(0,1) values generated on
+    the device; every step appends the next token of every request."""
+    import torch
+    from long_context_compressed_02_amd import binding as B
+    from long_context_compressed_02_amd import synth
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    pair = a.workload == "pair_1m"
+    w = synth.PAIR_DECODE_1M if pair else synth.HCA_DECODE_64K
+    ctxs = list(w.ctx)
+    Bsz = len(ctxs)
+    steps, warm = a.steps, a.warmup
+    total_new = steps + warm
+    cfg = B.make_cfg(**w.shape())
+    policy = {"auto": B.DSV4_POLICY_AUTO, "hi": B.DSV4_POLICY_HI, "lo": B.DSV4_POLICY_LO}[a.policy]
+    H, d, HI_, dI, k = w.n_heads, w.d, w.idx_heads, w.idx_dim, w.topk
+    need = [(c + total_new + 127) // 128 for c in ctxs]
+    mb = max(need)
+    perm = synth.permutation(w.wid, sum(need))
+    bt_h = np.full((Bsz, mb), -1, dtype=np.int32)
+    o = 0
+    for r, nb in enumerate(need):
+        bt_h[r, :nb] = perm[o:o + nb]
+        o += nb
+    bt = torch.from_numpy(bt_h).to(dev)
+    csa = B.LayerCache(cfg, B.DSV4_CSA, Bsz, mb, sum(need), bt) if pair else None
+    hca = B.LayerCache(cfg, B.DSV4_HCA, Bsz, mb, sum(need), bt)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5678)
+    rn = lambda *s_: torch.randn(*s_, generator=g, device=dev, dtype=torch.float32)
+    bf = lambda *s_: rn(*s_).to(torch.bfloat16)
+    t_setup = time.time()
+
+    def fill(cache, target, r, n, dim):
+        for a0 in range(0, n, 1 << 15):
+            nn = min(1 << 15, n - a0)
+            B.dsv4_cache_write_entries(cfg, cache, target, torch.full((nn,), r, dtype=torch.int32, device=dev),
+                                       torch.arange(a0, a0 + nn, dtype=torch.int32, device=dev), rn(nn, dim))
+    for r, c in enumerate(ctxs):
+        if pair:
+            fill(csa, B.DSV4_TARGET_ENTRY, r, c // 4, d)
+            fill(csa, B.DSV4_TARGET_INDEX_KEY, r, c // 4, dI)
+            B.dsv4_state_write_tokens(cfg, csa, r, c - 128, bf(128, d), bf(128, d), bf(128, dI), bf(128, dI))
+        fill(hca, B.DSV4_TARGET_ENTRY, r, c // 128, d)
+        B.dsv4_state_write_tokens(cfg, hca, r, c - 128, bf(128, d), bf(128, d))
+    steps_in = []
+    for s in range(total_new):
+        steps_in.append(dict(
+            kv=bf(Bsz, d), gate=bf(Bsz, d), kI=bf(Bsz, dI), gI=bf(Bsz, dI), kvh=bf(Bsz, d), gateh=bf(Bsz, d),
+            q=bf(Bsz, H, d), qh=bf(Bsz, H, d), qI=bf(Bsz, HI_, dI), w=rn(Bsz, HI_) / 8.0,
+            pos=torch.tensor([c + s for c in ctxs], dtype=torch.int32, device=dev)))
+    req = torch.arange(Bsz, dtype=torch.int32, device=dev)
+    sinks = torch.from_numpy(synth.sinks(w)).to(dev)
+    ws = torch.empty(B.dsv4_workspace_bytes(cfg, Bsz, mb * 32), dtype=torch.uint8, device=dev) if pair else None
+    topk = torch.empty((Bsz, k), dtype=torch.int32, device=dev)
+    out_c = torch.empty((Bsz, H, d), dtype=torch.bfloat16, device=dev)
+    out_h = torch.empty((Bsz, H, d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        x = steps_in[s]
+        if pair:
+            B.dsv4_compress_kv_decode(cfg, csa, x["kv"], x["gate"], x["kI"], x["gI"], req, x["pos"], stream)
+            B.dsv4_index_topk_decode(cfg, csa, x["qI"], x["w"], req, x["pos"], topk, ws, stream)
+            B.dsv4_csa_attend_decode(cfg, csa, x["q"], req, x["pos"], topk, sinks, out_c, policy, stream)
+        B.dsv4_compress_kv_decode(cfg, hca, x["kvh"], x["gateh"], None, None, req, x["pos"], stream)
+        B.dsv4_hca_attend_decode(cfg, hca, x["qh"], req, x["pos"], sinks, out_h, policy, stream)
+
+    ms_step, kern = _timed_steps(step, steps, warm)
+    # algorithmic work per step at the timed positions (averaged over the steps)
+    ts = [[c + s for c in ctxs] for s in range(warm, total_new)]
+    n_vis = np.mean([sum((t + 1) // 4 for t in row) for row in ts]) if pair else 0.0
+    n_h = np.mean([sum((t + 1) // 128 for t in row) for row in ts])
+    csa_recs = sum(min(k, (t + 1) // 4) + 128 for t in ts[0]) if pair else 0
+    hca_recs = n_h + 128 * Bsz
+    rec_b = (d - 64) + 2 * 64 + 4
+    att_flops = (csa_recs + hca_recs) * H * 4 * d
+    att_bytes = (csa_recs + hca_recs) * rec_b + (2 if pair else 1) * 2 * Bsz * H * d * 2
+    score_bytes = n_vis * (dI + 4 + 4)
+    att_s = kern["attend"]["total_ms"] / steps * 1e-3
+    att_tf = att_flops / att_s / 1e12
+    att_gbs = att_bytes / att_s / 1e9
+    dom = "attend" if (not pair or kern["attend"]["total_ms"] >= kern["index_score"]["total_ms"]) else "index_score"
+    if dom == "attend":
+        roof = {"kernel": "k_attend_lo", "bound": "mfma", "achieved": round(att_tf, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        sc_gbs = score_bytes / (kern["index_score"]["total_ms"] / steps * 1e-3) / 1e9
+        roof = {"kernel": "k_index_score_decode", "bound": "hbm", "achieved": round(sc_gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(sc_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    name = ("CSA/HCA decode queries/s (4 requests at 1M/512K/64K/4K context)" if pair else
+            "HCA decode queries/s (16 requests at 64K context)")
+    res = {
+        "metric": name, "value": round(Bsz / (ms_step * 1e-3), 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8/bf16", "data": "synthetic",
+        "config": {"workload": ("V4 CSA+HCA layer-pair decode, contexts " + "/".join(f"{c // 1024}K" for c in ctxs)
+                                if pair else f"V4 HCA layer decode, batch {Bsz} x {ctxs[0] // 1024}K"),
+                   "batch": Bsz, "ctx": ctxs, "topk": k if pair else None, "heads": H, "d": d, "policy": a.policy},
+        "roofline": roof,
+        "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items()},
+        "launches_per_step": {n_: v["launches"] / steps for n_, v in kern.items()},
+        "attend_TFLOPs": round(att_tf, 1), "attend_GBps": round(att_gbs, 1),
         "setup_s": round(t_setup, 1),
     }
     print(json.dumps(res), flush=True)
