@@ -91,11 +91,58 @@ ORC_API float orc_bf16_round(float x) {
     return r;
 }
 
+/* ------------------------------------------------------------------------ */
+/* FP4 of the indexer's query and key activations.  [R] section on FP4 QAT:  */
+/* the lightning indexer's QK activations are cached, loaded and multiplied  */
+/* in FP4; [X] 2.1: FP4 on the CSA indexer path; [H] 二, CSA step 2: the      */
+/* indexer scores in low precision (FP4).  The pages name no FP4 layout.     */
+/* Reading: OCP Microscaling MXFP4 -- blocks of 32 consecutive values share  */
+/* one power-of-two scale 2^x (an E8M0 byte, x in [-127, 127]) and each      */
+/* value is an E2M1 code: sign, 2 exponent bits (bias 1), 1 mantissa bit,    */
+/* magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (no infinities, no NaN).            */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an E2M1 code (low 4 bits), straight from the format definition. */
+ORC_API double orc_e2m1_decode(uint8_t c) {
+    int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+/* Nearest E2M1 code of y, ties to even mantissa, saturating to +-6 (the
+ * microscaling conversion rule for values past the largest magnitude).  As
+ * for E4M3: inside binade [2^u, 2^(u+1)) the step is 2^(u-1); below 1 the
+ * subnormal step 0.5 continues the first binade's. */
+ORC_API uint8_t orc_e2m1_encode(float y) {
+    uint8_t sign = signbit(y) ? 8 : 0;
+    double a = fabs((double)y);
+    if (!(a < 6.0)) return sign | 7;
+    int e;                              /* a = f * 2^e with f in [0.5, 1) */
+    frexp(a, &e);
+    int unb = e - 1;                    /* floor(log2 a)                  */
+    if (a == 0.0 || unb < 0) unb = 0;
+    double q = rint(ldexp(a, 1 - unb)); /* a / step, step = 2^(unb-1)     */
+    return sign | (uint8_t)(2 * unb + (int)q);
+}
+
+/* Shared exponent x of a block with largest magnitude amax: the microscaling
+ * rule x = floor(log2 amax) - 2 (2 = exponent of E2M1's largest magnitude),
+ * clamped to the E8M0 range; an all-zero block takes the smallest scale. */
+ORC_API int orc_mx_exponent(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    int e;
+    frexp((double)amax, &e);
+    int x = (e - 1) - 2;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
 /* Store one vector of n values the way the cache holds it and return the
  * value the cache then represents (fp64, exact).
  *   mode 0 : fp32 storage (each value rounded to fp32).
  *   mode 1 : the first n_fp8 values as E4M3 codes sharing one fp32 scale,
  *            the remaining n - n_fp8 values as bf16.
+ *   mode 2 : (indexer rows) MXFP4, blocks of 32 consecutive values, each
+ *            with its shared exponent from its own largest magnitude.
  * Scale rule (one reading of "FP8" in [V]): scale = amax / 448 with
  * code = E4M3(x * (448 / amax)); both quotients and the product are fp32
  * operations, the precision in which the kernels take the same decision.
@@ -104,6 +151,19 @@ ORC_API float orc_bf16_round(float x) {
 ORC_API void orc_store_vec(const double *x, int n, int n_fp8, int mode, double *out) {
     if (mode == 0) {
         for (int i = 0; i < n; ++i) out[i] = (double)(float)x[i];
+        return;
+    }
+    if (mode == 2) {                    /* MXFP4: all n values, blocks of 32 */
+        for (int b0 = 0; b0 < n; b0 += 32) {
+            const int nb = n - b0 < 32 ? n - b0 : 32;
+            float amax = 0.0f;
+            for (int i = 0; i < nb; ++i) amax = fmaxf(amax, fabsf((float)x[b0 + i]));
+            const int e = orc_mx_exponent(amax);
+            for (int i = 0; i < nb; ++i) {
+                const float y = ldexpf((float)x[b0 + i], -e);   /* exact: a power of two */
+                out[b0 + i] = ldexp(orc_e2m1_decode(orc_e2m1_encode(y)), e);
+            }
+        }
         return;
     }
     float amax = 0.0f;

@@ -61,6 +61,12 @@ def lib():
         L.orc_e4m3_encode.argtypes = [ctypes.c_float]
         L.orc_bf16_round.restype = ctypes.c_float
         L.orc_bf16_round.argtypes = [ctypes.c_float]
+        L.orc_e2m1_decode.restype = ctypes.c_double
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_e2m1_encode.argtypes = [ctypes.c_float]
+        L.orc_mx_exponent.restype = ctypes.c_int
+        L.orc_mx_exponent.argtypes = [ctypes.c_float]
         L.orc_store_rows.argtypes = [dp, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         L.orc_rope_rows.argtypes = [dp, ctypes.c_long, ctypes.c_int, ctypes.c_int, dp, ctypes.c_double]
         L.orc_pool_entries.argtypes = [dp, dp, ctypes.c_int, ctypes.POINTER(ctypes.c_long),
@@ -98,7 +104,8 @@ class OCfg:
     idx_dim: int = 128
     topk: int = 1024
     kv_mode: int = 1        # 0: fp32 storage, 1: FP8 E4M3 (one scale) + BF16 RoPE dims
-    idx_mode: int = 1       # 0: fp32 index keys / queries, 1: FP8 E4M3 with one scale per row
+    idx_mode: int = 1       # 0: fp32 index keys / queries, 1: FP8 E4M3 with one scale per row,
+                            # 2: MXFP4 (E2M1 codes, one power-of-two scale per 32 dims)
     rope_base: float = 10000.0
     tau: float = field(default=float("nan"))  # softmax scale, default 1/sqrt(d)
 
@@ -126,6 +133,18 @@ def bf16_round(x: float) -> float:
     return lib().orc_bf16_round(x)
 
 
+def e2m1_decode(code: int) -> float:
+    return lib().orc_e2m1_decode(code)
+
+
+def e2m1_encode(y: float) -> int:
+    return lib().orc_e2m1_encode(y)
+
+
+def mx_exponent(amax: float) -> int:
+    return lib().orc_mx_exponent(amax)
+
+
 def store_records(x, cfg: OCfg) -> np.ndarray:
     """KV record storage: fp8 first d - d_rope dims (one scale), bf16 RoPE dims."""
     x = _f64(x).reshape(-1, cfg.d)
@@ -135,7 +154,8 @@ def store_records(x, cfg: OCfg) -> np.ndarray:
 
 
 def store_index_rows(x, cfg: OCfg) -> np.ndarray:
-    """Index keys and index queries: all idx_dim dims FP8 with one scale per row."""
+    """Index keys and index queries: all idx_dim dims FP8 with one scale per row
+    (idx_mode 1), or MXFP4 with one power-of-two scale per 32 dims (idx_mode 2)."""
     x = _f64(x).reshape(-1, cfg.idx_dim)
     out = np.empty_like(x)
     lib().orc_store_rows(_dp(x), x.shape[0], cfg.idx_dim, cfg.idx_dim, cfg.idx_mode, _dp(out))

@@ -64,6 +64,76 @@ def test_bf16_round_matches_torch_and_hand():
     assert (got == ref).all()
 
 
+def test_e2m1_table_and_hand_cases():
+    g = gold("hand_cases.json")["e2m1"]
+    for c in range(16):
+        v = O.e2m1_decode(c)
+        assert v == g["decode"][c] and math.copysign(1, v) == math.copysign(1, g["decode"][c]), c
+        assert O.e2m1_encode(v) == c, c
+    for y, code in g["encode"]:
+        assert O.e2m1_encode(y) == code, y
+
+
+def test_e2m1_encode_is_nearest_by_search():
+    """Brute force: the nearest of the 8 magnitudes, ties to the even mantissa
+    bit (bit 0 of the code), saturating past 6."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    rng = np.random.default_rng(5)
+    ys = np.concatenate([np.arange(-8.0, 8.0 + 1e-9, 1.0 / 64), rng.uniform(-7, 7, 3000),
+                         [(a + b) / 2 for a, b in zip(mags[:-1], mags[1:])]]).astype(np.float32)
+    for y in ys:
+        a = abs(float(y))
+        dist = [abs(a - m) for m in mags]
+        best = min(dist)
+        cand = [c for c in range(8) if dist[c] == best]
+        c = cand[0] if len(cand) == 1 else [k for k in cand if k % 2 == 0][0]
+        want = c | (8 if math.copysign(1, float(y)) < 0 else 0)
+        assert O.e2m1_encode(float(y)) == want, float(y)
+
+
+def test_mx_exponent_rule():
+    for amax, x in [(1.0, -2), (6.0, 0), (7.99, 0), (8.0, 1), (0.3, -4), (0.25, -4), (0.0, -127),
+                    (2.0 ** -130, -127), (3.0e38, 125)]:
+        assert O.mx_exponent(amax) == x, amax
+    rng = np.random.default_rng(9)
+    for a in rng.lognormal(0, 4, 2000).astype(np.float32):
+        x = O.mx_exponent(float(a))
+        # the block's largest magnitude lands in [4, 8) after scaling (largest E2M1 binade)
+        assert 4.0 <= float(a) / 2.0 ** x < 8.0
+
+
+def test_mxfp4_store_rows_hand_and_bounds():
+    cfg = O.OCfg(idx_dim=32, idx_heads=4, idx_mode=2)
+    for case in gold("hand_cases.json")["mx_block"]["cases"]:
+        x = np.zeros(32)
+        x[:len(case["x"])] = case["x"]
+        st = O.store_index_rows(x, cfg)[0]
+        assert list(st[:len(case["expect"])]) == case["expect"]
+        assert (st[len(case["expect"]):] == 0).all()
+    # 128-dim rows: four independent blocks; every stored value is an E2M1
+    # value times its block's scale, within half a code step of the input
+    cfg = O.OCfg(idx_dim=128, idx_mode=2)
+    rng = np.random.default_rng(13)
+    x = rng.normal(0, 1, (200, 128)) * rng.lognormal(0, 2, (200, 1))
+    st = O.store_index_rows(x, cfg)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for r in range(200):
+        for b in range(4):
+            xb = x[r, 32 * b:32 * b + 32].astype(np.float32).astype(np.float64)
+            e = O.mx_exponent(float(np.abs(xb).max()))
+            y = st[r, 32 * b:32 * b + 32] / 2.0 ** e
+            assert np.isin(np.abs(y), mags).all()
+            u = np.abs(xb) / 2.0 ** e
+            step = np.where(u < 2, 0.5, np.where(u < 4, 1.0, 2.0))
+            err = np.abs(np.abs(y) - np.minimum(u, 6.0))
+            assert (err <= step / 2 + 1e-12).all()
+            assert (np.sign(y) * np.sign(xb) >= 0).all()
+    # a block's scale does not depend on the other blocks of the row
+    x2 = x.copy()
+    x2[:, 32:] *= 1000.0
+    assert np.array_equal(O.store_index_rows(x2, cfg)[:, :32], st[:, :32])
+
+
 def test_store_records_structure():
     cfg = O.OCfg(d=64, d_rope=16, n_heads=8)
     rng = np.random.default_rng(11)
