@@ -69,6 +69,8 @@ typedef int32_t dsv4_status;
 #define DSV4_STORE_FP32 0        /* records / index keys as fp32 (reference-precision mode) */
 #define DSV4_STORE_FP8 1         /* records: E4M3 non-RoPE dims + one fp32 scale + BF16 RoPE dims;
                                     index keys / queries: E4M3 + one fp32 scale per row */
+#define DSV4_STORE_MXFP4 2       /* index keys / queries only: OCP MXFP4 -- E2M1 codes, one E8M0
+                                    (power-of-two) scale per 32 consecutive dims */
 
 /* activation dtypes */
 #define DSV4_DT_F32 0
@@ -102,7 +104,10 @@ typedef int32_t dsv4_status;
  *   idx_dim      indexer head dim (multiple of 32, <= 128)                 [128]
  *   topk         entries kept per CSA query (<= 2048)                      [1024]
  *   kv_store     DSV4_STORE_FP8 (production) or DSV4_STORE_FP32
- *   idx_store    DSV4_STORE_FP8 (production) or DSV4_STORE_FP32
+ *   idx_store    DSV4_STORE_FP8 (production), DSV4_STORE_MXFP4 (the indexer in
+ *                FP4: rqlyzj.com section on FP4 QAT -- the indexer's QK
+ *                activations cached, loaded and multiplied in FP4;
+ *                hwcomputing.csdn.net section 二, CSA step 2) or DSV4_STORE_FP32
  *   act_dtype    DSV4_DT_BF16 or DSV4_DT_F32 for kv/gate/kI/gI/q/qI/out
  *   rope_base    [10000]
  *   softmax_scale tau in tau * q.k                                         [1/sqrt(d)]
@@ -150,6 +155,10 @@ typedef struct dsv4_cache {
  *  KV record (DSV4_STORE_FP32): d fp32 values (post-RoPE).
  *  Index block: entries_per_block keys of index_key_bytes (E4M3 or fp32)
  *    back to back, then (FP8 only) entries_per_block fp32 scales.
+ *  Index block (DSV4_STORE_MXFP4): entries_per_block keys of idx_dim/2 bytes
+ *    (dim 2i in the low nibble of byte i), then per key one 32-bit word of
+ *    E8M0 bytes, byte b the scale of dims [32b, 32b+32): the value of dim i
+ *    is E2M1(code_i) * 2^(byte - 127).
  *  State (per request): window ring of `window` records at offset 0, pending
  *    ring at pending_offset: pending_slots raw tokens, each
  *    [kv d][gate d][kI idx_dim][gI idx_dim] fp32 (kI, gI for CSA only).
@@ -228,7 +237,8 @@ dsv4_status dsv4_compress_kv_prefill(const dsv4_cfg *cfg, const dsv4_cache *cach
  * Lightning indexer + top-k, decode (CSA).  For query b at position t =
  * pos_dev[b] over the visible entries j < floor((t+1)/m):
  *   I[j] = sum_h w[b][h] * max(0, qI[b][h] . kI_j)
- * with qI quantised like the index keys (E4M3, one scale per (query, head)),
+ * with qI quantised like the index keys (E4M3 with one scale per (query,
+ * head), or MXFP4 with one per (query, head, 32 dims)),
  * then the min(k, N) largest I by (score desc, index asc), written ascending
  * to topk_dev[b][0..k), padded with -1.  Sources: vastsailsolution.com CSA
  * section (indexer: query projected into ReLU index heads scored against the

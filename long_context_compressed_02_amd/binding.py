@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libdsv4attn.so")
 
 DSV4_OK, DSV4_ERR_INVALID_ARG, DSV4_ERR_UNSUPPORTED, DSV4_ERR_WORKSPACE, DSV4_ERR_LAUNCH, DSV4_ERR_HIP = range(6)
 DSV4_CSA, DSV4_HCA = 0, 1
-DSV4_STORE_FP32, DSV4_STORE_FP8 = 0, 1
+DSV4_STORE_FP32, DSV4_STORE_FP8, DSV4_STORE_MXFP4 = 0, 1, 2
 DSV4_DT_F32, DSV4_DT_BF16 = 0, 1
 DSV4_POLICY_AUTO, DSV4_POLICY_HI, DSV4_POLICY_LO = 0, 1, 2
 DSV4_TARGET_ENTRY, DSV4_TARGET_INDEX_KEY = 0, 1

@@ -105,13 +105,15 @@ dsv4_status make_layout(const dsv4_cfg *c, int32_t kind, Lay *out) {
     if (c->idx_dim < 32 || c->idx_dim > 128 || (c->idx_dim % 32)) return DSV4_ERR_INVALID_ARG;
     if (c->topk < 1 || c->topk > 2048) return DSV4_ERR_INVALID_ARG;
     if (c->kv_store != DSV4_STORE_FP8 && c->kv_store != DSV4_STORE_FP32) return DSV4_ERR_INVALID_ARG;
-    if (c->idx_store != DSV4_STORE_FP8 && c->idx_store != DSV4_STORE_FP32) return DSV4_ERR_INVALID_ARG;
+    if (c->idx_store != DSV4_STORE_FP8 && c->idx_store != DSV4_STORE_FP32 && c->idx_store != DSV4_STORE_MXFP4)
+        return DSV4_ERR_INVALID_ARG;
     if (c->act_dtype != DSV4_DT_F32 && c->act_dtype != DSV4_DT_BF16) return DSV4_ERR_INVALID_ARG;
     if (!(c->rope_base > 0.0f) || !isfinite(c->rope_base)) return DSV4_ERR_INVALID_ARG;
     if (!(c->softmax_scale > 0.0f) || !isfinite(c->softmax_scale)) return DSV4_ERR_INVALID_ARG;
     const bool shape_built = (c->d == 512 && c->d_rope == 64) || (c->d == 64 && c->d_rope == 16);
     if (!shape_built) return DSV4_ERR_UNSUPPORTED;
-    if (c->kv_store != DSV4_STORE_FP8 || c->idx_store != DSV4_STORE_FP8) return DSV4_ERR_UNSUPPORTED;
+    if (c->kv_store != DSV4_STORE_FP8 || (c->idx_store != DSV4_STORE_FP8 && c->idx_store != DSV4_STORE_MXFP4))
+        return DSV4_ERR_UNSUPPORTED;
 
     Lay L;
     memset(&L, 0, sizeof(L));
@@ -142,7 +144,7 @@ dsv4_status make_layout(const dsv4_cfg *c, int32_t kind, Lay *out) {
     L.entry_block_bytes = (int64_t)L.epb * L.rec_bytes;
     L.HI = c->idx_heads;
     L.dI = c->idx_dim;
-    L.key_bytes = c->idx_store == DSV4_STORE_FP8 ? L.dI : 4 * L.dI;
+    L.key_bytes = c->idx_store == DSV4_STORE_MXFP4 ? L.dI / 2 : c->idx_store == DSV4_STORE_FP8 ? L.dI : 4 * L.dI;
     L.key_scale_off = L.epb * L.key_bytes;
     L.index_block_bytes = kind == DSV4_CSA ? al((int64_t)L.epb * L.key_bytes + (int64_t)L.epb * 4, 256) : 0;
     for (int i = 0; i < L.dr / 2 && i < 64; ++i)

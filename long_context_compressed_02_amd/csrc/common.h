@@ -58,6 +58,62 @@ __device__ __forceinline__ uint32_t fp8_code(float y) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
 }
 
+// OCP MXFP4 (indexer rows): blocks of 32 consecutive values share a
+// power-of-two scale 2^x stored as an E8M0 byte x + 127; each value is an
+// E2M1 code (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+//
+// Nearest E2M1 code of y, ties to the even mantissa bit, saturating to +-6:
+// inside binade [2^u, 2^(u+1)) (u = 0, 1, 2) the step is 2^(u-1), and below 1
+// the step 0.5 of the first binade continues down to 0.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+    const uint32_t s = (__float_as_uint(y) >> 28) & 8u;
+    const float a = fabsf(y);
+    if (!(a < 6.0f)) return s | 7u;
+    const int u = a >= 1.0f ? (int)(__float_as_uint(a) >> 23) - 127 : 0;
+    const float q = __builtin_rintf(__builtin_ldexpf(a, 1 - u));   // a / step, exact scaling
+    return s | (uint32_t)(2 * u + (int)q);
+}
+
+// Shared exponent of a block whose largest magnitude is amax: floor(log2 amax)
+// - 2 (2: the exponent of E2M1's largest magnitude, so the block's largest
+// value scales into [4, 8)), clamped to the E8M0 range; -127 for a block of
+// zeros (and for amax below the smallest normal fp32, where the rule gives
+// less than -127 anyway).
+__device__ __forceinline__ int mx_exponent(float amax) {
+    if (!(amax >= 1.17549435e-38f)) return -127;
+    const int x = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 2;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// One MXFP4 row of at most 128 values held by a wave, two per lane (lane l:
+// values 2l and 2l+1; v0, v1 say which are real): the 16 lanes of a DPP row
+// hold one 32-value block.  Returns the lane's code byte (value 2l in the low
+// nibble); *scales receives the four E8M0 bytes, block b in byte b (blocks
+// without real values get byte 0 and all-zero codes).
+__device__ __forceinline__ uint32_t mx4_row(float x0, float x1, bool v0, bool v1, uint32_t *scales) {
+    float am = fmaxf(v0 ? fabsf(x0) : 0.0f, v1 ? fabsf(x1) : 0.0f);
+    const int zero = 0;
+    am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(zero, __float_as_int(am), 0x111, 0xf, 0xf, false)));
+    am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(zero, __float_as_int(am), 0x112, 0xf, 0xf, false)));
+    am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(zero, __float_as_int(am), 0x114, 0xf, 0xf, false)));
+    am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(zero, __float_as_int(am), 0x118, 0xf, 0xf, false)));
+    // lane 16b+15 now holds block b's largest magnitude
+    uint32_t sc = 0, mine = 0;
+    const int row = (int)(threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int xb = mx_exponent(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), 16 * b + 15)));
+        sc |= (uint32_t)(xb + 127) << (8 * b);
+        mine = b == row ? (uint32_t)(xb + 127) : mine;
+    }
+    const int x = (int)mine - 127;
+    const uint32_t c0 = v0 ? e2m1_code(__builtin_ldexpf(x0, -x)) : 0u;
+    const uint32_t c1 = v1 ? e2m1_code(__builtin_ldexpf(x1, -x)) : 0u;
+    *scales = sc;
+    return c0 | (c1 << 4);
+}
+
 // Activation loads/stores in the configured dtype.
 __device__ __forceinline__ float load_act(const void *p, int64_t i, int act) {
     if (act == DSV4_DT_BF16) return bf16_to_f32(((const uint16_t *)p)[i]);

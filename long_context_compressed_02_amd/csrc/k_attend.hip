@@ -759,21 +759,40 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
         }
     };
 
-    // ---- chunk loads (same line-wise pattern as k_attend, all NLD loads of a
-    // chunk on this wave)
+    // ---- chunk loads, all NLD of a chunk on this wave.  When the code and
+    // RoPE pieces each come in whole groups of four, a chunk is loaded in the
+    // logits' operand layout -- lane (g, c16) holds pieces 4k+g of record
+    // 16rb+c16, load rb*KPR+k -- and the logits take their key operands from
+    // those registers; LDS then holds the chunk only for the transposed reads
+    // of O^T += V^T P^T (and the scales).  Otherwise the loads follow k_attend's
+    // line-wise pattern and both products read the chunk from LDS.
+    constexpr bool REGQK = NCH % 4 == 0 && RCH % 4 == 0;
+    constexpr int KPR = PPR / 4;                         // loads per record block (operand layout)
+    static_assert(PPR % 4 == 0 && NLD == 2 * KPR, "two record blocks of KPR loads per chunk");
     const int ld_a = lane / LW, ld_b = lane % LW;
     auto slot = [&](int c, int r) { return buf + (r * RS + c + (r >> 4) * SWZ) * 16; };
+    auto piece_rc = [&](int i, int &r, int &c) {
+        if constexpr (REGQK) {
+            r = 16 * (i / KPR) + c16;
+            c = 4 * (i % KPR) + g;
+        } else {
+            r = RPI * (i / (PPR / LW)) + ld_a;
+            c = LW * (i % (PPR / LW)) + ld_b;
+        }
+    };
     auto issue = [&](u32x4 (&pre)[NLD], int t) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int r = RPI * (i / (PPR / LW)) + ld_a, c = LW * (i % (PPR / LW)) + ld_b;
+            int r, c;
+            piece_rc(i, r, c);
             pre[i] = *(const u32x4 *)(loc_addr<PREFILL>(A, Q, locs[t * kChunk + r]) + 16 * c);
         }
     };
     auto stage = [&](const u32x4 (&pre)[NLD]) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-            const int r = RPI * (i / (PPR / LW)) + ld_a, c = LW * (i % (PPR / LW)) + ld_b;
+            int r, c;
+            piece_rc(i, r, c);
             *(u32x4 *)slot(c, r) = pre[i];
         }
     };
@@ -870,25 +889,29 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     // ---- one chunk: logits from the partial chains, online softmax, O^T += V^T P^T
     AttnState<NDB> S;
     state_clear(S);
-    auto compute = [&](int t) {
+    auto compute = [&](int t, u32x4 (&pre)[NLD], bool refill) {
         float lg[2][4], sc[2][4];
+        float dot[2][4], dr[2][4];
         const uint32_t vm = vmask[t];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            // all of the block's operand pieces first (their LDS latencies overlap),
-            // then the chains interleaved: chain q keeps its pairs in order
+            // all of the block's operand pieces first (from the registers, or
+            // from LDS with their latencies overlapped), then the chains
+            // interleaved: chain q keeps its pairs in order
             u32x4 u[KP], ur[KR];
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp) {
                 const int ch = 4 * kp + g;
                 u[kp] = (u32x4){0, 0, 0, 0};
-                if (NCH % 4 == 0 || ch < NCH) u[kp] = *(const u32x4 *)slot(ch, 16 * rb + c16);
+                if constexpr (REGQK) u[kp] = pre[rb * KPR + kp];
+                else if (NCH % 4 == 0 || ch < NCH) u[kp] = *(const u32x4 *)slot(ch, 16 * rb + c16);
             }
 #pragma unroll
             for (int ks = 0; ks < KR; ++ks) {
                 const int ch = 4 * ks + g;
                 ur[ks] = (u32x4){0, 0, 0, 0};
-                if (RCH % 4 == 0 || ch < RCH) ur[ks] = *(const u32x4 *)slot(NCH + ch, 16 * rb + c16);
+                if constexpr (REGQK) ur[ks] = pre[rb * KPR + NCH / 4 + ks];
+                else if (RCH % 4 == 0 || ch < RCH) ur[ks] = *(const u32x4 *)slot(NCH + ch, 16 * rb + c16);
             }
             f32x4 x[kParts], xr = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -911,16 +934,27 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rb + 4 * g + i;
-                const bool ok = (vm >> r) & 1u;
-                sc[rb][i] = *(const float *)slot(CREC - 1, r);
                 float a = x[0][i];
 #pragma unroll
                 for (int q = 1; q < kParts; ++q) a = a + x[q][i];
-                lg[rb][i] = ok ? tau2 * (sc[rb][i] * a + xr[i]) : -INFINITY;
+                dot[rb][i] = a;
+                dr[rb][i] = xr[i];
             }
             __builtin_amdgcn_sched_barrier(0);   // one record block's operands at a time
         }
+        if constexpr (REGQK) {                   // the registers are free: next loads, then the staged chunk
+            if (refill) issue(pre, t + PFD);
+            wave_lds_fence();
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rb + 4 * g + i;
+                const bool ok = (vm >> r) & 1u;
+                sc[rb][i] = *(const float *)slot(CREC - 1, r);
+                lg[rb][i] = ok ? tau2 * (sc[rb][i] * dot[rb][i] + dr[rb][i]) : -INFINITY;
+            }
         float cmax = -INFINITY;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
@@ -985,9 +1019,11 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     auto step = [&](u32x4 (&pre)[NLD], int t) {
         wave_lds_fence();                    // the previous chunk's reads come first
         stage(pre);
-        if (t + PFD < mine) issue(pre, t + PFD);
-        wave_lds_fence();                    // staged chunk visible to the whole wave
-        compute(t);
+        if constexpr (!REGQK) {
+            if (t + PFD < mine) issue(pre, t + PFD);
+            wave_lds_fence();                // staged chunk visible to the whole wave
+        }
+        compute(t, pre, t + PFD < mine);
     };
     if constexpr (PFD == 2) {
 #pragma unroll 1

@@ -98,7 +98,8 @@ __device__ void store_record(const Lay &L, float (&x)[(D / 64) > 0 ? D / 64 : 1]
 }
 
 // Store an index key (dI <= 128 values) held by one wave: lane l owns dims
-// [l*KPL, l*KPL+KPL) with KPL = 2 (values past dI are ignored).
+// [l*KPL, l*KPL+KPL) with KPL = 2 (values past dI are ignored).  The 4-byte
+// scale slot holds the fp32 scale (FP8) or the four E8M0 block scales (MXFP4).
 __device__ void store_index_key(const Lay &L, const float (&x)[2], uint8_t *key, float *scale_slot) {
     const int lane = threadIdx.x & 63;
     const int d0 = lane * 2;
@@ -106,6 +107,13 @@ __device__ void store_index_key(const Lay &L, const float (&x)[2], uint8_t *key,
         float *o = (float *)key;
         if (d0 < L.dI) o[d0] = x[0];
         if (d0 + 1 < L.dI) o[d0 + 1] = x[1];
+        return;
+    }
+    if (L.idx_store == DSV4_STORE_MXFP4) {            // codes, then the key's word of block scales
+        uint32_t scales;
+        const uint32_t byte = mx4_row(x[0], x[1], d0 < L.dI, d0 + 1 < L.dI, &scales);
+        if (d0 < L.dI) key[lane] = (uint8_t)byte;
+        if (lane == 0) *(uint32_t *)scale_slot = scales;
         return;
     }
     float am = 0.0f;

@@ -29,8 +29,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- query quantisation
-// One wave per (query, head) row: E4M3 codes (zero-padded to 128 bytes) and
-// wq = w * scale.  Same decision rule as the stored index keys.
+// One wave per (query, head) row, into a 128-byte slot: E4M3 codes (zero-
+// padded to 128 bytes) and wq = w * scale, or (MXFP4) 64 bytes of E2M1 codes
+// (zero past dI), the word of E8M0 block scales at byte 64, and wq = w.  Same
+// decision rule as the stored index keys.
 __global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, const float *w,
                                                        int rows, uint8_t *q8, float *wq) {
     const int lane = threadIdx.x & 63;
@@ -39,6 +41,16 @@ __global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, co
     const int dI = L.dI;
     float x0 = 2 * lane < dI ? load_act(qI, row * dI + 2 * lane, L.act) : 0.0f;
     float x1 = 2 * lane + 1 < dI ? load_act(qI, row * dI + 2 * lane + 1, L.act) : 0.0f;
+    if (L.idx_store == DSV4_STORE_MXFP4) {
+        uint32_t scales;
+        const uint32_t byte = mx4_row(x0, x1, 2 * lane < dI, 2 * lane + 1 < dI, &scales);
+        q8[row * 128 + lane] = (uint8_t)byte;
+        if (lane == 0) {
+            *(uint32_t *)(q8 + row * 128 + 64) = scales;
+            wq[row] = w ? w[row] : 1.0f;
+        }
+        return;
+    }
     float am = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
     float scale = 1.0f, inv = 1.0f;
     if (am >= 1e-30f) {
@@ -79,9 +91,16 @@ constexpr int kKeysPerWG = 4 * kKeysPerWave;
 static_assert(kKeysPerWave % 64 == 0, "scoring ranges are whole pipeline groups");
 
 // HB: 16-row blocks of index heads (idx_heads <= 16*HB); FULL: idx_dim == 128
-// (no padded operand bytes).  Both are compile-time so that the loads and the
-// four MFMAs of a sub-block are straight-line code the compiler can pipeline.
-template <int HB, bool FULL>
+// (no padded operand bytes); F4: MXFP4 rows (E2M1 operands, the E8M0 block
+// scales applied by the MFMA itself).  All are compile-time so that the loads
+// and the MFMAs of a sub-block are straight-line code the compiler can pipeline.
+//
+// MXFP4: lane group g holds the 32 dims [32g, 32g+32) of a row -- 16 bytes,
+// one MX block -- and passes that block's E8M0 byte as its scale operand, so
+// the MFMA returns sum_b 2^(xq_b + xk_b) * (codes of block b . codes of block
+// b) (exact products, fp32 sums): the dot product of the stored values.  The
+// head weights then apply as they are (wq = w).
+template <int HB, bool FULL, bool F4>
 __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C, const uint8_t *q8,
                                                             const float *wq, const int32_t *req,
                                                             const int32_t *pos, float *scores,
@@ -103,14 +122,22 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     const i32x4 z4 = {0, 0, 0, 0};
     // A operand: query codes (zero-padded to 128 bytes per row), rows = index heads
     i32x8 A[HB];
+    uint32_t sa[HB];                               // (MXFP4) the lane's block scale per head block
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         const int row = hb * 16 + c16;
         const bool ok = row < L.HI;
         const uint8_t *p = q8 + ((int64_t)q * L.HI + (ok ? row : 0)) * 128;
         i32x8 a;
-        a.lo = *(const i32x4 *)(p + o0);
-        a.hi = *(const i32x4 *)(p + o1);
+        if constexpr (F4) {
+            a.lo = *(const i32x4 *)(p + 16 * g);
+            a.hi = z4;
+            sa[hb] = ok ? (*(const uint32_t *)(p + 64) >> (8 * g)) & 0xffu : 0u;
+        } else {
+            a.lo = *(const i32x4 *)(p + o0);
+            a.hi = *(const i32x4 *)(p + o1);
+            sa[hb] = 127u;
+        }
         A[hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
     }
     // head weights in LDS (registers are kept for the operands: at 96 VGPRs or
@@ -133,7 +160,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     // B operands: 16-key sub-blocks, each inside one 128-token cache block
     // (lane = key c16).  An unmapped block reads block 0 and is masked by its
     // zero scale.
-    auto load_sb = [&](int kb, i32x8 &Bk, float &sk) {
+    auto load_sb = [&](int kb, i32x8 &Bk, float &sk, uint32_t &sb) {
         const int kc = kb < N ? kb : k0;                       // stay in mapped memory past the end
         const int bi = (kc * L.m) / kBlockTokens - blk0;       // wave-uniform
         const int bid = bi < 64 ? __builtin_amdgcn_readlane(btv, bi)   // (ranges of 64+ blocks: strides >= 32)
@@ -142,6 +169,18 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
         const uint8_t *base = pool + (int64_t)(okb ? bid : 0) * L.index_block_bytes;
         const int slot0 = kc % L.epb;
         const uint8_t *p = base + slot0 * L.key_bytes + lane_off;
+        if constexpr (F4) {
+            // block g of the key: 16 bytes (zero when the key has no block g)
+            const bool vg = FULL || 16 * g < L.key_bytes;
+            const i32x4 l0 = *(const i32x4 *)(p + (vg ? 16 * g : 0));
+            Bk.lo = vg ? l0 : z4;
+            Bk.hi = z4;
+            const uint32_t w = ((const uint32_t *)(base + L.key_scale_off))[slot0 + c16];
+            sb = (w >> (8 * g)) & 0xffu;
+            sk = okb ? 1.0f : 0.0f;
+            return;
+        }
+        sb = 127u;
         if constexpr (FULL) {
             Bk.lo = *(const i32x4 *)(p + o0);
             Bk.hi = *(const i32x4 *)(p + o1);
@@ -157,12 +196,17 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     };
     float *srow = scores + (int64_t)q * ld;
     uint32_t kmn = 0xffffffffu, kmx = 0u;          // key range of the finite scores this lane writes
-    auto score_sb = [&](int kb, const i32x8 &Bk, float sk) {
+    auto score_sb = [&](int kb, const i32x8 &Bk, float sk, uint32_t sb) {
         f32x4 acc[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f},
-                                                                       0, 0, 0, 127, 0, 127);
+        for (int hb = 0; hb < HB; ++hb) {
+            if constexpr (F4)
+                acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    A[hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, (int)sa[hb], 0, (int)sb);
+            else
+                acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    A[hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+        }
         float part = 0.0f;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
@@ -185,24 +229,25 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     constexpr int NG = kKeysPerWave / 16 / GS;
     i32x8 B0[GS], B1[GS];
     float s0[GS], s1[GS];
+    uint32_t e0[GS], e1[GS];
 #pragma unroll
-    for (int i = 0; i < GS; ++i) load_sb(k0 + 16 * i, B0[i], s0[i]);
+    for (int i = 0; i < GS; ++i) load_sb(k0 + 16 * i, B0[i], s0[i], e0[i]);
 #pragma unroll
     for (int grp = 0; grp < NG; grp += 2) {
         const int kg = k0 + grp * GS * 16;
         if (kg >= N) break;                        // wave-uniform
 #pragma unroll
-        for (int i = 0; i < GS; ++i) load_sb(kg + GS * 16 + 16 * i, B1[i], s1[i]);
+        for (int i = 0; i < GS; ++i) load_sb(kg + GS * 16 + 16 * i, B1[i], s1[i], e1[i]);
 #pragma unroll
-        for (int i = 0; i < GS; ++i) score_sb(kg + 16 * i, B0[i], s0[i]);
+        for (int i = 0; i < GS; ++i) score_sb(kg + 16 * i, B0[i], s0[i], e0[i]);
         const int kh = kg + GS * 16;
         if (kh >= N) break;
         if (grp + 2 < NG) {
 #pragma unroll
-            for (int i = 0; i < GS; ++i) load_sb(kh + GS * 16 + 16 * i, B0[i], s0[i]);
+            for (int i = 0; i < GS; ++i) load_sb(kh + GS * 16 + 16 * i, B0[i], s0[i], e0[i]);
         }
 #pragma unroll
-        for (int i = 0; i < GS; ++i) score_sb(kh + 16 * i, B1[i], s1[i]);
+        for (int i = 0; i < GS; ++i) score_sb(kh + 16 * i, B1[i], s1[i], e1[i]);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -232,14 +277,15 @@ static_assert(kPfKeys % kPfChunk == 0, "whole tiles per workgroup");
 // LDS the prefill scorer needs beyond its static arrays: the block ids of its key range.
 int64_t score_prefill_dyn_lds(const Lay &L) { return ((int64_t)kPfKeys * L.m / kBlockTokens + 2) * 4; }
 
-template <int HB, bool FULL>
+template <int HB, bool FULL, bool F4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_index_score_prefill(Lay L, dsv4_cache C, const uint8_t *q8,
                                                              const float *wq, const int32_t *req,
                                                              const int32_t *pos, int n, float *scores,
                                                              int64_t ld, uint2 *wr, int nwr) {
     constexpr int QW = kPfWaveRows;
     __shared__ __attribute__((aligned(16))) uint8_t tile[2][kPfChunk * kPfRowBytes];
-    __shared__ float tsc[2][kPfChunk];
+    __shared__ float tsc[2][kPfChunk];                 // key scale (FP8), or 1 / 0: key mapped or not (MXFP4)
+    __shared__ uint32_t tsw[F4 ? 2 : 1][F4 ? kPfChunk : 1];   // (MXFP4) the keys' words of block scales
     __shared__ f32x4 wls[kPfRows][HB * 4];             // [row][hb][g]: heads hb*16 + 4g + i
     extern __shared__ int32_t btl[];                     // block ids of the key range
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -272,8 +318,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int blk0 = (kbeg * L.m) / kBlockTokens;
     const int nbl = (kPfKeys * L.m) / kBlockTokens + 2;
     const uint8_t *pool = (const uint8_t *)C.index_keys;
-    constexpr int PKMAX = 8;                             // 16-byte pieces of a 128-byte key
-    const int PK = dI / 16;
+    constexpr int PKMAX = F4 ? 4 : 8;                    // 16-byte pieces of a key (at most 64 / 128 bytes)
+    const int PK = L.key_bytes / 16;
     int done = 0;
 #pragma unroll
     for (int i = 0; i < kPfRows; ++i)
@@ -301,6 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // A operands of this wave's rows
         const int wr0 = wave * QW;                       // first row (within the workgroup) of this wave
         i32x8 A[QW][HB];
+        uint32_t sa[QW][HB];                             // (MXFP4) the lane's block scale
 #pragma unroll
         for (int i = 0; i < QW; ++i)
 #pragma unroll
@@ -310,7 +357,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 const uint8_t *p = q8 + ((int64_t)(ok ? row0 + wr0 + i : 0) * L.HI + (ok ? hrow : 0)) * 128;
                 i32x8 a;
                 a.lo = *(const i32x4 *)(p + 16 * g);
-                a.hi = *(const i32x4 *)(p + 64 + 16 * g);
+                if constexpr (F4) {
+                    a.hi = (i32x4){0, 0, 0, 0};
+                    sa[i][hb] = ok ? (*(const uint32_t *)(p + 64) >> (8 * g)) & 0xffu : 0u;
+                } else {
+                    a.hi = *(const i32x4 *)(p + 64 + 16 * g);
+                    sa[i][hb] = 127u;
+                }
                 A[i][hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
             }
         // one tile's loads: thread piece tid + 256u is piece (u mod PK) of key (tid + 256u) / PK;
@@ -318,6 +371,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // unmapped blocks, read block 0 and get scale 0.
         i32x4 stg[PKMAX];
         float stg_s;
+        uint32_t stg_w = 0;
         auto load_tile = [&](int kc0) {
 #pragma unroll
             for (int u = 0; u < PKMAX; ++u) {
@@ -331,9 +385,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             const int k = kc0 + tid;
             const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
             const bool ok = bid >= 0 && bid < C.n_blocks;
-            const float sv = *(const float *)(pool + (ok ? (int64_t)bid * L.index_block_bytes + L.key_scale_off +
-                                                               (k % L.epb) * 4 : 0));
-            stg_s = ok ? sv : 0.0f;
+            const uint32_t sv = *(const uint32_t *)(pool + (ok ? (int64_t)bid * L.index_block_bytes + L.key_scale_off +
+                                                                  (k % L.epb) * 4 : 0));
+            if constexpr (F4) {
+                stg_s = ok ? 1.0f : 0.0f;
+                stg_w = sv;
+            } else {
+                stg_s = ok ? __uint_as_float(sv) : 0.0f;
+            }
         };
         auto store_tile = [&](int b) {
 #pragma unroll
@@ -343,6 +402,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                 *(i32x4 *)(tile[b] + kk * kPfRowBytes + off) = stg[u];
             }
             tsc[b][tid] = stg_s;
+            if constexpr (F4) tsw[b][tid] = stg_w;
         };
         uint32_t kmn[QW], kmx[QW];
         // rows two at a time with no branch between them (their MFMAs, weightings
@@ -352,7 +412,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             i32x8 Bk;
             const uint8_t *kr = tile[b] + (sb * 16 + c16) * kPfRowBytes;
             Bk.lo = *(const i32x4 *)(kr + 16 * g);
-            Bk.hi = *(const i32x4 *)(kr + 64 + 16 * g);
+            uint32_t sbk = 127u;
+            if constexpr (F4) {
+                Bk.hi = (i32x4){0, 0, 0, 0};
+                sbk = (tsw[b][sb * 16 + c16] >> (8 * g)) & 0xffu;
+            } else {
+                Bk.hi = *(const i32x4 *)(kr + 64 + 16 * g);
+            }
             const float sk = tsc[b][sb * 16 + c16];
 #pragma unroll
             for (int i0 = 0; i0 < QW; i0 += 2) {
@@ -360,9 +426,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-                    for (int hb = 0; hb < HB; ++hb)
-                        acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            A[i0 + ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+                    for (int hb = 0; hb < HB; ++hb) {
+                        if constexpr (F4)
+                            acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                A[i0 + ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, (int)sa[i0 + ii][hb], 0,
+                                (int)sbk);
+                        else
+                            acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                A[i0 + ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+                    }
                 float part[2];
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
@@ -1203,20 +1275,24 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
     dim3 g((unsigned)((ws.ld + kKeysPerWG - 1) / kKeysPerWG), n);
     const int hb = (L.HI + 15) / 16;
     const bool full = L.dI == 128;
-#define DSV4_SCORE(HBV, FV) \
-    hipLaunchKernelGGL((k_index_score_decode<HBV, FV>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, ws.ld, \
-                       ws.wr, ws.nwr)
-    if (full) {
-        if (hb == 4) DSV4_SCORE(4, true);
-        else if (hb == 3) DSV4_SCORE(3, true);
-        else if (hb == 2) DSV4_SCORE(2, true);
-        else DSV4_SCORE(1, true);
+#define DSV4_SCORE(HBV, FV, F4V) \
+    hipLaunchKernelGGL((k_index_score_decode<HBV, FV, F4V>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, \
+                       ws.ld, ws.wr, ws.nwr)
+#define DSV4_SCORE_HB(FV, F4V)                \
+    do {                                      \
+        if (hb == 4) DSV4_SCORE(4, FV, F4V);  \
+        else if (hb == 3) DSV4_SCORE(3, FV, F4V); \
+        else if (hb == 2) DSV4_SCORE(2, FV, F4V); \
+        else DSV4_SCORE(1, FV, F4V);          \
+    } while (0)
+    if (L.idx_store == DSV4_STORE_MXFP4) {
+        if (full) DSV4_SCORE_HB(true, true);
+        else DSV4_SCORE_HB(false, true);
     } else {
-        if (hb == 4) DSV4_SCORE(4, false);
-        else if (hb == 3) DSV4_SCORE(3, false);
-        else if (hb == 2) DSV4_SCORE(2, false);
-        else DSV4_SCORE(1, false);
+        if (full) DSV4_SCORE_HB(true, false);
+        else DSV4_SCORE_HB(false, false);
     }
+#undef DSV4_SCORE_HB
 #undef DSV4_SCORE
     return hipGetLastError();
 }
@@ -1227,20 +1303,24 @@ hipError_t launch_score_prefill(const Lay &L, const dsv4_cache &C, const int32_t
     const int hb = (L.HI + 15) / 16;
     const bool full = L.dI == 128;
     const size_t dyn = (size_t)score_prefill_dyn_lds(L);
-#define DSV4_SCORE(HBV, FV) \
-    hipLaunchKernelGGL((k_index_score_prefill<HBV, FV>), g, dim3(256), dyn, s, L, C, ws.q8, ws.wq, req, pos, n, \
+#define DSV4_SCORE(HBV, FV, F4V) \
+    hipLaunchKernelGGL((k_index_score_prefill<HBV, FV, F4V>), g, dim3(256), dyn, s, L, C, ws.q8, ws.wq, req, pos, n, \
                        ws.scores, ws.ld, ws.wr, ws.nwr)
-    if (full) {
-        if (hb == 4) DSV4_SCORE(4, true);
-        else if (hb == 3) DSV4_SCORE(3, true);
-        else if (hb == 2) DSV4_SCORE(2, true);
-        else DSV4_SCORE(1, true);
+#define DSV4_SCORE_HB(FV, F4V)                \
+    do {                                      \
+        if (hb == 4) DSV4_SCORE(4, FV, F4V);  \
+        else if (hb == 3) DSV4_SCORE(3, FV, F4V); \
+        else if (hb == 2) DSV4_SCORE(2, FV, F4V); \
+        else DSV4_SCORE(1, FV, F4V);          \
+    } while (0)
+    if (L.idx_store == DSV4_STORE_MXFP4) {
+        if (full) DSV4_SCORE_HB(true, true);
+        else DSV4_SCORE_HB(false, true);
     } else {
-        if (hb == 4) DSV4_SCORE(4, false);
-        else if (hb == 3) DSV4_SCORE(3, false);
-        else if (hb == 2) DSV4_SCORE(2, false);
-        else DSV4_SCORE(1, false);
+        if (full) DSV4_SCORE_HB(true, false);
+        else DSV4_SCORE_HB(false, false);
     }
+#undef DSV4_SCORE_HB
 #undef DSV4_SCORE
     return hipGetLastError();
 }

@@ -12,13 +12,17 @@ from oracle import oracle as O
 DEV = "cuda"
 
 
-def cfgs(shape: dict, act=B.DSV4_DT_BF16, topk=None):
+# the oracle's storage mode for each of the library's index-row formats
+IDX_MODE = {B.DSV4_STORE_FP8: 1, B.DSV4_STORE_MXFP4: 2}
+
+
+def cfgs(shape: dict, act=B.DSV4_DT_BF16, topk=None, idx_store=B.DSV4_STORE_FP8):
     """The library's cfg and the oracle's cfg for the same shape."""
     sh = dict(shape)
     if topk is not None:
         sh["topk"] = topk
-    lib_cfg = B.make_cfg(act_dtype=act, **sh)
-    ocfg = O.OCfg(**sh)
+    lib_cfg = B.make_cfg(act_dtype=act, idx_store=idx_store, **sh)
+    ocfg = O.OCfg(idx_mode=IDX_MODE[idx_store], **sh)
     return lib_cfg, ocfg
 
 
@@ -59,9 +63,21 @@ def decode_records(raw: torch.Tensor, d: int, d_rope: int, rec_bytes: int) -> np
     return torch.cat([codes * scale, rope], dim=1).numpy()
 
 
-def decode_keys(raw_block: torch.Tensor, epb: int, d_i: int) -> np.ndarray:
+# E2M1 magnitudes of codes 0..7 (OCP MXFP4 element format); bit 3 is the sign
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def decode_keys(raw_block: torch.Tensor, epb: int, d_i: int, idx_store=B.DSV4_STORE_FP8) -> np.ndarray:
     """One index block -> float64 [epb, d_i]."""
     r = raw_block.cpu()
+    if idx_store == B.DSV4_STORE_MXFP4:
+        kb = d_i // 2
+        b = r[:epb * kb].view(epb, kb).numpy().astype(np.int64)
+        codes = np.stack([b & 15, b >> 4], axis=2).reshape(epb, d_i)      # dim 2i in the low nibble of byte i
+        vals = _E2M1[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+        words = r[epb * kb:epb * kb + 4 * epb].view(epb, 4).numpy().astype(np.int64)   # byte j: dims [32j, 32j+32)
+        exps = np.repeat(words[:, :d_i // 32] - 127, 32, axis=1)
+        return vals * np.exp2(exps.astype(np.float64))
     codes = r[:epb * d_i].view(epb, d_i).contiguous().view(torch.float8_e4m3fn).to(torch.float64)
     sc = r[epb * d_i:epb * d_i + 4 * epb].contiguous().view(torch.float32).to(torch.float64)
     return (codes * sc[:, None]).numpy()
@@ -88,7 +104,7 @@ def key_rows(cache: B.LayerCache, r: int, js, bt_host) -> np.ndarray:
         blk = int(bt_host[r, (j * (128 // epb)) // 128])
         if blk not in blocks:
             blocks[blk] = decode_keys(cache.index_keys[blk * lay.index_block_bytes:(blk + 1) * lay.index_block_bytes],
-                                      epb, cfg.idx_dim)
+                                      epb, cfg.idx_dim, cfg.idx_store)
         out.append(blocks[blk][j % epb])
     return np.stack(out)
 
@@ -123,6 +139,23 @@ def assert_records_close(got: np.ndarray, ref: np.ndarray, d_rope: int, max_flip
         scale = np.abs(ref[:, :dn]).max(axis=1, keepdims=True) / 448.0
         sub = np.broadcast_to(scale, diff.shape)[diff] * 2.0 ** -9
         assert (np.abs(g - r) <= np.maximum(step, sub) * 1.0001).all(), "a stored value is off by more than one step"
+
+
+def assert_mx_rows_close(got: np.ndarray, ref: np.ndarray, max_flip_frac=2e-3):
+    """MXFP4 rows computed on the two sides (pooled in fp32 on the GPU, fp64 in
+    the oracle) agree exactly except where a pre-rounding value straddles a
+    rounding boundary (then they differ by one E2M1 step, at most half the
+    block's largest magnitude) -- or, rarer, where a block's largest magnitude
+    straddles a power of two and the shared exponent moves by one."""
+    assert got.shape == ref.shape
+    diff = got != ref
+    frac = diff.mean()
+    assert frac <= max_flip_frac, f"{frac:.2e} of stored values differ"
+    if diff.any():
+        nb = got.shape[1] // 32
+        bmax = np.abs(ref).reshape(-1, nb, 32).max(axis=2)
+        bound = np.repeat(bmax, 32, axis=1) * 0.5
+        assert (np.abs(got - ref)[diff] <= bound[diff] * 1.0001).all(), "a stored value is off by more than one step"
 
 
 def rel_err_per_head(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -56,6 +56,28 @@ def test_cache_write_entries(shape, kind):
             assert np.array_equal(Hh.key_rows(cache, r, js, bth), O.store_index_rows(kv, oc))
 
 
+@pytest.mark.parametrize("shape", [PROD, TINY], ids=["d512", "d64"])
+def test_cache_write_index_keys_mxfp4(shape):
+    """MXFP4 index keys: codes and block exponents are fp32 decisions on both
+    sides, so the stored values match the oracle's exactly."""
+    cfg, oc = Hh.cfgs(shape, idx_store=B.DSV4_STORE_MXFP4)
+    ctx = [4000, 9000]
+    cache, bth = _new_cache(cfg, B.DSV4_CSA, ctx)
+    rng = np.random.default_rng(6)
+    for r, c in enumerate(ctx):
+        n = c // oc.m_csa
+        js = np.arange(n)
+        # wide dynamic range across keys and across the blocks of a key
+        kv = (rng.standard_normal((n, oc.idx_dim), dtype=np.float32) *
+              rng.lognormal(0, 3, (n, 1)).astype(np.float32) *
+              np.repeat(rng.lognormal(0, 1, (1, oc.idx_dim // 32)), 32, axis=1).astype(np.float32))
+        kv[0] = 0.0                                       # an all-zero key
+        B.dsv4_cache_write_entries(cfg, cache, B.DSV4_TARGET_INDEX_KEY, Hh.i32([r] * n), Hh.i32(js),
+                                   torch.from_numpy(kv).to(Hh.DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(Hh.key_rows(cache, r, js, bth), O.store_index_rows(kv, oc))
+
+
 # ------------------------------------------------------------------ compressor
 def _tokens(oc, T, seed):
     g = np.random.default_rng([7, seed])
@@ -67,10 +89,11 @@ def _tokens(oc, T, seed):
 
 
 @pytest.mark.parametrize("shape", [PROD, TINY], ids=["d512", "d64"])
-@pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
-def test_compress_decode_equals_prefill_and_oracle(shape, kind):
+@pytest.mark.parametrize("kind,idx", [(B.DSV4_CSA, B.DSV4_STORE_FP8), (B.DSV4_HCA, B.DSV4_STORE_FP8),
+                                      (B.DSV4_CSA, B.DSV4_STORE_MXFP4)], ids=["csa", "hca", "csa-mxfp4"])
+def test_compress_decode_equals_prefill_and_oracle(shape, kind, idx):
     act = B.DSV4_DT_BF16
-    cfg, oc = Hh.cfgs(shape, act=act)
+    cfg, oc = Hh.cfgs(shape, act=act, idx_store=idx)
     T = 300 if kind == B.DSV4_CSA else 400
     nreq = 2
     csa = kind == B.DSV4_CSA
@@ -116,15 +139,19 @@ def test_compress_decode_equals_prefill_and_oracle(shape, kind):
         if csa:
             gk = Hh.key_rows(dec, r, js, bth)
             rk = O.index_keys_from_pool(kI, gI, js, oc)
-            Hh.assert_records_close(gk, rk, 0)
+            if idx == B.DSV4_STORE_MXFP4:
+                Hh.assert_mx_rows_close(gk, rk)
+            else:
+                Hh.assert_records_close(gk, rk, 0)
         wpos = list(range(T - oc.window, T))
         Hh.assert_records_close(Hh.window_rows(dec, r, wpos), O.window_records(kv[wpos], wpos, oc), oc.d_rope)
 
 
 # ------------------------------------------------------------------ indexer + top-k
 @pytest.mark.parametrize("k", [256, 1024])
-def test_index_topk_decode(k):
-    cfg, oc = Hh.cfgs(PROD, topk=k)
+@pytest.mark.parametrize("idx", [B.DSV4_STORE_FP8, B.DSV4_STORE_MXFP4], ids=["fp8", "mxfp4"])
+def test_index_topk_decode(k, idx):
+    cfg, oc = Hh.cfgs(PROD, topk=k, idx_store=idx)
     ctx = [3, 1000, 4099, 20001, 4000, 160004]   # query position t = ctx - 1 (the last: two top-k segments)
     cache, bth = _new_cache(cfg, B.DSV4_CSA, ctx, seed=2)
     nq = len(ctx)

@@ -12,6 +12,8 @@ invariance at full size (bitwise).
                     blocks at other addresses) must give the same bytes
   prefill_8k_on_256k  one 8192-token chunk appended to a 256K-token prefix
                     (65536 CSA entries), top-512
+  index_mxfp4_decode_128k_b32  the decode indexer + top-k of decode_128k_b32
+                    with MXFP4 index rows
 
 Inputs are seeded synthetic N(0,1) values of the workloads' shapes.  Entries and
 index keys are written through the cache-fill call; the oracle stores the same
@@ -183,6 +185,47 @@ def test_decode_128k_b32():
         swaps += _check(gtk[r], go[r], idx, s, o, oc.topk, f"csa r{r}")
         oh_ref = _oracle_hca(d, t, qhx[r], sinks, oc)
         _check(None, gh[r], None, None, oh_ref, 0, f"hca r{r}")
+    assert swaps <= 2
+
+
+# ------------------------------------------------------------------ the same step with the indexer in MXFP4
+def test_index_mxfp4_decode_128k_b32():
+    """The decode indexer + top-k at batch 32 x 128K (32768 keys per request)
+    with MXFP4 index keys and queries: replicas on other blocks give the same
+    bytes, and the two distinct requests match the oracle's MXFP4 selection."""
+    w = synth.CSA_DECODE_128K
+    cfg, oc = Hh.cfgs(w.shape(), idx_store=B.DSV4_STORE_MXFP4)
+    ctx = 131072
+    n_req = 32
+    print("index_mxfp4_decode_128k_b32: building caches", flush=True)
+    distinct = [Req((5, i), ctx, oc, with_hca=False) for i in range(2)]
+    bt, nb, mb = Hh.block_table([ctx] * n_req, extra_blocks=4, seed=n_req)
+    csa = B.LayerCache(cfg, B.DSV4_CSA, n_req, mb, nb, bt)
+    for r in range(n_req):
+        d = distinct[r % 2]
+        if not hasattr(d, "_keys_dev"):
+            d._keys_dev = torch.from_numpy(d.keys).to(DEV)
+        _fill(cfg, csa, B.DSV4_TARGET_INDEX_KEY, r, d._keys_dev)
+    _, qI1, w1 = synth.decode_queries(w, 2, sub=41)
+    rep = lambda a: np.ascontiguousarray(np.concatenate([a] * (n_req // 2)))
+    qIt, qIx = Hh.act_tensor(rep(qI1), ACT)
+    wt = torch.from_numpy(rep(w1)).to(DEV)
+    t = ctx - 1
+    ws = torch.empty(B.dsv4_workspace_bytes(cfg, n_req, mb * 32), dtype=torch.uint8, device=DEV)
+    tk = torch.empty((n_req, oc.topk), dtype=torch.int32, device=DEV)
+    print("index_mxfp4_decode_128k_b32: running", flush=True)
+    B.dsv4_index_topk_decode(cfg, csa, qIt, wt, Hh.i32(range(n_req)), Hh.i32([t] * n_req), tk, ws)
+    torch.cuda.synchronize()
+    for r in range(2, n_req):
+        assert torch.equal(tk[r], tk[r % 2])
+    gtk = tk.cpu().numpy()
+    swaps = 0
+    for r in range(2):
+        keys = O.store_index_rows(distinct[r].keys[: (t + 1) // oc.m_csa], oc)
+        idx, s = O.csa_select(t, qIx[r], w1[r].astype(np.float64), keys, oc)
+        sw = Hh.topk_match(gtk[r], idx, s, oc.topk)
+        print(f"  r{r}: top-{oc.topk} {'equal' if not sw else f'{sw} tie swaps'}", flush=True)
+        swaps += sw
     assert swaps <= 2
 
 

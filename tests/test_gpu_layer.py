@@ -15,21 +15,27 @@ pytestmark = pytest.mark.gpu
 # also differ where a stored index-key code flipped at a rounding boundary: one
 # E4M3 step in one of 128 key dims moves a score by ~1e-3 of its size at most.
 E2E_BAND = 2e-3
+# MXFP4 keys: one E2M1 step is up to a quarter of the block's largest value,
+# so a flipped code moves its key's score by up to ~10% (such flips need a
+# pre-rounding value within ~1e-7 of a boundary: in practice none occur).
+E2E_BAND_MX = 0.1
 
 
-def _check_topk_e2e(got, ref, scores, k):
+def _check_topk_e2e(got, ref, scores, k, band=E2E_BAND):
     """Returns positions whose lists differ (each difference within the band)."""
-    return Hh.topk_match(got, ref, scores, k, band_rel=E2E_BAND)
+    return Hh.topk_match(got, ref, scores, k, band_rel=band)
 
 
-def test_tiny_layer_prefill_then_decode():
+@pytest.mark.parametrize("idx_store", [B.DSV4_STORE_FP8, B.DSV4_STORE_MXFP4], ids=["fp8", "mxfp4"])
+def test_tiny_layer_prefill_then_decode(idx_store):
     """Tiny CSA layer (hidden 256, 8 heads of 64, RoPE 16, window 16, indexer
     4x32, top-32): prefill of 1024 tokens then 16 decode steps, inputs projected
-    from seeded hidden states, FP8/BF16 storage."""
+    from seeded hidden states, FP8/BF16 storage, index rows FP8 or MXFP4."""
     w = synth.TINY_CSA
     act = B.DSV4_DT_F32
     shape = w.shape()
-    cfg, oc = Hh.cfgs(shape, act=act)
+    cfg, oc = Hh.cfgs(shape, act=act, idx_store=idx_store)
+    band = E2E_BAND_MX if idx_store == B.DSV4_STORE_MXFP4 else E2E_BAND
     P = synth.tiny_hidden(w, steps=16)
     T0, T = w.ctx[0], w.ctx[0] + 16
     x = P["x"].astype(np.float64)
@@ -75,7 +81,7 @@ def test_tiny_layer_prefill_then_decode():
     for t in range(T):
         o, idx, s = O.csa_query(t, q[t], qI[t], wt[t].astype(np.float64), sinks, ents, keys, lambda u: wrec[u],
                                 oc, return_scores=True)
-        d = _check_topk_e2e(got_tk[t], idx, s, w.topk)
+        d = _check_topk_e2e(got_tk[t], idx, s, w.topk, band)
         differing += d > 0
         if d == 0:
             errs.append(Hh.rel_err_per_head(got_out[t], o).max())
@@ -85,15 +91,17 @@ def test_tiny_layer_prefill_then_decode():
     assert np.median(errs) <= 5e-3, np.median(errs)
 
 
-@pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
-def test_prefill_chunk_on_prefix(kind):
+@pytest.mark.parametrize("kind,idx_store", [(B.DSV4_CSA, B.DSV4_STORE_FP8), (B.DSV4_HCA, B.DSV4_STORE_FP8),
+                                            (B.DSV4_CSA, B.DSV4_STORE_MXFP4)], ids=["csa", "hca", "csa-mxfp4"])
+def test_prefill_chunk_on_prefix(kind, idx_store):
     """Production shape: a 2048-token prefix (entries written directly, raw tail
     in the state cache) plus a 300-token chunk: compressor, indexer, top-k and
     attention in prefill, checked at sampled queries, then one decode step that
     must see the chunk's state."""
     k = 512
     act = B.DSV4_DT_BF16
-    cfg, oc = Hh.cfgs(synth.CSA_PREFILL_8K.shape(), act=act, topk=k)
+    cfg, oc = Hh.cfgs(synth.CSA_PREFILL_8K.shape(), act=act, topk=k, idx_store=idx_store)
+    band = E2E_BAND_MX if idx_store == B.DSV4_STORE_MXFP4 else E2E_BAND
     csa = kind == B.DSV4_CSA
     kname = "csa" if csa else "hca"
     m = oc.m_csa if csa else oc.m_hca
@@ -158,7 +166,7 @@ def test_prefill_chunk_on_prefix(kind):
         if csa:
             o, idx, s = O.csa_query(t, qx[i], qIx[i], wq[i].astype(np.float64), sinks, ents, keys, window_of, oc,
                                     return_scores=True)
-            d = _check_topk_e2e(gtk[i], idx, s, k)
+            d = _check_topk_e2e(gtk[i], idx, s, k, band)
             diffs += d > 0
             if d:
                 continue
