@@ -33,8 +33,11 @@ FLAGS = [
 # Per-file code-generation options.  Attention: MFMA accumulators in
 # ordinary VGPRs (the online-softmax rescale is VALU work on them; with the
 # accumulators in AGPRs the compiler copies all of them back and forth on
-# every chunk).
-FILE_FLAGS = {"k_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# every chunk).  Indexer: the scores leave the MFMA straight into the VALU
+# epilogue (ReLU, head weights), which would otherwise copy every result out
+# of an AGPR first.
+FILE_FLAGS = {"k_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

@@ -73,6 +73,14 @@ __device__ __forceinline__ float group_sum4(float v) {
     return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
+// The weighted ReLU term of a head: w * max(0, x) + acc in one rounding (fma).
+// max(0, x) is taken on the bits (integer max with 0: a negative float is a
+// negative integer), one instruction where a float max would also canonicalise
+// its operand.
+__device__ __forceinline__ float relu_fma(float x, float w, float acc) {
+    return __builtin_fmaf(__int_as_float(max(__float_as_int(x), 0)), w, acc);
+}
+
 // Order-preserving key of a score: larger score -> larger key; -0 == +0; NaN
 // below everything.
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
         for (int hb = 0; hb < HB; ++hb) {
             const f32x4 w4 = wls[hb * 4 + g];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part = part + fmaxf(acc[hb][i], 0.0f) * w4[i];
+            for (int i = 0; i < 4; ++i) part = relu_fma(acc[hb][i], w4[i], part);
         }
         part = group_sum4(part);
         if (g == 0 && kb + c16 < N) {
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     for (int hb = 0; hb < HB; ++hb) {
                         const f32x4 w4 = wls[wr0 + i0 + ii][hb * 4 + g];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) part[ii] = part[ii] + fmaxf(acc[ii][hb][j], 0.0f) * w4[j];
+                        for (int j = 0; j < 4; ++j) part[ii] = relu_fma(acc[ii][hb][j], w4[j], part[ii]);
                     }
                 }
 #pragma unroll
