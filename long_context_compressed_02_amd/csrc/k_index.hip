@@ -163,19 +163,25 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     // the block ids of this wave's key range, one per lane, read once up front
     // (a per-sub-block lookup would make every group of key loads wait for
     // the previous one: loads complete in order)
-    const int blk0 = (k0 * L.m) / kBlockTokens;
+    // key index -> cache block and slot: the stride m and the entries per block
+    // 128/m are powers of two, so these are shifts and masks of non-negative
+    // values (scalar work per sub-block, shared by the compute unit's waves)
+    const uint32_t lgb = (uint32_t)__builtin_ctz((uint32_t)L.epb);   // key k is in block k >> lgb
+    const uint32_t slot_mask = (uint32_t)L.epb - 1u;
+    const int blk0 = (int)((uint32_t)k0 >> lgb);
     const int btv = blk0 + lane < C.max_blocks ? btr[blk0 + lane] : -1;
     // B operands: 16-key sub-blocks, each inside one 128-token cache block
     // (lane = key c16).  An unmapped block reads block 0 and is masked by its
     // zero scale.
     auto load_sb = [&](int kb, i32x8 &Bk, float &sk, uint32_t &sb) {
         const int kc = kb < N ? kb : k0;                       // stay in mapped memory past the end
-        const int bi = (kc * L.m) / kBlockTokens - blk0;       // wave-uniform
+        const int blk = (int)((uint32_t)kc >> lgb);
+        const int bi = blk - blk0;                             // wave-uniform
         const int bid = bi < 64 ? __builtin_amdgcn_readlane(btv, bi)   // (ranges of 64+ blocks: strides >= 32)
-                                : __builtin_amdgcn_readfirstlane(btr[(kc * L.m) / kBlockTokens]);
+                                : __builtin_amdgcn_readfirstlane(btr[blk]);
         const bool okb = bid >= 0 && bid < C.n_blocks && kb < N;
         const uint8_t *base = pool + (int64_t)(okb ? bid : 0) * L.index_block_bytes;
-        const int slot0 = kc % L.epb;
+        const int slot0 = (int)((uint32_t)kc & slot_mask);
         const uint8_t *p = base + slot0 * L.key_bytes + lane_off;
         if constexpr (F4) {
             // block g of the key: 16 bytes (zero when the key has no block g)
