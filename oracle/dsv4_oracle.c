@@ -333,3 +333,38 @@ ORC_API void orc_attend(const double *q, const double *sinks, int H, int d, doub
         free(lg);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Grouped output projection.  [R] section on depth compensation: the 128   */
+/* heads' outputs (128 x 512 = 65536 dims) are not projected to the model   */
+/* width in one matrix; the heads are split into 16 groups, each group's    */
+/* output is first condensed into a short group summary, and the 16         */
+/* summaries are projected to the model width.  Reading: two linear maps,   */
+/*   y[g] = W1[g] . o[g]   (o[g]: the group's heads concatenated, gd dims;  */
+/*                          y[g]: r dims), stored as bf16 (the operand of   */
+/*                          the second product),                           */
+/*   out  = W2 . concat_g y[g]   (hidden dims).                             */
+/* Sums in fp64; y rounded to bf16 through fp32, the precision in which the  */
+/* kernels take the same rounding decision.                                  */
+/* ------------------------------------------------------------------------ */
+ORC_API void orc_out_proj(const double *o, long T, int G, int gd, int r, const double *w1,
+                          const double *w2, int hidden, double *y_out, double *out) {
+#pragma omp parallel for schedule(dynamic)
+    for (long t = 0; t < T; ++t) {
+        double *y = y_out + t * (long)G * r;
+        for (int g = 0; g < G; ++g)
+            for (int j = 0; j < r; ++j) {
+                const double *w = w1 + ((long)g * r + j) * gd;
+                const double *x = o + t * (long)G * gd + (long)g * gd;
+                double acc = 0.0;
+                for (int i = 0; i < gd; ++i) acc += w[i] * x[i];
+                y[(long)g * r + j] = (double)orc_bf16_round((float)acc);
+            }
+        for (int n = 0; n < hidden; ++n) {
+            const double *w = w2 + (long)n * G * r;
+            double acc = 0.0;
+            for (int k = 0; k < G * r; ++k) acc += w[k] * y[k];
+            out[t * (long)hidden + n] = acc;
+        }
+    }
+}

@@ -75,6 +75,8 @@ def lib():
         L.orc_topk.argtypes = [dp, ctypes.c_long, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)]
         L.orc_attend.argtypes = [dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_double, dp,
                                  ctypes.c_long, dp, dp]
+        L.orc_out_proj.argtypes = [dp, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp,
+                                   ctypes.c_int, dp, dp]
         _lib = L
     return _lib
 
@@ -214,6 +216,25 @@ def attend(q_rot, sinks, recs, tau: float, return_sink_mass: bool = False):
     sm = np.empty(H, dtype=np.float64)
     lib().orc_attend(_dp(q), _dp(z), H, d, tau, _dp(r), r.shape[0], _dp(out), _dp(sm))
     return (out, sm) if return_sink_mass else out
+
+
+def out_proj(o, w1, w2):
+    """Grouped output projection (rqlyzj.com article, section on depth
+    compensation): o [T, G*gd] (each row the heads' outputs, group-major),
+    w1 [G, r, gd], w2 [hidden, G*r].  Returns (y [T, G*r] rounded to bf16,
+    out [T, hidden])."""
+    w1 = _f64(w1)
+    G, r, gd = w1.shape
+    w2 = _f64(w2)
+    hidden = w2.shape[0]
+    assert w2.shape[1] == G * r
+    o = _f64(o).reshape(-1, G * gd)
+    T = o.shape[0]
+    y = np.empty((T, G * r), dtype=np.float64)
+    out = np.empty((T, hidden), dtype=np.float64)
+    if T:
+        lib().orc_out_proj(_dp(o), T, G, gd, r, _dp(w1), _dp(w2), hidden, _dp(y), _dp(out))
+    return y, out
 
 
 # ---------------------------------------------------------------------------

@@ -422,3 +422,59 @@ def test_window_membership():
     assert list(O.window_tokens(0, cfg)) == [0]
     assert list(O.window_tokens(127, cfg)) == list(range(128))
     assert list(O.window_tokens(1000, cfg)) == list(range(873, 1001))
+
+
+# ----------------------------------------------------------------- grouped output projection
+def _int_case(T, G, gd, r, hidden, seed):
+    """Small-integer inputs: every fp64 sum is exact, so any order agrees."""
+    g = np.random.default_rng(seed)
+    o = g.integers(-8, 9, (T, G * gd)).astype(np.float64)
+    w1 = g.integers(-8, 9, (G, r, gd)).astype(np.float64)
+    w2 = g.integers(-4, 5, (hidden, G * r)).astype(np.float64)
+    return o, w1, w2
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(torch.float32).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def test_out_proj_is_block_diagonal_product():
+    """The grouped form equals one product with the block-diagonal matrix of
+    the groups' maps, the summary rounded to bf16 (torch's rounding)."""
+    o, w1, w2 = _int_case(7, 4, 24, 16, 40, 1)
+    G, r, gd = w1.shape
+    bd = np.zeros((G * r, G * gd))
+    for k in range(G):
+        bd[k * r:(k + 1) * r, k * gd:(k + 1) * gd] = w1[k]
+    y_ref = _bf16(o @ bd.T)
+    y, out = O.out_proj(o, w1, w2)
+    assert np.array_equal(y, y_ref)
+    assert np.array_equal(out, y_ref @ w2.T)
+    # the rounding matters here: the summaries exceed bf16's 8-bit significand
+    assert not np.array_equal(y, o @ bd.T)
+
+
+def test_out_proj_special_cases():
+    # one group: two plain products
+    o, w1, w2 = _int_case(5, 1, 32, 8, 12, 2)
+    y, out = O.out_proj(o, w1, w2)
+    assert np.array_equal(out, _bf16(o @ w1[0].T) @ w2.T)
+    # identity group maps: the summary is the input itself (exact in bf16)
+    o, _, w2 = _int_case(3, 3, 16, 16, 10, 3)
+    eye = np.broadcast_to(np.eye(16), (3, 16, 16)).copy()
+    y, out = O.out_proj(o, eye, w2)
+    assert np.array_equal(y, o) and np.array_equal(out, o @ w2.T)
+    # relabelling the groups (heads, group maps and the columns of W2 alike)
+    # leaves the output unchanged
+    o, w1, w2 = _int_case(6, 4, 8, 4, 9, 4)
+    perm = [2, 0, 3, 1]
+    o_p = o.reshape(6, 4, 8)[:, perm].reshape(6, 32)
+    w2_p = w2.reshape(9, 4, 4)[:, perm].reshape(9, 16)
+    assert np.array_equal(O.out_proj(o_p, w1[perm], w2_p)[1], O.out_proj(o, w1, w2)[1])
+    # zero rows stay zero; scaling W2 scales the output
+    o[2] = 0.0
+    _, out = O.out_proj(o, w1, w2)
+    assert (out[2] == 0).all()
+    assert np.array_equal(O.out_proj(o, w1, 2.0 * w2)[1], 2.0 * out)
+
