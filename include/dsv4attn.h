@@ -318,6 +318,26 @@ dsv4_status dsv4_hca_attend_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
                                     void *stream);
 
 /*
+ * Grouped output projection of the attention output (rqlyzj.com article,
+ * section on depth compensation: the heads are split into groups, each
+ * group's output is condensed into a short group summary, and the summaries
+ * are projected to the model width).  With G = groups, gd = (n_heads/G)*d:
+ *   y[t][g][j] = sum_i W1[g][j][i] * o[t][g*gd + i]        (j < rank), rounded to bf16
+ *   out[t][n]  = sum_k W2[n][k] * y[t][k]                    (k < G*rank, n < hidden)
+ * Each output element is reduced by one wave in a fixed order (k ascending in
+ * steps of 32), so a token's result is bitwise independent of T and of the
+ * other rows (no split-K).
+ *   o     [T][n_heads][d] bf16 (the attention output; cfg->act_dtype must be BF16)
+ *   w1    [G][rank][gd] bf16;  w2 [hidden][G*rank] bf16
+ *   y_ws  [T][G*rank] bf16 caller-owned workspace (receives the summaries)
+ *   out   [T][hidden] bf16
+ * n_heads % G == 0, gd % 32 == 0, rank and hidden multiples of 128.
+ * DSV4_ERR_UNSUPPORTED for an fp32 act dtype.
+ */
+dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *o,
+                          const void *w1, const void *w2, void *y_ws, void *out, int32_t T, void *stream);
+
+/*
  * Cache fill (benchmarks, tests, reloading a saved prefix).  Writes n entries
  * (target DSV4_TARGET_ENTRY: a KV record, RoPE at the entry's block-end
  * position m*j+m-1 then stored; DSV4_TARGET_INDEX_KEY: a CSA index key,
@@ -346,7 +366,8 @@ dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache
 #define DSV4_K_INDEX_SCORE 1
 #define DSV4_K_TOPK 2
 #define DSV4_K_ATTEND 3
-#define DSV4_K_COUNT 4
+#define DSV4_K_PROJ 4
+#define DSV4_K_COUNT 5
 dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on);
 dsv4_status dsv4_timer_read(int32_t kernel_id, int32_t reset, double *total_ms, int64_t *count);
 

@@ -25,14 +25,14 @@ DSV4_DT_F32, DSV4_DT_BF16 = 0, 1
 DSV4_POLICY_AUTO, DSV4_POLICY_HI, DSV4_POLICY_LO = 0, 1, 2
 DSV4_TARGET_ENTRY, DSV4_TARGET_INDEX_KEY = 0, 1
 DSV4_BLOCK_TOKENS = 128
-DSV4_K_COMPRESS, DSV4_K_INDEX_SCORE, DSV4_K_TOPK, DSV4_K_ATTEND, DSV4_K_COUNT = range(5)
+DSV4_K_COMPRESS, DSV4_K_INDEX_SCORE, DSV4_K_TOPK, DSV4_K_ATTEND, DSV4_K_PROJ, DSV4_K_COUNT = range(6)
 
 EXPORTS = [
     "dsv4_status_string", "dsv4_get_layout", "dsv4_workspace_bytes", "dsv4_compress_kv_decode",
     "dsv4_compress_kv_prefill", "dsv4_index_topk_decode", "dsv4_index_topk_prefill",
     "dsv4_csa_attend_decode", "dsv4_hca_attend_decode", "dsv4_csa_attend_prefill",
     "dsv4_hca_attend_prefill", "dsv4_cache_write_entries", "dsv4_state_write_tokens",
-    "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows",
+    "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
 ]
 
 
@@ -90,6 +90,7 @@ def lib():
             "dsv4_state_write_tokens": [cp, kp, i32, i32, i32, vp, vp, vp, vp, vp],
             "dsv4_topk_rows_ws_bytes": [i32, i32, i32, ctypes.POINTER(i64)],
             "dsv4_topk_rows": [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp],
+            "dsv4_out_proj": [cp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp],
             "dsv4_timer_enable": [i32, i32],
             "dsv4_timer_read": [i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         }
@@ -242,6 +243,13 @@ def dsv4_topk_rows(scores, n, max_n: int, k: int, out, ws, stream=None):
     _ck("dsv4_topk_rows", lib().dsv4_topk_rows(
         _p(scores), scores.stride(0), _p(n), n.shape[0], max_n, k, _p(out), _p(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def dsv4_out_proj(cfg, groups: int, rank: int, hidden: int, o, w1, w2, y_ws, out, stream=None):
+    """o: bf16 [T, n_heads, d]; w1: bf16 [groups, rank, n_heads/groups*d]; w2: bf16 [hidden, groups*rank];
+    y_ws: bf16 [T, groups*rank]; out: bf16 [T, hidden]."""
+    _ck("dsv4_out_proj", lib().dsv4_out_proj(ctypes.byref(cfg), groups, rank, hidden, _p(o), _p(w1), _p(w2),
+                                             _p(y_ws), _p(out), o.shape[0], _stream(stream)))
 
 
 def dsv4_timer_enable(kernel_id: int, on: bool = True):

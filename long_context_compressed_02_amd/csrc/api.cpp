@@ -447,6 +447,27 @@ dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache
     return hip_status(launch_state_tokens(L, *cache, req, pos0, n, kv, gate, kI, gI, S(stream)));
 }
 
+dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *o,
+                          const void *w1, const void *w2, void *y_ws, void *out, int32_t T, void *stream) {
+    if (!cfg) return DSV4_ERR_INVALID_ARG;
+    const int H = cfg->n_heads, d = cfg->d;
+    if (H < 1 || d < 1 || groups < 1 || H % groups) return DSV4_ERR_INVALID_ARG;
+    const int64_t gd = (int64_t)(H / groups) * d;
+    if (gd % 32 || gd > (1 << 24)) return DSV4_ERR_INVALID_ARG;
+    if (rank < 128 || rank % 128 || hidden < 128 || hidden % 128) return DSV4_ERR_INVALID_ARG;
+    if ((int64_t)groups * rank > (1 << 24)) return DSV4_ERR_INVALID_ARG;
+    if (T < 0) return DSV4_ERR_INVALID_ARG;
+    if (cfg->act_dtype != DSV4_DT_BF16) return DSV4_ERR_UNSUPPORTED;
+    if (T == 0) return DSV4_OK;
+    if (!o || !w1 || !w2 || !y_ws || !out) return DSV4_ERR_INVALID_ARG;
+    if (((uintptr_t)o | (uintptr_t)w1 | (uintptr_t)w2 | (uintptr_t)y_ws | (uintptr_t)out) & 15)
+        return DSV4_ERR_INVALID_ARG;
+    if ((T + 31) / 32 > 65535) return DSV4_ERR_UNSUPPORTED;
+    Timed tm(DSV4_K_PROJ, S(stream));
+    return hip_status(launch_out_proj((const uint16_t *)o, T, H, d, groups, rank, hidden, (const uint16_t *)w1,
+                                      (const uint16_t *)w2, (uint16_t *)y_ws, out, 0, S(stream)));
+}
+
 dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on) {
     if (kernel_id < 0 || kernel_id >= DSV4_K_COUNT) return DSV4_ERR_INVALID_ARG;
     g_timers[kernel_id].on = on != 0;

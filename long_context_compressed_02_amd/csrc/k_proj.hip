@@ -1,0 +1,155 @@
+// k_proj.hip -- the grouped output projection for gfx950.
+//
+// What is computed (rqlyzj.com article, section on depth compensation: the
+// 128 heads' outputs are not projected to the model width in one matrix; the
+// heads form 16 groups, each group's output is first condensed into a short
+// group summary, and the 16 summaries are projected to the model width):
+//     y[t][g] = W1[g] . o[t][g]         o[t][g]: the group's heads, gd = (H/G)*d dims
+//                                        y[t][g]: r dims, stored as bf16
+//     out[t]  = W2 . concat_g y[t][g]   hidden dims
+// Both products are C[z][m][n] = sum_k A[z][m][k] * B[z][n][k] with A the
+// activations (rows = tokens, k contiguous) and B the weights (rows = outputs,
+// k contiguous), on v_mfma_f32_16x16x32_bf16.
+//
+// Batch invariance (m.youleyou.com article, "what was sacrificed": no split-K):
+// every output element is reduced by one wave, k in steps of 32 in increasing
+// order, with the same MFMA instruction whatever the tile; the tiling differs
+// only in how many rows / columns a wave and a workgroup own.  So a token's
+// output is bitwise the same whether it is one row of a decode batch or of a
+// prefill chunk.
+//
+// The operands go straight from memory into MFMA registers: lane (g, c16) of
+// a 16x16x32 step reads 16 bytes -- k = 8g .. 8g+7 of row c16 -- of A and of B.
+// A D-deep ring of such loads per wave keeps enough bytes in flight: the decode
+// shape (a few dozen tokens) streams the weights once and is bound by HBM; the
+// prefill shape reuses each loaded operand across a 64x64 wave tile.
+#include "launch.h"
+
+namespace dsv4 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmArgs {
+    const uint16_t *A;      // [z][M][lda] bf16
+    const uint16_t *B;      // [z][N][ldb] bf16
+    void *C;                // [z][M][ldc] bf16 or fp32
+    int64_t lda, ldb, ldc;  // row strides (elements)
+    int64_t sA, sB, sC;     // batch strides (elements)
+    int M, N, K;
+    int c_f32;              // C in fp32 (else bf16, round to nearest even)
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    union { u32x4 u; bf16x8 b; } x;
+    x.u = v;
+    return x.b;
+}
+
+// WM x WN 16x16 blocks per wave, WGM x WGN waves per workgroup (4 in all), D
+// k-steps of loads in flight.
+template <int WM, int WN, int WGM, int WGN, int D>
+__global__ __launch_bounds__(256) void k_gemm_nt(GemmArgs G) {
+    static_assert(WGM * WGN == 4, "four waves");
+    const int z = blockIdx.z;
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int m0 = blockIdx.y * (WGM * WM * 16) + wm * WM * 16;
+    const int n0 = blockIdx.x * (WGN * WN * 16) + wn * WN * 16;
+    const uint16_t *A = G.A + (int64_t)z * G.sA;
+    const uint16_t *B = G.B + (int64_t)z * G.sB;
+    // row pointers at k = 8g: rows past M read row M-1 (their results are not stored)
+    const uint16_t *ap[WM];
+    const uint16_t *bp[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+        const int row = m0 + 16 * i + c16;
+        ap[i] = A + (int64_t)(row < G.M ? row : G.M - 1) * G.lda + 8 * g;
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) bp[j] = B + (int64_t)(n0 + 16 * j + c16) * G.ldb + 8 * g;
+    f32x4 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int nk = G.K / 32;                             // k-steps (K is a multiple of 32)
+    u32x4 ra[D][WM], rb[D][WN];
+    // step s's loads; steps past the end re-read the last step (never used), so
+    // every ring slot is refilled on every path and the counter waits stay exact
+    auto load = [&](int slot, int s) {
+        const int kk = 32 * (s < nk ? s : nk - 1);
+#pragma unroll
+        for (int i = 0; i < WM; ++i) ra[slot][i] = *(const u32x4 *)(ap[i] + kk);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) rb[slot][j] = *(const u32x4 *)(bp[j] + kk);
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+#pragma unroll 1
+    for (int s0 = 0; s0 < nk; s0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (s0 + d < nk) {                           // (uniform)
+#pragma unroll
+                for (int i = 0; i < WM; ++i)
+#pragma unroll
+                    for (int j = 0; j < WN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[d][i]), as_bf16x8(rb[d][j]),
+                                                                            acc[i][j], 0, 0, 0);
+            }
+            load(d, s0 + d + D);
+        }
+    }
+    // lane (g, c16) holds rows 4g+i, column c16 of each 16x16 block
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 16 * i + 4 * g + e, col = n0 + 16 * j + c16;
+                if (row >= G.M) continue;
+                const int64_t off = (int64_t)z * G.sC + (int64_t)row * G.ldc + col;
+                if (G.c_f32) ((float *)G.C)[off] = acc[i][j][e];
+                else ((uint16_t *)G.C)[off] = bf16_bits(acc[i][j][e]);
+            }
+}
+
+// Tilings.  Small batches: a wave owns one 16x16 block and keeps 8 k-steps of
+// loads in flight (the weights are streamed once; parallelism comes from the
+// columns).  Large batches: a wave owns 64x64, a workgroup 128x128.
+constexpr int kProjSmallRows = 256;
+constexpr int kSmallTileM = 32, kSmallTileN = 32;
+constexpr int kLargeTileM = 128, kLargeTileN = 128;
+
+int proj_tile_n() { return kLargeTileN; }
+
+static hipError_t launch_gemm(const GemmArgs &G, int batch, hipStream_t s) {
+    if (G.M <= kProjSmallRows) {
+        dim3 grid((unsigned)(G.N / kSmallTileN), (unsigned)((G.M + kSmallTileM - 1) / kSmallTileM), (unsigned)batch);
+        hipLaunchKernelGGL((k_gemm_nt<1, 1, 2, 2, 8>), grid, dim3(256), 0, s, G);
+    } else {
+        dim3 grid((unsigned)(G.N / kLargeTileN), (unsigned)((G.M + kLargeTileM - 1) / kLargeTileM), (unsigned)batch);
+        hipLaunchKernelGGL((k_gemm_nt<4, 4, 2, 2, 2>), grid, dim3(256), 0, s, G);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_out_proj(const uint16_t *o, int T, int H, int d, int groups, int rank, int hidden,
+                           const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *out, int out_f32,
+                           hipStream_t s) {
+    const int gd = H / groups * d;
+    GemmArgs g1{o, w1, y, (int64_t)H * d, gd, (int64_t)groups * rank, gd, (int64_t)rank * gd, rank,
+                T, rank, gd, 0};
+    hipError_t e = launch_gemm(g1, groups, s);
+    if (e != hipSuccess) return e;
+    GemmArgs g2{y, w2, out, (int64_t)groups * rank, (int64_t)groups * rank, hidden, 0, 0, 0,
+                T, hidden, groups * rank, out_f32};
+    return launch_gemm(g2, 1, s);
+}
+
+}  // namespace dsv4

@@ -92,4 +92,9 @@ int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa);
 int64_t attend_lds_max(const Lay &L, int64_t list_max);
 constexpr int64_t kLdsMax = 160 * 1024;   // LDS of one gfx950 workgroup
 
+// Grouped output projection (two batch-invariant bf16 products).
+hipError_t launch_out_proj(const uint16_t *o, int T, int H, int d, int groups, int rank, int hidden,
+                           const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *out, int out_f32,
+                           hipStream_t s);
+
 }  // namespace dsv4
