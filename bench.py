@@ -28,6 +28,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 METRIC = "CSA/HCA decode queries/s at 128K–1M ctx; % HBM BW and % MFMA peak"
 
 
@@ -39,13 +40,19 @@ def parse():
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--ctx", type=int, default=131072)
     ap.add_argument("--policy", default="auto", choices=["auto", "hi", "lo"])
+    ap.add_argument("--idx-store", default="fp8", choices=["fp8", "mxfp4"],
+                    help="indexer query / key rows: E4M3 with one scale per row (fp8), or MXFP4 (E2M1 with a "
+                         "power-of-two scale per 32 dims); decode and prefill workloads")
     ap.add_argument("--cpu-sample", type=int, default=8, help="queries timed on the CPU oracle (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (traffic calibration under --pmc)")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "hca_decode", "pair_1m"],
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "hca_decode", "pair_1m", "out_proj"],
                     help="decode: the CSA+HCA decode step, batch 32 at 128K (the headline); prefill: one "
                          "8192-token CSA chunk on a 256K-token prefix; hca_decode: the HCA decode step, batch 16 at "
-                         "64K; pair_1m: the CSA+HCA decode step for 4 requests at 1M/512K/64K/4K")
+                         "64K; pair_1m: the CSA+HCA decode step for 4 requests at 1M/512K/64K/4K; out_proj: the "
+                         "grouped output projection (128 heads x 512 -> 16 groups of rank 1024 -> 7168) of --batch "
+                         "tokens")
     return ap.parse_args()
 
 
@@ -58,6 +65,8 @@ def main():
         return prefill_main(a)
     if a.workload in ("hca_decode", "pair_1m"):
         return decode_mix_main(a)
+    if a.workload == "out_proj":
+        return out_proj_main(a)
     import torch
     from long_context_compressed_02_amd import binding as B
     from long_context_compressed_02_amd import synth
@@ -68,7 +77,8 @@ def main():
     Bsz, ctx = a.batch, a.ctx
     steps, warm = a.steps, a.warmup
     total_new = steps + warm
-    cfg = B.make_cfg(**w.shape())
+    mx = a.idx_store == "mxfp4"
+    cfg = B.make_cfg(idx_store=B.DSV4_STORE_MXFP4 if mx else B.DSV4_STORE_FP8, **w.shape())
     policy = {"auto": B.DSV4_POLICY_AUTO, "hi": B.DSV4_POLICY_HI, "lo": B.DSV4_POLICY_LO}[a.policy]
     H, d, HI_, dI, k = w.n_heads, w.d, w.idx_heads, w.idx_dim, w.topk
 
@@ -169,8 +179,8 @@ def main():
     # algorithmic work per step (positions ctx+s, averaged over the timed steps)
     n_vis = np.mean([(ctx + s + 1) // 4 for s in range(warm, total_new)])
     n_h = np.mean([(ctx + s + 1) // 128 for s in range(warm, total_new)])
-    key_b = dI + 4                                      # E4M3 key + fp32 scale
-    score_bytes = Bsz * n_vis * (key_b + 4) + Bsz * HI_ * (dI + 4)       # keys+scales read, scores written, queries
+    row_b = (dI // 2 if mx else dI) + 4                 # E2M1 codes + 4 E8M0 bytes, or E4M3 codes + fp32 scale
+    score_bytes = Bsz * n_vis * (row_b + 4) + Bsz * HI_ * row_b       # keys+scales read, scores written, queries
     score_flops = Bsz * n_vis * HI_ * dI * 2
     rec_b = (d - 64) + 2 * 64 + 4                        # 580 B per stored record
     csa_recs = Bsz * (k + 128)
@@ -197,16 +207,17 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if a.cpu_sample > 0:
-        cpu = cpu_baseline(w, a.cpu_sample, ctx + warm)
+        cpu = cpu_baseline(w, a.cpu_sample, ctx + warm, idx_mode=2 if mx else 1)
 
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8/bf16", "data": "synthetic",
+        "dtype": "mxfp4/fp8/bf16" if mx else "fp8/bf16", "data": "synthetic",
         "config": {"workload": f"V4-Pro CSA+HCA layer-pair decode, batch {Bsz} x {ctx // 1024}K ctx "
                                f"({ctx // 4} CSA / {ctx // 128} HCA entries per request), top-{k}, "
-                               f"{H} heads x d {d}, window 128",
-                   "batch": Bsz, "ctx": ctx, "topk": k, "heads": H, "d": d, "policy": a.policy},
+                               f"{H} heads x d {d}, window 128" + (", MXFP4 indexer" if mx else ""),
+                   "batch": Bsz, "ctx": ctx, "topk": k, "heads": H, "d": d, "policy": a.policy,
+                   "idx_store": a.idx_store},
         "roofline": roof,
         "cpu_baseline": cpu,
         "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items()},
@@ -230,7 +241,9 @@ def prefill_main(a):
     dev = "cuda"
     torch.cuda.set_device(0)
     w = synth.CSA_PREFILL_8K
-    cfg = B.make_cfg(**w.shape())
+    mx = a.idx_store == "mxfp4"
+    cfg = B.make_cfg(idx_store=B.DSV4_STORE_MXFP4 if mx else B.DSV4_STORE_FP8, **w.shape())
+    idx_peak = FP4_PEAK_TFLOPS if mx else FP8_PEAK_TFLOPS
     H, d, HI_, dI, k = w.n_heads, w.d, w.idx_heads, w.idx_dim, w.topk
     P, C = w.ctx[0], w.chunk
     T = P + C
@@ -305,8 +318,8 @@ def prefill_main(a):
     idx_tf = idx_flops / (idx_ms * 1e-3) / 1e12 if idx_ms > 0 else 0.0
     att_tf = att_flops / (att_ms * 1e-3) / 1e12 if att_ms > 0 else 0.0
     dom = "index_score" if kern["index_score"]["total_ms"] >= kern["attend"]["total_ms"] else "attend"
-    roof = ({"kernel": "k_index_score_decode", "bound": "mfma", "achieved": round(idx_tf, 2),
-             "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tf / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    roof = ({"kernel": "k_index_score_prefill", "bound": "mfma", "achieved": round(idx_tf, 2),
+             "peak": idx_peak, "unit": "TFLOP/s", "frac": round(idx_tf / idx_peak, 4), "traffic": None}
             if dom == "index_score" else
             {"kernel": "k_attend", "bound": "mfma", "achieved": round(att_tf, 2), "peak": BF16_PEAK_TFLOPS,
              "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4), "traffic": None})
@@ -314,13 +327,69 @@ def prefill_main(a):
         "metric": "CSA prefill tokens/s (8192-token chunk on a 262144-token prefix)",
         "value": round(C / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8/bf16", "data": "synthetic",
+        "dtype": "mxfp4/fp8/bf16" if mx else "fp8/bf16", "data": "synthetic",
         "config": {"workload": f"V4 CSA layer prefill, chunk {C} on a {P // 1024}K prefix, top-{k}, "
-                               f"{H} heads x d {d}", "chunk": C, "prefix": P, "topk": k},
+                               f"{H} heads x d {d}" + (", MXFP4 indexer" if mx else ""), "chunk": C, "prefix": P,
+                   "topk": k, "idx_store": a.idx_store},
         "roofline": roof,
         "breakdown_ms": {n_: round(v["total_ms"] / steps, 3) for n_, v in kern.items()},
         "indexer_TFLOPs": round(idx_tf, 1), "attend_TFLOPs": round(att_tf, 1),
         "setup_s": round(t_setup, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def out_proj_main(a):
+    """The grouped output projection of --batch tokens' attention outputs
+    (V4-Pro: 128 heads x 512 dims, 16 groups, group rank 1024, model width
+    7168), bf16 weights and activations generated on the device before
+    timing.  Small batches stream the 369 MB of weights once (HBM-bound);
+    large batches are MFMA-bound."""
+    import torch
+    from long_context_compressed_02_amd import binding as B
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    H, d, G, r, hidden = 128, 512, 16, 1024, 7168
+    T = a.batch
+    cfg = B.make_cfg()
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    rn = lambda *s_: torch.randn(*s_, generator=g, device=dev, dtype=torch.float32)
+    gd = H // G * d
+    o = rn(T, H, d).to(torch.bfloat16)
+    w1 = (rn(G, r, gd) / gd ** 0.5).to(torch.bfloat16)
+    w2 = (rn(hidden, G * r) / (G * r) ** 0.5).to(torch.bfloat16)
+    y = torch.empty((T, G * r), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    w1p, w2p = torch.empty_like(w1), torch.empty_like(w2)
+    B.dsv4_out_proj_pack(cfg, G, r, hidden, w1, w2, w1p, w2p, stream)     # once, before timing
+    del w1, w2
+
+    def step(_s):
+        B.dsv4_out_proj(cfg, G, r, hidden, o, w1p, w2p, y, out, stream)
+
+    ms, kern = _timed_steps(step, a.steps, a.warmup)
+    flops = 2.0 * T * (G * r * gd + hidden * G * r)
+    wbytes = 2.0 * (G * r * gd + hidden * G * r)
+    abytes = 2.0 * T * (H * d + 2 * G * r + hidden)
+    sec = ms * 1e-3
+    small = T <= 256
+    achieved = (wbytes + abytes) / sec / 1e9 if small else flops / sec / 1e12
+    peak = HBM_PEAK_GBS if small else BF16_PEAK_TFLOPS
+    roof = {"kernel": "k_gemm_nt", "bound": "hbm" if small else "mfma", "achieved": round(achieved, 2),
+            "peak": peak, "unit": "GB/s" if small else "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    res = {
+        "metric": "grouped output projection tokens/s", "value": round(T / sec, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"grouped output projection of {T} tokens: {H} heads x {d} -> {G} groups of rank "
+                               f"{r} -> {hidden}", "tokens": T, "heads": H, "d": d, "groups": G, "rank": r,
+                   "hidden": hidden},
+        "roofline": roof,
+        "TFLOPs": round(flops / sec / 1e12, 1), "GBps": round((wbytes + abytes) / sec / 1e9, 1),
+        "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items() if v["launches"]},
     }
     print(json.dumps(res), flush=True)
 
@@ -347,7 +416,7 @@ def _timed_steps(step, steps, warm):
         step(s)
     torch.cuda.synchronize()
     names = {B.DSV4_K_COMPRESS: "compress", B.DSV4_K_INDEX_SCORE: "index_score", B.DSV4_K_TOPK: "topk",
-             B.DSV4_K_ATTEND: "attend"}
+             B.DSV4_K_ATTEND: "attend", B.DSV4_K_PROJ: "out_proj"}
     kern = {}
     for kid, nm in names.items():
         ms, n = B.dsv4_timer_read(kid, True)
@@ -493,12 +562,12 @@ def measured_traffic():
     return int(m.group(1))
 
 
-def cpu_baseline(w, nq, t):
+def cpu_baseline(w, nq, t, idx_mode=1):
     """The oracle (as it stands) on a bounded sample: nq CSA+HCA queries of the
     same workload at position t (index keys, top-k and attention per query)."""
     from long_context_compressed_02_amd import synth
     from oracle import oracle as O
-    oc = O.OCfg(**w.shape())
+    oc = O.OCfg(idx_mode=idx_mode, **w.shape())
     n = (t + 1) // 4
     nh = (t + 1) // 128
     q, qI, wt = synth.decode_queries(w, nq, sub=777)

@@ -328,14 +328,23 @@ dsv4_status dsv4_hca_attend_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
  * steps of 32), so a token's result is bitwise independent of T and of the
  * other rows (no split-K).
  *   o     [T][n_heads][d] bf16 (the attention output; cfg->act_dtype must be BF16)
- *   w1    [G][rank][gd] bf16;  w2 [hidden][G*rank] bf16
+ *   w1p, w2p  the weights as packed by dsv4_out_proj_pack
  *   y_ws  [T][G*rank] bf16 caller-owned workspace (receives the summaries)
  *   out   [T][hidden] bf16
  * n_heads % G == 0, gd % 32 == 0, rank and hidden multiples of 128.
  * DSV4_ERR_UNSUPPORTED for an fp32 act dtype.
  */
 dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *o,
-                          const void *w1, const void *w2, void *y_ws, void *out, int32_t T, void *stream);
+                          const void *w1p, const void *w2p, void *y_ws, void *out, int32_t T, void *stream);
+
+/* Pack the projection weights once (same sizes as the inputs; caller-owned):
+ *   w1 [G][rank][gd] bf16 -> w1p,  w2 [hidden][G*rank] bf16 -> w2p.
+ * Packed order of a matrix W [N][K]: for each 16-row block n0 and each 32-wide
+ * k-step k0, 512 elements in which position 8*l + e (l < 64, e < 8) holds
+ * W[n0 + l%16][k0 + 8*(l/16) + e] -- the MFMA operand of that block and step,
+ * one contiguous kilobyte. */
+dsv4_status dsv4_out_proj_pack(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *w1,
+                               const void *w2, void *w1p, void *w2p, void *stream);
 
 /*
  * Cache fill (benchmarks, tests, reloading a saved prefix).  Writes n entries

@@ -33,6 +33,7 @@ EXPORTS = [
     "dsv4_csa_attend_decode", "dsv4_hca_attend_decode", "dsv4_csa_attend_prefill",
     "dsv4_hca_attend_prefill", "dsv4_cache_write_entries", "dsv4_state_write_tokens",
     "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
+    "dsv4_out_proj_pack",
 ]
 
 
@@ -91,6 +92,7 @@ def lib():
             "dsv4_topk_rows_ws_bytes": [i32, i32, i32, ctypes.POINTER(i64)],
             "dsv4_topk_rows": [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp],
             "dsv4_out_proj": [cp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp],
+            "dsv4_out_proj_pack": [cp, i32, i32, i32, vp, vp, vp, vp, vp],
             "dsv4_timer_enable": [i32, i32],
             "dsv4_timer_read": [i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         }
@@ -245,11 +247,17 @@ def dsv4_topk_rows(scores, n, max_n: int, k: int, out, ws, stream=None):
         _stream(stream)))
 
 
-def dsv4_out_proj(cfg, groups: int, rank: int, hidden: int, o, w1, w2, y_ws, out, stream=None):
-    """o: bf16 [T, n_heads, d]; w1: bf16 [groups, rank, n_heads/groups*d]; w2: bf16 [hidden, groups*rank];
+def dsv4_out_proj(cfg, groups: int, rank: int, hidden: int, o, w1p, w2p, y_ws, out, stream=None):
+    """o: bf16 [T, n_heads, d]; w1p, w2p: the weights packed by dsv4_out_proj_pack;
     y_ws: bf16 [T, groups*rank]; out: bf16 [T, hidden]."""
-    _ck("dsv4_out_proj", lib().dsv4_out_proj(ctypes.byref(cfg), groups, rank, hidden, _p(o), _p(w1), _p(w2),
+    _ck("dsv4_out_proj", lib().dsv4_out_proj(ctypes.byref(cfg), groups, rank, hidden, _p(o), _p(w1p), _p(w2p),
                                              _p(y_ws), _p(out), o.shape[0], _stream(stream)))
+
+
+def dsv4_out_proj_pack(cfg, groups: int, rank: int, hidden: int, w1, w2, w1p, w2p, stream=None):
+    """w1: bf16 [groups, rank, n_heads/groups*d]; w2: bf16 [hidden, groups*rank]; w1p, w2p: same sizes."""
+    _ck("dsv4_out_proj_pack", lib().dsv4_out_proj_pack(ctypes.byref(cfg), groups, rank, hidden, _p(w1), _p(w2),
+                                                       _p(w1p), _p(w2p), _stream(stream)))
 
 
 def dsv4_timer_enable(kernel_id: int, on: bool = True):

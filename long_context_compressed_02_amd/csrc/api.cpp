@@ -447,8 +447,7 @@ dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache
     return hip_status(launch_state_tokens(L, *cache, req, pos0, n, kv, gate, kI, gI, S(stream)));
 }
 
-dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *o,
-                          const void *w1, const void *w2, void *y_ws, void *out, int32_t T, void *stream) {
+static dsv4_status proj_shape(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden) {
     if (!cfg) return DSV4_ERR_INVALID_ARG;
     const int H = cfg->n_heads, d = cfg->d;
     if (H < 1 || d < 1 || groups < 1 || H % groups) return DSV4_ERR_INVALID_ARG;
@@ -456,6 +455,26 @@ dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int
     if (gd % 32 || gd > (1 << 24)) return DSV4_ERR_INVALID_ARG;
     if (rank < 128 || rank % 128 || hidden < 128 || hidden % 128) return DSV4_ERR_INVALID_ARG;
     if ((int64_t)groups * rank > (1 << 24)) return DSV4_ERR_INVALID_ARG;
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_out_proj_pack(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *w1,
+                               const void *w2, void *w1p, void *w2p, void *stream) {
+    dsv4_status st = proj_shape(cfg, groups, rank, hidden);
+    if (st != DSV4_OK) return st;
+    if (!w1 || !w2 || !w1p || !w2p) return DSV4_ERR_INVALID_ARG;
+    if (((uintptr_t)w1 | (uintptr_t)w2 | (uintptr_t)w1p | (uintptr_t)w2p) & 15) return DSV4_ERR_INVALID_ARG;
+    const int gd = cfg->n_heads / groups * cfg->d;
+    hipError_t e = launch_pack_b((const uint16_t *)w1, (uint16_t *)w1p, groups, rank, gd, S(stream));
+    if (e != hipSuccess) return DSV4_ERR_LAUNCH;
+    return hip_status(launch_pack_b((const uint16_t *)w2, (uint16_t *)w2p, 1, hidden, groups * rank, S(stream)));
+}
+
+dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden, const void *o,
+                          const void *w1, const void *w2, void *y_ws, void *out, int32_t T, void *stream) {
+    dsv4_status st = proj_shape(cfg, groups, rank, hidden);
+    if (st != DSV4_OK) return st;
+    const int H = cfg->n_heads, d = cfg->d;
     if (T < 0) return DSV4_ERR_INVALID_ARG;
     if (cfg->act_dtype != DSV4_DT_BF16) return DSV4_ERR_UNSUPPORTED;
     if (T == 0) return DSV4_OK;

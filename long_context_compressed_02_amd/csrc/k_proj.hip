@@ -20,9 +20,14 @@
 //
 // The operands go straight from memory into MFMA registers: lane (g, c16) of
 // a 16x16x32 step reads 16 bytes -- k = 8g .. 8g+7 of row c16 -- of A and of B.
-// A D-deep ring of such loads per wave keeps enough bytes in flight: the decode
-// shape (a few dozen tokens) streams the weights once and is bound by HBM; the
-// prefill shape reuses each loaded operand across a 64x64 wave tile.
+// The weights are packed once (dsv4_out_proj_pack) in exactly that order: the
+// operand of (16-row block, k-step) is one contiguous kilobyte, lane l's 16
+// bytes at 16l, so every weight load reads whole lines in sequence (read
+// straight from the row-major matrix, each load would touch 16 rows 64 bytes
+// apiece, and HBM served that pattern at a quarter of its rate).  A D-deep
+// ring of loads per wave keeps bytes in flight: the decode shape (a few dozen
+// tokens) streams the weights once and is bound by HBM; the prefill shape
+// reuses each loaded operand across a 64x64 wave tile.
 #include "launch.h"
 
 namespace dsv4 {
@@ -33,13 +38,31 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
     const uint16_t *A;      // [z][M][lda] bf16
-    const uint16_t *B;      // [z][N][ldb] bf16
+    const uint16_t *B;      // [z][N/16][K/32][64 lanes][8] bf16, packed (see k_pack_b)
     void *C;                // [z][M][ldc] bf16 or fp32
-    int64_t lda, ldb, ldc;  // row strides (elements)
+    int64_t lda, ldc;       // row strides (elements)
     int64_t sA, sB, sC;     // batch strides (elements)
     int M, N, K;
     int c_f32;              // C in fp32 (else bf16, round to nearest even)
 };
+
+// Pack W [z][N][K] (row-major, k contiguous) into the MFMA operand order:
+// tile (n/16, k/32) is 512 elements, lane (k%32/8)*16 + n%16 holds the 8
+// elements k - k%8 .. +8 of row n.  One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void k_pack_b(const uint16_t *W, uint16_t *P, int N, int K, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // piece index in the packed order
+    if (i >= total) return;
+    const int nk = K / 32;
+    const int lane = (int)(i & 63);
+    const int64_t tile = i >> 6;
+    const int s = (int)(tile % nk);
+    const int64_t zb = tile / nk;                  // z * (N/16) + column block
+    const int nb16 = N / 16;
+    const int64_t z = zb / nb16;
+    const int nb = (int)(zb % nb16);
+    const int n = 16 * nb + (lane & 15), k = 32 * s + 8 * (lane >> 4);
+    *(u32x4 *)(P + 8 * i) = *(const u32x4 *)(W + (z * N + n) * (int64_t)K + k);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     union { u32x4 u; bf16x8 b; } x;
@@ -68,24 +91,24 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmArgs G) {
         const int row = m0 + 16 * i + c16;
         ap[i] = A + (int64_t)(row < G.M ? row : G.M - 1) * G.lda + 8 * g;
     }
+    const int nk = G.K / 32;                             // k-steps (K is a multiple of 32)
 #pragma unroll
-    for (int j = 0; j < WN; ++j) bp[j] = B + (int64_t)(n0 + 16 * j + c16) * G.ldb + 8 * g;
+    for (int j = 0; j < WN; ++j) bp[j] = B + (int64_t)((n0 + 16 * j) / 16) * nk * 512 + 8 * lane;
     f32x4 acc[WM][WN];
 #pragma unroll
     for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nk = G.K / 32;                             // k-steps (K is a multiple of 32)
     u32x4 ra[D][WM], rb[D][WN];
     // step s's loads; steps past the end re-read the last step (never used), so
     // every ring slot is refilled on every path and the counter waits stay exact
     auto load = [&](int slot, int s) {
-        const int kk = 32 * (s < nk ? s : nk - 1);
+        const int sc = s < nk ? s : nk - 1;
 #pragma unroll
-        for (int i = 0; i < WM; ++i) ra[slot][i] = *(const u32x4 *)(ap[i] + kk);
+        for (int i = 0; i < WM; ++i) ra[slot][i] = *(const u32x4 *)(ap[i] + 32 * sc);
 #pragma unroll
-        for (int j = 0; j < WN; ++j) rb[slot][j] = *(const u32x4 *)(bp[j] + kk);
+        for (int j = 0; j < WN; ++j) rb[slot][j] = *(const u32x4 *)(bp[j] + (int64_t)512 * sc);
     };
 #pragma unroll
     for (int s = 0; s < D; ++s) load(s, s);
@@ -140,16 +163,21 @@ static hipError_t launch_gemm(const GemmArgs &G, int batch, hipStream_t s) {
 }
 
 hipError_t launch_out_proj(const uint16_t *o, int T, int H, int d, int groups, int rank, int hidden,
-                           const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *out, int out_f32,
+                           const uint16_t *w1p, const uint16_t *w2p, uint16_t *y, void *out, int out_f32,
                            hipStream_t s) {
     const int gd = H / groups * d;
-    GemmArgs g1{o, w1, y, (int64_t)H * d, gd, (int64_t)groups * rank, gd, (int64_t)rank * gd, rank,
+    GemmArgs g1{o, w1p, y, (int64_t)H * d, (int64_t)groups * rank, gd, (int64_t)rank * gd, rank,
                 T, rank, gd, 0};
     hipError_t e = launch_gemm(g1, groups, s);
     if (e != hipSuccess) return e;
-    GemmArgs g2{y, w2, out, (int64_t)groups * rank, (int64_t)groups * rank, hidden, 0, 0, 0,
-                T, hidden, groups * rank, out_f32};
+    GemmArgs g2{y, w2p, out, (int64_t)groups * rank, hidden, 0, 0, 0, T, hidden, groups * rank, out_f32};
     return launch_gemm(g2, 1, s);
+}
+
+hipError_t launch_pack_b(const uint16_t *W, uint16_t *P, int batch, int N, int K, hipStream_t s) {
+    const int64_t total = (int64_t)batch * N * K / 8;
+    hipLaunchKernelGGL(k_pack_b, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, W, P, N, K, total);
+    return hipGetLastError();
 }
 
 }  // namespace dsv4

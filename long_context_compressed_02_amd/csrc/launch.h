@@ -94,7 +94,8 @@ constexpr int64_t kLdsMax = 160 * 1024;   // LDS of one gfx950 workgroup
 
 // Grouped output projection (two batch-invariant bf16 products).
 hipError_t launch_out_proj(const uint16_t *o, int T, int H, int d, int groups, int rank, int hidden,
-                           const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *out, int out_f32,
+                           const uint16_t *w1p, const uint16_t *w2p, uint16_t *y, void *out, int out_f32,
                            hipStream_t s);
+hipError_t launch_pack_b(const uint16_t *W, uint16_t *P, int batch, int N, int K, hipStream_t s);
 
 }  // namespace dsv4

@@ -29,13 +29,42 @@ def _case(T, H, d, G, r, hidden, seed):
     return bf(o), bf(w1), bf(w2)
 
 
+_packed = {}
+
+
 def _run(cfg, G, r, hidden, o, w1, w2):
+    key = (w1.data_ptr(), w2.data_ptr())
+    if key not in _packed:
+        w1p, w2p = torch.empty_like(w1), torch.empty_like(w2)
+        B.dsv4_out_proj_pack(cfg, G, r, hidden, w1, w2, w1p, w2p)
+        _packed.clear()
+        _packed[key] = (w1, w2, w1p, w2p)
+    w1p, w2p = _packed[key][2:]
     T = o.shape[0]
     y = torch.empty((T, G * r), dtype=torch.bfloat16, device=DEV)
     out = torch.empty((T, hidden), dtype=torch.bfloat16, device=DEV)
-    B.dsv4_out_proj(cfg, G, r, hidden, o, w1, w2, y, out)
+    B.dsv4_out_proj(cfg, G, r, hidden, o, w1p, w2p, y, out)
     torch.cuda.synchronize()
     return y, out
+
+
+def test_out_proj_pack_layout():
+    """The packed order, element by element against the documented formula."""
+    cfg = B.make_cfg(d=64, d_rope=16, n_heads=32)
+    G, r, hidden = 4, 128, 256
+    gd = 32 // G * 64
+    w1 = torch.arange(G * r * gd, dtype=torch.int32).remainder(30011).to(torch.bfloat16).view(G, r, gd).to(DEV)
+    w2 = torch.arange(hidden * G * r, dtype=torch.int32).remainder(30011).to(torch.bfloat16).view(hidden, G * r).to(DEV)
+    w1p, w2p = torch.empty_like(w1), torch.empty_like(w2)
+    B.dsv4_out_proj_pack(cfg, G, r, hidden, w1, w2, w1p, w2p)
+    torch.cuda.synchronize()
+    for W, P in ((w2.cpu(), w2p.cpu().view(-1)), (w1[2].cpu(), w1p[2].cpu().view(-1))):
+        N, K = W.shape
+        n0, k0, l, e = np.meshgrid(np.arange(0, N, 16), np.arange(0, K, 32), np.arange(64), np.arange(8),
+                                   indexing="ij")
+        pos = ((n0 // 16) * (K // 32) + k0 // 32) * 512 + 8 * l + e
+        ref = W[torch.from_numpy((n0 + l % 16).ravel()), torch.from_numpy((k0 + 8 * (l // 16) + e).ravel())]
+        assert torch.equal(P[torch.from_numpy(pos.ravel())], ref)
 
 
 def _check(y, out, o, w1, w2, rows):
