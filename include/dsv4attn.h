@@ -357,6 +357,28 @@ dsv4_status dsv4_cache_write_entries(const dsv4_cfg *cfg, const dsv4_cache *cach
                                      const int32_t *req_dev, const int32_t *entry_dev, int32_t n,
                                      const float *values_dev, void *stream);
 
+/*
+ * Dump and reload of one request's cache (vastsailsolution.com V4 article,
+ * state-cache and classic-cache paragraph; xiaoyuzhoufm.com summary 2.1: an
+ * on-disk KV cache for requests sharing a prefix, full-cache or periodic
+ * checkpoints).  After n_tokens tokens a request's cache is its state cache
+ * plus the classic-cache blocks covering tokens [0, n_tokens).  The dump is
+ * those bytes in a fixed order, independent of the physical block ids:
+ *   [state_bytes] [entry blocks 0 .. nb-1] [index blocks 0 .. nb-1 (CSA)]
+ * with nb = ceil(n_tokens / 128); dsv4_cache_dump_bytes gives its size.  A
+ * reload writes a dump into request `req` of a cache with the same
+ * configuration through that request's block table (other block ids, another
+ * pool): decoding then continues bit for bit as it would have on the original.
+ * Blocks the table does not map are dumped as zeros and skipped on reload.
+ *   buf_dev  device memory of at least dsv4_cache_dump_bytes bytes, 16-byte aligned
+ *   (a host copy of it -- disk -- is the caller's)
+ */
+dsv4_status dsv4_cache_dump_bytes(const dsv4_cfg *cfg, int32_t kind, int32_t n_tokens, int64_t *out);
+dsv4_status dsv4_cache_dump(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t n_tokens,
+                            void *buf_dev, int64_t buf_bytes, void *stream);
+dsv4_status dsv4_cache_load(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t n_tokens,
+                            const void *buf_dev, int64_t buf_bytes, void *stream);
+
 /* Write raw tokens [pos0, pos0+n) of request `req` into its state cache (window
  * ring and pending ring; only the last W resp. pending_slots tokens land), as
  * the appends would have, without forming entries.  kv, gate [n][d] and

@@ -33,7 +33,7 @@ EXPORTS = [
     "dsv4_csa_attend_decode", "dsv4_hca_attend_decode", "dsv4_csa_attend_prefill",
     "dsv4_hca_attend_prefill", "dsv4_cache_write_entries", "dsv4_state_write_tokens",
     "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
-    "dsv4_out_proj_pack",
+    "dsv4_out_proj_pack", "dsv4_cache_dump_bytes", "dsv4_cache_dump", "dsv4_cache_load",
 ]
 
 
@@ -93,6 +93,9 @@ def lib():
             "dsv4_topk_rows": [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp],
             "dsv4_out_proj": [cp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp],
             "dsv4_out_proj_pack": [cp, i32, i32, i32, vp, vp, vp, vp, vp],
+            "dsv4_cache_dump_bytes": [cp, i32, i32, ctypes.POINTER(i64)],
+            "dsv4_cache_dump": [cp, kp, i32, i32, vp, i64, vp],
+            "dsv4_cache_load": [cp, kp, i32, i32, vp, i64, vp],
             "dsv4_timer_enable": [i32, i32],
             "dsv4_timer_read": [i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         }
@@ -232,6 +235,23 @@ def dsv4_state_write_tokens(cfg, cache: LayerCache, req: int, pos0: int, kv, gat
     _ck("dsv4_state_write_tokens", lib().dsv4_state_write_tokens(
         ctypes.byref(cfg), ctypes.byref(cache.c), req, pos0, kv.shape[0], _p(kv), _p(gate), _p(kI), _p(gI),
         _stream(stream)))
+
+
+def dsv4_cache_dump_bytes(cfg, kind: int, n_tokens: int) -> int:
+    out = ctypes.c_int64()
+    _ck("dsv4_cache_dump_bytes", lib().dsv4_cache_dump_bytes(ctypes.byref(cfg), kind, n_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def dsv4_cache_dump(cfg, cache: LayerCache, req: int, n_tokens: int, buf, stream=None):
+    """buf: uint8 device tensor of at least dsv4_cache_dump_bytes bytes."""
+    _ck("dsv4_cache_dump", lib().dsv4_cache_dump(ctypes.byref(cfg), ctypes.byref(cache.c), req, n_tokens, _p(buf),
+                                                 buf.numel() * buf.element_size(), _stream(stream)))
+
+
+def dsv4_cache_load(cfg, cache: LayerCache, req: int, n_tokens: int, buf, stream=None):
+    _ck("dsv4_cache_load", lib().dsv4_cache_load(ctypes.byref(cfg), ctypes.byref(cache.c), req, n_tokens, _p(buf),
+                                                 buf.numel() * buf.element_size(), _stream(stream)))
 
 
 def dsv4_topk_rows_ws_bytes(n_rows: int, max_n: int, k: int) -> int:

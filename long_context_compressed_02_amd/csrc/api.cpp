@@ -447,6 +447,39 @@ dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache
     return hip_status(launch_state_tokens(L, *cache, req, pos0, n, kv, gate, kI, gI, S(stream)));
 }
 
+dsv4_status dsv4_cache_dump_bytes(const dsv4_cfg *cfg, int32_t kind, int32_t n_tokens, int64_t *out) {
+    if (!out || n_tokens < 1) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, kind, &L);
+    if (st != DSV4_OK) return st;
+    *out = cache_dump_bytes(L, (n_tokens + kBlockTokens - 1) / kBlockTokens);
+    return DSV4_OK;
+}
+
+static dsv4_status cache_xfer(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t n_tokens,
+                              const void *buf, int64_t buf_bytes, bool to_buf, void *stream) {
+    if (!cache) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, cache->kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, cache->kind)) != DSV4_OK) return st;
+    if (req < 0 || req >= cache->n_req || n_tokens < 1) return DSV4_ERR_INVALID_ARG;
+    const int nb = (n_tokens + kBlockTokens - 1) / kBlockTokens;
+    if (nb > cache->max_blocks) return DSV4_ERR_INVALID_ARG;
+    if (!buf || ((uintptr_t)buf & 15) || buf_bytes < cache_dump_bytes(L, nb)) return DSV4_ERR_INVALID_ARG;
+    return hip_status(launch_cache_xfer(L, *cache, req, nb, (uint8_t *)buf, to_buf, S(stream)));
+}
+
+dsv4_status dsv4_cache_dump(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t n_tokens,
+                            void *buf_dev, int64_t buf_bytes, void *stream) {
+    return cache_xfer(cfg, cache, req, n_tokens, buf_dev, buf_bytes, true, stream);
+}
+
+dsv4_status dsv4_cache_load(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t n_tokens,
+                            const void *buf_dev, int64_t buf_bytes, void *stream) {
+    return cache_xfer(cfg, cache, req, n_tokens, buf_dev, buf_bytes, false, stream);
+}
+
 static dsv4_status proj_shape(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int32_t hidden) {
     if (!cfg) return DSV4_ERR_INVALID_ARG;
     const int H = cfg->n_heads, d = cfg->d;

@@ -97,5 +97,9 @@ hipError_t launch_out_proj(const uint16_t *o, int T, int H, int d, int groups, i
                            const uint16_t *w1p, const uint16_t *w2p, uint16_t *y, void *out, int out_f32,
                            hipStream_t s);
 hipError_t launch_pack_b(const uint16_t *W, uint16_t *P, int batch, int N, int K, hipStream_t s);
+// Dump / reload of one request's cache (state, then its entry and index blocks).
+int64_t cache_dump_bytes(const Lay &L, int nb);
+hipError_t launch_cache_xfer(const Lay &L, const dsv4_cache &C, int r, int nb, uint8_t *buf, bool to_buf,
+                             hipStream_t s);
 
 }  // namespace dsv4
