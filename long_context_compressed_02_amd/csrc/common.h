@@ -125,13 +125,24 @@ __device__ __forceinline__ float load_act(const void *p, int64_t i, int act) {
 // products with the quotient are exact for positions below 2^26), so large
 // positions keep full accuracy; the reduced angle's sine and cosine are then
 // taken in fp32.
-__device__ __forceinline__ void rope_cs(const Lay &L, int64_t pos, int i, float &c, float &s) {
-    const double ang = (double)pos * L.theta[i];
+__device__ __forceinline__ void rope_cs_theta(double theta, int64_t pos, float &c, float &s) {
+    const double ang = (double)pos * theta;
     const double kq = rint(ang * 0.15915494309189535);          // 1 / (2*pi)
     double r = __fma_rn(-kq, 6.28318530717958623200e+00, ang);  // 2*pi, split in three parts
     r = __fma_rn(-kq, 2.44929359829470641e-16, r);
     r = __fma_rn(-kq, -5.97232958240207e-33, r);
     sincosf((float)r, &s, &c);
+}
+__device__ __forceinline__ void rope_cs(const Lay &L, int64_t pos, int i, float &c, float &s) {
+    rope_cs_theta(L.theta[i], pos, c, s);
+}
+// theta_i for a lane-dependent i < n, read from the argument block with
+// uniform (scalar) loads: a per-lane indexed read is a vector load, and the
+// wait for it also waits for every vector load issued before it.
+__device__ __forceinline__ double theta_pick(const Lay &L, int i, int n) {
+    double th = 0.0;
+    for (int k = 0; k < n && k < 64; ++k) th = i == k ? L.theta[k] : th;
+    return th;
 }
 
 // Wave-wide max over the 64 lanes, returned to every lane.  Max is exact and

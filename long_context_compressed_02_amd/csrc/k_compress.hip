@@ -188,12 +188,15 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
     const int n = emit ? (int)(t - s0 + 1) : 1;
     const bool staged = emit && n <= kStageWin;
     float *newtok = tokbuf[staged ? n - 1 : 0];      // the new token, in ring layout
+    // the block of a completed entry (and of its index key), read with the
+    // token loads below rather than after the pooling: one memory round trip
+    const int64_t ebid = emit ? block_id(C.block_table, C.max_blocks, C.n_blocks, r, (j * L.m) / kBlockTokens) : -1;
 
     // 1. cos/sin of position t (the window record and the entry both sit
     // there), on the last wave while the others start their loads
     if (tid >= 192 && tid - 192 < DR / 2) {
         float c, sn;
-        rope_cs(L, t, tid - 192, c, sn);
+        rope_cs_theta(theta_pick(L, tid - 192, DR / 2), t, c, sn);
         cs_tab[tid - 192] = make_float2(c, sn);
     }
     // 2. one batch of loads into LDS: token slot s of the window (the new one
@@ -281,7 +284,8 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
     }
     // 5. the completed entry (wave 1) and its index key (wave 2)
     if (emit && wave == 1) {
-        uint8_t *dst = entry_ptr(L, C, r, j);
+        uint8_t *dst = ebid >= 0 ? (uint8_t *)C.entries + ebid * L.entry_block_bytes + (j % L.epb) * L.rec_bytes
+                                 : nullptr;
         if (dst) {
             float x[VPL];
 #pragma unroll
@@ -291,7 +295,12 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
     }
     if (emit && csa && wave == 2) {
         float *ss = nullptr;
-        uint8_t *dst = key_ptr(L, C, r, j, &ss);
+        uint8_t *dst = nullptr;
+        if (ebid >= 0) {
+            uint8_t *blk = (uint8_t *)C.index_keys + ebid * L.index_block_bytes;
+            ss = (float *)(blk + L.key_scale_off) + (j % L.epb);
+            dst = blk + (j % L.epb) * L.key_bytes;
+        }
         if (dst) {
             float x[2];
             x[0] = (2 * lane < dI) ? pooled[D + 2 * lane] : 0.0f;
