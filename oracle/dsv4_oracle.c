@@ -136,6 +136,34 @@ ORC_API int orc_mx_exponent(float amax) {
     return x < -127 ? -127 : (x > 127 ? 127 : x);
 }
 
+/* MXFP8 (OCP microscaling, E4M3 elements) of the indexer path's activations
+ * [X 2.1, R FP4 QAT section: the indexer path runs in low precision; the
+ * activations of its projections are read as FP8 with the same block-scale
+ * scheme as the FP4 rows]: blocks of 32 consecutive values share 2^x with
+ * x = floor(log2 amax) - 8 (8 = the exponent of E4M3's largest value 448),
+ * clamped to [-127, 127]; each value is RNE(v / 2^x) in E4M3, saturating to
+ * +-448.  Returns the represented values. */
+ORC_API void orc_mxfp8_rows(const double *x, long rows, int n, double *out) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r)
+        for (int b0 = 0; b0 < n; b0 += 32) {
+            const int nb = n - b0 < 32 ? n - b0 : 32;
+            float amax = 0.0f;
+            for (int i = 0; i < nb; ++i) amax = fmaxf(amax, fabsf((float)x[r * n + b0 + i]));
+            int e = -127;
+            if (amax > 0.0f) {
+                int ex;
+                frexp((double)amax, &ex);
+                e = (ex - 1) - 8;
+                e = e < -127 ? -127 : (e > 127 ? 127 : e);
+            }
+            for (int i = 0; i < nb; ++i) {
+                const float y = ldexpf((float)x[r * n + b0 + i], -e);
+                out[r * n + b0 + i] = ldexp(orc_e4m3_decode(orc_e4m3_encode(y)), e);
+            }
+        }
+}
+
 /* Store one vector of n values the way the cache holds it and return the
  * value the cache then represents (fp64, exact).
  *   mode 0 : fp32 storage (each value rounded to fp32).

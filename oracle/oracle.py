@@ -77,6 +77,7 @@ def lib():
                                  ctypes.c_long, dp, dp]
         L.orc_out_proj.argtypes = [dp, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp,
                                    ctypes.c_int, dp, dp]
+        L.orc_mxfp8_rows.argtypes = [dp, ctypes.c_long, ctypes.c_int, dp]
         _lib = L
     return _lib
 
@@ -216,6 +217,33 @@ def attend(q_rot, sinks, recs, tau: float, return_sink_mass: bool = False):
     sm = np.empty(H, dtype=np.float64)
     lib().orc_attend(_dp(q), _dp(z), H, d, tau, _dp(r), r.shape[0], _dp(out), _dp(sm))
     return (out, sm) if return_sink_mass else out
+
+
+def mxfp8_rows(x) -> np.ndarray:
+    """Rows as MXFP8: E4M3 values with one power-of-two scale per 32 dims."""
+    x = _f64(x)
+    x2 = x.reshape(-1, x.shape[-1])
+    out = np.empty_like(x2)
+    lib().orc_mxfp8_rows(_dp(np.ascontiguousarray(x2)), x2.shape[0], x2.shape[1], _dp(out))
+    return out.reshape(x.shape)
+
+
+def mxfp4_rows(x) -> np.ndarray:
+    """Rows as MXFP4: E2M1 values with one power-of-two scale per 32 dims."""
+    x = _f64(x)
+    x2 = np.ascontiguousarray(x.reshape(-1, x.shape[-1]))
+    out = np.empty_like(x2)
+    lib().orc_store_rows(_dp(x2), x2.shape[0], x2.shape[1], x2.shape[1], 2, _dp(out))
+    return out.reshape(x.shape)
+
+
+def mx_linear(x, w) -> np.ndarray:
+    """A projection on the indexer's low-precision path (vastsailsolution.com
+    CSA section: the query is first projected down to d_c = 1024, then up to
+    the index heads; rqlyzj.com FP4 QAT section and xiaoyuzhoufm.com 2.1: this
+    path runs in FP4).  Reading: weights w [N, K] stored MXFP4, activations x
+    [M, K] quantised to MXFP8 on the fly, out = x_q . w_q^T summed in fp64."""
+    return mxfp8_rows(x) @ mxfp4_rows(w).T
 
 
 def out_proj(o, w1, w2):

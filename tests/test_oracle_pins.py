@@ -478,3 +478,54 @@ def test_out_proj_special_cases():
     assert (out[2] == 0).all()
     assert np.array_equal(O.out_proj(o, w1, 2.0 * w2)[1], 2.0 * out)
 
+
+# ----------------------------------------------------------------- MX linear (indexer path)
+def test_mxfp8_rows_rule_and_bounds():
+    # hand block: amax 3.0 -> floor(log2 3) - 8 = -7, scale 2^-7: 3.0 -> 384 (an E4M3
+    # value), 1.01 -> 129.28 -> 128 (step 16 in [128, 256)), 0.1 -> 12.8 -> 13
+    # (step 1 in [8, 16)) -> 13/128
+    x = np.zeros(32)
+    x[:3] = [3.0, 1.01, 0.1]
+    st = O.mxfp8_rows(x[None])[0]
+    assert list(st[:3]) == [3.0, 1.0, 13.0 / 128] and (st[3:] == 0).all()
+    # saturation: amax 1.9 -> x = -8, 1.9 * 256 = 486.4 > 448 -> 448 / 256
+    assert O.mxfp8_rows(np.array([[1.9] + [0.0] * 31]))[0, 0] == 448.0 / 256
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((100, 96)) * rng.lognormal(0, 3, (100, 1))
+    st = O.mxfp8_rows(x)
+    for r in range(100):
+        for b in range(3):
+            xb = x[r, 32 * b:32 * b + 32].astype(np.float32).astype(np.float64)
+            amax = np.abs(xb).max()
+            e = int(np.floor(np.log2(amax))) - 8
+            y = st[r, 32 * b:32 * b + 32] / 2.0 ** e
+            # every value an E4M3 value (torch's cast is exact on representable values)
+            assert np.array_equal(torch.from_numpy(y).to(torch.float8_e4m3fn).to(torch.float64).numpy(), y)
+            # and the nearest one (torch's RNE cast) of the scaled input, saturated at 448
+            u = np.clip(xb / 2.0 ** e, -448, 448)
+            ref = torch.from_numpy(u).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+            assert np.array_equal(y, ref)
+
+
+def test_mx_linear_exact_on_representable_inputs():
+    """Inputs already exact in MXFP8 / MXFP4 pass the quantisers unchanged, so
+    the linear map is the plain product (numpy, exact on small integers)."""
+    rng = np.random.default_rng(23)
+    # activations: integers |v| <= 14 with a 14 in every block -> scale 2^-5, v * 32 in
+    # E4M3 (a 15 would not be: 480 > 448 saturates to 448, the price of the
+    # floor(log2 amax) - 8 rule, pinned below)
+    x = rng.integers(-14, 15, (9, 64)).astype(np.float64)
+    x[:, ::32] = 14.0
+    # weights: E2M1 magnitudes times 2^0 with a 6 (or 4) leading every block -> scale 2^0
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    w = mags[rng.integers(0, 8, (24, 64))] * rng.choice([-1.0, 1.0], (24, 64))
+    w[:, ::32] = 6.0
+    assert np.array_equal(O.mxfp8_rows(x), x) and np.array_equal(O.mxfp4_rows(w), w)
+    assert np.array_equal(O.mx_linear(x, w), x @ w.T)
+    y = np.zeros((1, 32))
+    y[0, :2] = [15.0, 1.0]
+    assert list(O.mxfp8_rows(y)[0, :2]) == [14.0, 1.0]
+    # and a block's quantisation does not depend on the others
+    x2 = x.copy()
+    x2[:, 32:] *= 1024.0
+    assert np.array_equal(O.mxfp8_rows(x2)[:, :32], O.mxfp8_rows(x)[:, :32])
