@@ -49,12 +49,13 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (traffic calibration under --pmc)")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "hca_decode", "pair_1m", "out_proj"],
+                    choices=["decode", "prefill", "hca_decode", "pair_1m", "out_proj", "index_q"],
                     help="decode: the CSA+HCA decode step, batch 32 at 128K (the headline); prefill: one "
                          "8192-token CSA chunk on a 256K-token prefix; hca_decode: the HCA decode step, batch 16 at "
                          "64K; pair_1m: the CSA+HCA decode step for 4 requests at 1M/512K/64K/4K; out_proj: the "
                          "grouped output projection (128 heads x 512 -> 16 groups of rank 1024 -> 7168) of --batch "
-                         "tokens")
+                         "tokens; index_q: the indexer's query path (7168 -> 1024 -> 64 x 128, MXFP4 weights, MXFP8 "
+                         "activations) of --batch tokens")
     return ap.parse_args()
 
 
@@ -69,6 +70,8 @@ def main():
         return decode_mix_main(a)
     if a.workload == "out_proj":
         return out_proj_main(a)
+    if a.workload == "index_q":
+        return index_q_main(a)
     import torch
     from long_context_compressed_02_amd import binding as B
     from long_context_compressed_02_amd import synth
@@ -396,6 +399,65 @@ def out_proj_main(a):
     print(json.dumps(res), flush=True)
 
 
+def index_q_main(a):
+    """The indexer's query path of --batch tokens: x [T, 7168] bf16 -> d_c =
+    1024 (bf16) -> 64 heads x 128 (fp32), both products on MXFP4 weights
+    (quantised and packed once, before timing) with the activations quantised
+    to MXFP8 on the way in.  Small batches stream the 7.8 MB of packed weights
+    (HBM-bound); a prefill chunk is bound by the matrix cores."""
+    import torch
+    from long_context_compressed_02_amd import binding as B
+
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    hidden, dc, HI, dI = 7168, 1024, 64, 128
+    T = a.batch
+    cfg = B.make_cfg(act_dtype=B.DSV4_DT_F32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(78)
+    rn = lambda *s_: torch.randn(*s_, generator=g, device=dev, dtype=torch.float32)
+    x = rn(T, hidden).to(torch.bfloat16)
+    wdq = (rn(dc, hidden) / hidden ** 0.5).to(torch.bfloat16)
+    wuq = (rn(HI * dI, dc) / dc ** 0.5).to(torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    wdq_p = torch.empty(B.dsv4_mx_pack_bytes(dc, hidden, False), dtype=torch.uint8, device=dev)
+    wuq_p = torch.empty(B.dsv4_mx_pack_bytes(HI * dI, dc, False), dtype=torch.uint8, device=dev)
+    B.dsv4_mx_pack_weight(wdq, wdq_p, stream)                  # once, before timing
+    B.dsv4_mx_pack_weight(wuq, wuq_p, stream)
+    del wdq, wuq
+    ws = torch.empty(B.dsv4_index_q_proj_ws_bytes(cfg, T, hidden, dc), dtype=torch.uint8, device=dev)
+    qI = torch.empty((T, HI, dI), dtype=torch.float32, device=dev)
+
+    def step(_s):
+        B.dsv4_index_q_proj(cfg, x, dc, wdq_p, wuq_p, ws, qI, stream)
+
+    ms, kern = _timed_steps(step, a.steps, a.warmup)
+    flops = 2.0 * T * (dc * hidden + HI * dI * dc)
+    # algorithmic bytes: packed weights once; x read; MXFP8 written and read
+    # (1 + 1/32 bytes per value) and d_c written and read (bf16), for both
+    # products; queries written
+    wbytes = float(wdq_p.numel() + wuq_p.numel())
+    abytes = T * (2.0 * hidden + 2 * (33 / 32) * (hidden + dc) + 2 * 2.0 * dc + 4.0 * HI * dI)
+    sec = ms * 1e-3
+    small = T <= 256
+    achieved = (wbytes + abytes) / sec / 1e9 if small else flops / sec / 1e12
+    peak = HBM_PEAK_GBS if small else FP8_PEAK_TFLOPS
+    roof = {"kernel": "k_mx_gemm", "bound": "hbm" if small else "mfma", "achieved": round(achieved, 2),
+            "peak": peak, "unit": "GB/s" if small else "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    res = {
+        "metric": "indexer query projection tokens/s", "value": round(T / sec, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4", "data": "synthetic",
+        "config": {"workload": f"indexer query path of {T} tokens: {hidden} -> {dc} -> {HI} x {dI}, MXFP4 "
+                               f"weights, MXFP8 activations", "tokens": T, "hidden": hidden, "dc": dc,
+                   "idx_heads": HI, "idx_dim": dI},
+        "roofline": roof,
+        "TFLOPs": round(flops / sec / 1e12, 1), "GBps": round((wbytes + abytes) / sec / 1e9, 1),
+        "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items() if v["launches"]},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def _timed_steps(step, steps, warm):
     """Warm up, time `steps` steps with events on the current stream, then run
     them again with the library's per-kernel timers on."""
@@ -418,7 +480,7 @@ def _timed_steps(step, steps, warm):
         step(s)
     torch.cuda.synchronize()
     names = {B.DSV4_K_COMPRESS: "compress", B.DSV4_K_INDEX_SCORE: "index_score", B.DSV4_K_TOPK: "topk",
-             B.DSV4_K_ATTEND: "attend", B.DSV4_K_PROJ: "out_proj"}
+             B.DSV4_K_ATTEND: "attend", B.DSV4_K_PROJ: "out_proj", B.DSV4_K_MX: "mx_linear"}
     kern = {}
     for kid, nm in names.items():
         ms, n = B.dsv4_timer_read(kid, True)

@@ -347,6 +347,55 @@ dsv4_status dsv4_out_proj_pack(const dsv4_cfg *cfg, int32_t groups, int32_t rank
                                const void *w2, void *w1p, void *w2p, void *stream);
 
 /*
+ * Linear layers of the indexer's low-precision path (vastsailsolution.com V4
+ * article, CSA section: the indexer's query is projected down to d_c = 1024
+ * dims, then up to the multi-head index queries; rqlyzj.com article, FP4 QAT
+ * section, and xiaoyuzhoufm.com summary 2.1: the indexer runs in FP4):
+ *   out [M][N] = x [M][K] . W [N][K]^T
+ * with W stored MXFP4 (E2M1 values, an E8M0 scale 2^(floor(log2 amax) - 2)
+ * per 32 consecutive k) and x, bf16, quantised on the way in to MXFP8 (E4M3
+ * values, scale 2^(floor(log2 amax) - 8) per 32 k, saturating at 448); the
+ * products summed in fp32.  No split-K: a row's output is bitwise the same in
+ * any batch.  K a multiple of 128, N of 16; M, N, K at most 2^20.
+ *
+ * dsv4_mx_pack_bytes  bytes of a packed operand of `rows` rows: fp8 = 0 for
+ *                     packed weights (MXFP4), 1 for the activation workspace
+ *                     dsv4_mx_linear needs (MXFP8 of x).
+ * dsv4_mx_pack_weight quantise and pack W (bf16 [N][K], 16-byte aligned) into
+ *                     wp (caller-owned, dsv4_mx_pack_bytes(N, K, 0) bytes):
+ *                     per 16-row block and 128-wide k-step, 1 KB in which
+ *                     bytes 16l .. 16l+15 hold the E2M1 codes of row l%16,
+ *                     k = 32(l/16) .. +31 (value 2i in the low nibble of byte
+ *                     i); then per 16-row block and group of four k-steps, 64
+ *                     words whose byte j is lane l's scale for k-step 4q+j.
+ * dsv4_mx_linear      x bf16 [M][K]; wp packed weights; ws device workspace of
+ *                     at least dsv4_mx_pack_bytes(M, K, 1) bytes, 256-byte
+ *                     aligned; out [M][N], out_dtype DSV4_DT_F32 or
+ *                     DSV4_DT_BF16 (round to nearest even).
+ */
+dsv4_status dsv4_mx_pack_bytes(int32_t rows, int32_t K, int32_t fp8, int64_t *out);
+dsv4_status dsv4_mx_pack_weight(const void *w, int32_t N, int32_t K, void *wp, int64_t wp_bytes, void *stream);
+dsv4_status dsv4_mx_linear(const void *x, int32_t M, int32_t K, const void *wp, int32_t N, void *ws,
+                           int64_t ws_bytes, void *out, int32_t out_dtype, void *stream);
+
+/*
+ * The indexer's query path (same passages): cq = bf16(x . Wdq^T), then
+ * qI = cq . Wuq^T, both as dsv4_mx_linear.
+ *   x     [T][hidden] bf16
+ *   wdq_p Wdq [dc][hidden] packed by dsv4_mx_pack_weight
+ *   wuq_p Wuq [idx_heads*idx_dim][dc] packed likewise
+ *   qI    [T][idx_heads][idx_dim] in cfg->act_dtype (the input of the index
+ *         scoring entry points)
+ *   ws    at least dsv4_index_q_proj_ws_bytes bytes, 256-byte aligned
+ *         (receives cq, then the MXFP8 activations)
+ * hidden and dc multiples of 128, idx_heads*idx_dim a multiple of 16.
+ */
+dsv4_status dsv4_index_q_proj_ws_bytes(const dsv4_cfg *cfg, int32_t T, int32_t hidden, int32_t dc, int64_t *out);
+dsv4_status dsv4_index_q_proj(const dsv4_cfg *cfg, const void *x, int32_t T, int32_t hidden, int32_t dc,
+                              const void *wdq_p, const void *wuq_p, void *ws, int64_t ws_bytes, void *qI,
+                              void *stream);
+
+/*
  * Cache fill (benchmarks, tests, reloading a saved prefix).  Writes n entries
  * (target DSV4_TARGET_ENTRY: a KV record, RoPE at the entry's block-end
  * position m*j+m-1 then stored; DSV4_TARGET_INDEX_KEY: a CSA index key,
@@ -398,7 +447,8 @@ dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache
 #define DSV4_K_TOPK 2
 #define DSV4_K_ATTEND 3
 #define DSV4_K_PROJ 4
-#define DSV4_K_COUNT 5
+#define DSV4_K_MX 5
+#define DSV4_K_COUNT 6
 dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on);
 dsv4_status dsv4_timer_read(int32_t kernel_id, int32_t reset, double *total_ms, int64_t *count);
 

@@ -25,7 +25,7 @@ DSV4_DT_F32, DSV4_DT_BF16 = 0, 1
 DSV4_POLICY_AUTO, DSV4_POLICY_HI, DSV4_POLICY_LO = 0, 1, 2
 DSV4_TARGET_ENTRY, DSV4_TARGET_INDEX_KEY = 0, 1
 DSV4_BLOCK_TOKENS = 128
-DSV4_K_COMPRESS, DSV4_K_INDEX_SCORE, DSV4_K_TOPK, DSV4_K_ATTEND, DSV4_K_PROJ, DSV4_K_COUNT = range(6)
+DSV4_K_COMPRESS, DSV4_K_INDEX_SCORE, DSV4_K_TOPK, DSV4_K_ATTEND, DSV4_K_PROJ, DSV4_K_MX, DSV4_K_COUNT = range(7)
 
 EXPORTS = [
     "dsv4_status_string", "dsv4_get_layout", "dsv4_workspace_bytes", "dsv4_compress_kv_decode",
@@ -34,6 +34,8 @@ EXPORTS = [
     "dsv4_hca_attend_prefill", "dsv4_cache_write_entries", "dsv4_state_write_tokens",
     "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
     "dsv4_out_proj_pack", "dsv4_cache_dump_bytes", "dsv4_cache_dump", "dsv4_cache_load",
+    "dsv4_mx_pack_bytes", "dsv4_mx_pack_weight", "dsv4_mx_linear", "dsv4_index_q_proj_ws_bytes",
+    "dsv4_index_q_proj",
 ]
 
 
@@ -96,6 +98,11 @@ def lib():
             "dsv4_cache_dump_bytes": [cp, i32, i32, ctypes.POINTER(i64)],
             "dsv4_cache_dump": [cp, kp, i32, i32, vp, i64, vp],
             "dsv4_cache_load": [cp, kp, i32, i32, vp, i64, vp],
+            "dsv4_mx_pack_bytes": [i32, i32, i32, ctypes.POINTER(i64)],
+            "dsv4_mx_pack_weight": [vp, i32, i32, vp, i64, vp],
+            "dsv4_mx_linear": [vp, i32, i32, vp, i32, vp, i64, vp, i32, vp],
+            "dsv4_index_q_proj_ws_bytes": [cp, i32, i32, i32, ctypes.POINTER(i64)],
+            "dsv4_index_q_proj": [cp, vp, i32, i32, i32, vp, vp, vp, i64, vp, vp],
             "dsv4_timer_enable": [i32, i32],
             "dsv4_timer_read": [i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         }
@@ -278,6 +285,42 @@ def dsv4_out_proj_pack(cfg, groups: int, rank: int, hidden: int, w1, w2, w1p, w2
     """w1: bf16 [groups, rank, n_heads/groups*d]; w2: bf16 [hidden, groups*rank]; w1p, w2p: same sizes."""
     _ck("dsv4_out_proj_pack", lib().dsv4_out_proj_pack(ctypes.byref(cfg), groups, rank, hidden, _p(w1), _p(w2),
                                                        _p(w1p), _p(w2p), _stream(stream)))
+
+
+def dsv4_mx_pack_bytes(rows: int, K: int, fp8: bool) -> int:
+    out = ctypes.c_int64()
+    _ck("dsv4_mx_pack_bytes", lib().dsv4_mx_pack_bytes(rows, K, int(fp8), ctypes.byref(out)))
+    return out.value
+
+
+def dsv4_mx_pack_weight(w, wp, stream=None):
+    """w: bf16 [N, K]; wp: uint8 device tensor of dsv4_mx_pack_bytes(N, K, False) bytes."""
+    _ck("dsv4_mx_pack_weight", lib().dsv4_mx_pack_weight(_p(w), w.shape[0], w.shape[1], _p(wp),
+                                                         wp.numel() * wp.element_size(), _stream(stream)))
+
+
+def dsv4_mx_linear(x, wp, N: int, ws, out, stream=None):
+    """x: bf16 [M, K]; wp: packed MXFP4 weights [N, K]; ws: uint8 workspace of
+    dsv4_mx_pack_bytes(M, K, True) bytes; out: fp32 or bf16 [M, N]."""
+    import torch
+    dt = DSV4_DT_F32 if out.dtype == torch.float32 else DSV4_DT_BF16
+    _ck("dsv4_mx_linear", lib().dsv4_mx_linear(_p(x), x.shape[0], x.shape[1], _p(wp), N, _p(ws),
+                                               ws.numel() * ws.element_size(), _p(out), dt, _stream(stream)))
+
+
+def dsv4_index_q_proj_ws_bytes(cfg, T: int, hidden: int, dc: int) -> int:
+    out = ctypes.c_int64()
+    _ck("dsv4_index_q_proj_ws_bytes", lib().dsv4_index_q_proj_ws_bytes(ctypes.byref(cfg), T, hidden, dc,
+                                                                       ctypes.byref(out)))
+    return out.value
+
+
+def dsv4_index_q_proj(cfg, x, dc: int, wdq_p, wuq_p, ws, qI, stream=None):
+    """x: bf16 [T, hidden]; wdq_p, wuq_p: packed MXFP4 weights; ws: uint8 workspace;
+    qI: [T, idx_heads, idx_dim] in the act dtype."""
+    _ck("dsv4_index_q_proj", lib().dsv4_index_q_proj(ctypes.byref(cfg), _p(x), x.shape[0], x.shape[1], dc,
+                                                     _p(wdq_p), _p(wuq_p), _p(ws), ws.numel() * ws.element_size(),
+                                                     _p(qI), _stream(stream)))
 
 
 def dsv4_timer_enable(kernel_id: int, on: bool = True):

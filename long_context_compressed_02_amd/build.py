@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libdsv4attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "k_compress.hip", "k_index.hip", "k_attend.hip", "k_proj.hip", "k_cache.hip"]
+SOURCES = ["api.cpp", "k_compress.hip", "k_index.hip", "k_attend.hip", "k_proj.hip", "k_cache.hip", "k_mx.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # no fused multiply-add contraction: reductions keep one fixed rounding sequence

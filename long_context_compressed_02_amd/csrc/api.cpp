@@ -520,6 +520,75 @@ dsv4_status dsv4_out_proj(const dsv4_cfg *cfg, int32_t groups, int32_t rank, int
                                       (const uint16_t *)w2, (uint16_t *)y_ws, out, 0, S(stream)));
 }
 
+static bool mx_shape_ok(int64_t M, int64_t N, int64_t K) {
+    return M >= 0 && M <= (1 << 20) && N >= 16 && N <= (1 << 20) && N % 16 == 0 && K >= 128 && K <= (1 << 20) &&
+           K % 128 == 0;
+}
+
+dsv4_status dsv4_mx_pack_bytes(int32_t rows, int32_t K, int32_t fp8, int64_t *out) {
+    if (!out || rows < 0 || rows > (1 << 20) || K < 128 || K > (1 << 20) || K % 128) return DSV4_ERR_INVALID_ARG;
+    *out = mx_pack_bytes(rows, K, fp8 != 0);
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_mx_pack_weight(const void *w, int32_t N, int32_t K, void *wp, int64_t wp_bytes, void *stream) {
+    if (!mx_shape_ok(0, N, K) || !w || !wp) return DSV4_ERR_INVALID_ARG;
+    if (((uintptr_t)w | (uintptr_t)wp) & 15) return DSV4_ERR_INVALID_ARG;
+    if (wp_bytes < mx_pack_bytes(N, K, false)) return DSV4_ERR_WORKSPACE;
+    return hip_status(launch_mx_quant((const uint16_t *)w, N, K, false, (uint8_t *)wp, S(stream)));
+}
+
+static dsv4_status mx_linear(const void *x, int M, int K, const void *wp, int N, uint8_t *ws, void *out, int ldc,
+                             int c_f32, hipStream_t s) {
+    hipError_t e = launch_mx_quant((const uint16_t *)x, M, K, true, ws, s);
+    if (e != hipSuccess) return DSV4_ERR_LAUNCH;
+    return hip_status(launch_mx_gemm(ws, (const uint8_t *)wp, M, N, K, out, ldc, c_f32, s));
+}
+
+dsv4_status dsv4_mx_linear(const void *x, int32_t M, int32_t K, const void *wp, int32_t N, void *ws,
+                           int64_t ws_bytes, void *out, int32_t out_dtype, void *stream) {
+    if (!mx_shape_ok(M, N, K)) return DSV4_ERR_INVALID_ARG;
+    if (out_dtype != DSV4_DT_F32 && out_dtype != DSV4_DT_BF16) return DSV4_ERR_INVALID_ARG;
+    if (M == 0) return DSV4_OK;
+    if (!x || !wp || !out) return DSV4_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)wp) & 15) return DSV4_ERR_INVALID_ARG;
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < mx_pack_bytes(M, K, true)) return DSV4_ERR_WORKSPACE;
+    if ((M + 127) / 128 > 65535) return DSV4_ERR_UNSUPPORTED;
+    Timed tm(DSV4_K_MX, S(stream));
+    return mx_linear(x, M, K, wp, N, (uint8_t *)ws, out, N, out_dtype == DSV4_DT_F32, S(stream));
+}
+
+static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+dsv4_status dsv4_index_q_proj_ws_bytes(const dsv4_cfg *cfg, int32_t T, int32_t hidden, int32_t dc, int64_t *out) {
+    if (!cfg || !out || T < 0) return DSV4_ERR_INVALID_ARG;
+    const int64_t nq = (int64_t)cfg->idx_heads * cfg->idx_dim;
+    if (!mx_shape_ok(T, dc, hidden) || !mx_shape_ok(T, nq, dc)) return DSV4_ERR_INVALID_ARG;
+    const int64_t a = mx_pack_bytes(T, hidden, true), b = mx_pack_bytes(T, dc, true);
+    *out = round256((int64_t)T * dc * 2) + (a > b ? a : b);
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_index_q_proj(const dsv4_cfg *cfg, const void *x, int32_t T, int32_t hidden, int32_t dc,
+                              const void *wdq_p, const void *wuq_p, void *ws, int64_t ws_bytes, void *qI,
+                              void *stream) {
+    int64_t need = 0;
+    dsv4_status st = dsv4_index_q_proj_ws_bytes(cfg, T, hidden, dc, &need);
+    if (st != DSV4_OK) return st;
+    if (cfg->act_dtype != DSV4_DT_F32 && cfg->act_dtype != DSV4_DT_BF16) return DSV4_ERR_INVALID_ARG;
+    if (T == 0) return DSV4_OK;
+    if (!x || !wdq_p || !wuq_p || !qI) return DSV4_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)wdq_p | (uintptr_t)wuq_p) & 15) return DSV4_ERR_INVALID_ARG;
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < need) return DSV4_ERR_WORKSPACE;
+    if ((T + 127) / 128 > 65535) return DSV4_ERR_UNSUPPORTED;
+    const int nq = cfg->idx_heads * cfg->idx_dim;
+    uint8_t *cq = (uint8_t *)ws, *act = cq + round256((int64_t)T * dc * 2);
+    Timed tm(DSV4_K_MX, S(stream));
+    st = mx_linear(x, T, hidden, wdq_p, dc, act, cq, dc, 0, S(stream));
+    if (st != DSV4_OK) return st;
+    return mx_linear(cq, T, dc, wuq_p, nq, act, qI, nq, cfg->act_dtype == DSV4_DT_F32, S(stream));
+}
+
 dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on) {
     if (kernel_id < 0 || kernel_id >= DSV4_K_COUNT) return DSV4_ERR_INVALID_ARG;
     g_timers[kernel_id].on = on != 0;

@@ -1,0 +1,272 @@
+// k_mx.hip -- linear layers of the indexer's low-precision path for gfx950.
+//
+// What is computed (vastsailsolution.com V4 article, CSA section: the
+// indexer's query is first projected down to d_c = 1024 dims, then up to the
+// multi-head index queries; rqlyzj.com article, FP4 QAT section, and
+// xiaoyuzhoufm.com summary 2.1: the indexer runs in FP4): out = x . W^T with
+//   W [N][K]  weights, stored once as MXFP4 (E2M1 values, one E8M0 power-of-two
+//             scale per 32 consecutive k: exponent floor(log2 amax) - 2);
+//   x [M][K]  bf16 activations, quantised on the way in to MXFP8 (E4M3 values,
+//             one scale per 32 k: exponent floor(log2 amax) - 8);
+// summed in fp32 by v_mfma_scale_f32_16x16x128_f8f6f4 (A = FP8, B = FP4, the
+// scales applied by the instruction per lane).
+//
+// Operand order of a 16x16x128 step (measured with a probe on gfx950, every
+// other candidate order failing): lane l (g = l/16, c = l%16) supplies
+//   B (FP4): row c's k = 32g .. 32g+31, 16 bytes, value 2i in the low nibble
+//            of byte i;
+//   A (FP8): row c's k = 16g .. 16g+15 in bytes 0..15 and k = 64+16g ..
+//            64+16g+15 in bytes 16..31;
+//   scales:  one byte per operand, the scale of row c's k-block g (k = 32g ..
+//            32g+31), wherever those values sit in the registers.
+// So a B lane holds exactly its own MX block, while an A block spreads over two
+// lanes: block g's first 16 values go to lane group 2(g%2), its last 16 to
+// lane group 2(g%2)+1, in the half g/2 of their 32 bytes.  Both operands are
+// written in register order, so every load is a contiguous kilobyte per wave:
+//   codes   tile (16-row block, 128-wide k-step): FP8: two 1 KB halves, half h
+//           holding bytes 16h .. 16h+15 of each lane at 16l; FP4: one 1 KB
+//           piece, lane l's 16 bytes at 16l
+//   scales  per (16-row block, group of four k-steps): 64 lanes x 4 bytes,
+//           byte j = lane l's scale for k-step 4q+j (0x7f past the last step)
+// Rows are padded to a multiple of 16 with zeros (scale byte 0, codes 0).
+//
+// Batch invariance (m.youleyou.com article, "what was sacrificed": no split-K):
+// one wave reduces each output over k in increasing order with the same
+// instruction whatever the tiling, so a row's output is bitwise the same in any
+// batch.
+#include "launch.h"
+
+namespace dsv4 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+int64_t mx_pack_bytes(int rows, int K, bool fp8) {
+    const int64_t rb = (rows + 15) / 16, nks = K / 128, nq = (nks + 3) / 4;
+    return rb * nks * (fp8 ? 2048 : 1024) + rb * nq * 256;
+}
+__host__ __device__ static inline int64_t mx_code_bytes(int rows, int K, bool fp8) {
+    return (int64_t)((rows + 15) / 16) * (K / 128) * (fp8 ? 2048 : 1024);
+}
+
+// MXFP8 shared exponent: floor(log2 amax) - 8 (8: the exponent of E4M3's
+// largest value 448, so the block's largest magnitude scales into [256, 512)
+// and saturates to 448 above it), clamped to the E8M0 range; -127 for a block
+// of zeros or below the smallest normal fp32.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+    if (!(amax >= 1.17549435e-38f)) return -127;
+    const int x = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 8;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// One thread per (16-row block, group of four k-steps, lane (g, c)):
+// quantises row c's block g (k = 32g .. 32g+31) of each of the four k-steps,
+// writes the codes where the operand order puts them and the lane's scale word.
+template <bool F8>
+__global__ __launch_bounds__(256) void k_mx_quant(const uint16_t *X, int rows, int K, uint8_t *P, int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int lane = (int)(i & 63), g = lane >> 4;
+    const int nks = K / 128, nq = (nks + 3) / 4;
+    const int64_t t = i >> 6;
+    const int kq = (int)(t % nq);
+    const int64_t rb = t / nq;
+    const int64_t row = rb * 16 + (lane & 15);
+    const bool live = row < rows;
+    uint8_t *scales = P + mx_code_bytes(rows, K, F8);
+    uint32_t sw = 0x7f7f7f7fu;
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+        const int ks = 4 * kq + j;
+        if (ks >= nks) break;
+        u32x4 raw[4] = {};
+        if (live) {
+            const u32x4 *src = (const u32x4 *)(X + row * K + 128 * ks + 32 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) raw[v] = src[v];
+        }
+        float x[32];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                x[8 * v + 2 * w] = __uint_as_float(raw[v][w] << 16);
+                x[8 * v + 2 * w + 1] = __uint_as_float(raw[v][w] & 0xffff0000u);
+            }
+        float amax = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 32; ++v) amax = fmaxf(amax, fabsf(x[v]));
+        const int e = F8 ? mx8_exponent(amax) : mx_exponent(amax);
+        sw = (sw & ~(0xffu << (8 * j))) | ((uint32_t)(e + 127) << (8 * j));
+        if constexpr (F8) {
+            u32x4 c[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        word |= fp8_code(__builtin_ldexpf(x[16 * h + 4 * w + b], -e)) << (8 * b);
+                    c[h][w] = word;
+                }
+            // first 16 values -> lane group 2(g%2), last 16 -> 2(g%2)+1, half g/2
+            const int l0 = 16 * (2 * (g & 1)) + (lane & 15);
+            uint8_t *dst = P + ((rb * nks + ks) * 2 + (g >> 1)) * 1024;
+            *(u32x4 *)(dst + 16 * l0) = c[0];
+            *(u32x4 *)(dst + 16 * (l0 + 16)) = c[1];
+        } else {
+            u32x4 c;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) word |= e2m1_code(__builtin_ldexpf(x[8 * w + b], -e)) << (4 * b);
+                c[w] = word;
+            }
+            *(u32x4 *)(P + (rb * nks + ks) * 1024 + 16 * lane) = c;
+        }
+    }
+    ((uint32_t *)(scales + (rb * nq + kq) * 256))[lane] = sw;
+}
+
+struct MxArgs {
+    const uint8_t *A;       // MXFP8 activations, packed (rows padded to 16)
+    const uint8_t *B;       // MXFP4 weights, packed
+    void *C;                // [M][ldc] fp32 or bf16
+    int64_t a_scale_off, b_scale_off;
+    int64_t ldc;
+    int M, N, K;
+    int c_f32;
+};
+
+// WM x WN 16x16 blocks per wave, WGM x WGN waves per workgroup (4 in all), D
+// k-steps of loads in flight.
+template <int WM, int WN, int WGM, int WGN, int D>
+__global__ __launch_bounds__(256) void k_mx_gemm(MxArgs G) {
+    static_assert(WGM * WGN == 4, "four waves");
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int nks = G.K / 128, nq = (nks + 3) / 4;
+    const int rbs = (G.M + 15) / 16, cbs = G.N / 16;
+    const int rb0 = blockIdx.y * (WGM * WM) + wm * WM;
+    const int cb0 = blockIdx.x * (WGN * WN) + wn * WN;
+    // blocks past the matrix read the last one (their results are not stored)
+    const uint8_t *ap[WM];
+    const uint8_t *bp[WN];
+    const uint32_t *asp[WM];
+    const uint32_t *bsp[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+        const int64_t rb = rb0 + i < rbs ? rb0 + i : rbs - 1;
+        ap[i] = G.A + rb * nks * 2048 + 16 * lane;
+        asp[i] = (const uint32_t *)(G.A + G.a_scale_off + rb * nq * 256) + lane;
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+        const int64_t cb = cb0 + j < cbs ? cb0 + j : cbs - 1;
+        bp[j] = G.B + cb * nks * 1024 + 16 * lane;
+        bsp[j] = (const uint32_t *)(G.B + G.b_scale_off + cb * nq * 256) + lane;
+    }
+    f32x4 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+    i32x4 ra[D][WM][2], rbv[D][WN];
+    uint32_t sa[D][WM], sb[D][WN];
+    // step s's loads; steps past the end re-read the last step (never used), so
+    // every ring slot is refilled on every path and the counter waits stay exact
+    auto load = [&](int slot, int s) {
+        const int sc = s < nks ? s : nks - 1;
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+            ra[slot][i][0] = *(const i32x4 *)(ap[i] + (int64_t)2048 * sc);
+            ra[slot][i][1] = *(const i32x4 *)(ap[i] + (int64_t)2048 * sc + 1024);
+            sa[slot][i] = asp[i][64 * (sc >> 2)];
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            rbv[slot][j] = *(const i32x4 *)(bp[j] + (int64_t)1024 * sc);
+            sb[slot][j] = bsp[j][64 * (sc >> 2)];
+        }
+    };
+    const i32x4 z4 = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < D; ++s) load(s, s);
+#pragma unroll 1
+    for (int s0 = 0; s0 < nks; s0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int s = s0 + d;
+            if (s < nks) {                               // (uniform)
+                const int sh = 8 * (s & 3);
+#pragma unroll
+                for (int i = 0; i < WM; ++i) {
+                    i32x8 a;
+                    a.lo = ra[d][i][0];
+                    a.hi = ra[d][i][1];
+#pragma unroll
+                    for (int j = 0; j < WN; ++j) {
+                        i32x8 b;
+                        b.lo = rbv[d][j];
+                        b.hi = z4;
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a, b, acc[i][j], 0, 4, 0, (int)(sa[d][i] >> sh), 0, (int)(sb[d][j] >> sh));
+                    }
+                }
+            }
+            load(d, s + D);
+        }
+    }
+    // lane (g, c16) holds rows 4g+e, column c16 of each 16x16 block
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+            const int col = 16 * (cb0 + j) + c16;
+            if (cb0 + j >= cbs) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * (rb0 + i) + 4 * g + e;
+                if (row >= G.M) continue;
+                const int64_t off = (int64_t)row * G.ldc + col;
+                if (G.c_f32) ((float *)G.C)[off] = acc[i][j][e];
+                else ((uint16_t *)G.C)[off] = bf16_bits(acc[i][j][e]);
+            }
+        }
+}
+
+// Tilings.  Up to 64 rows: a wave owns all (2 or 4) row blocks of one
+// column block and keeps 8 k-steps of loads in flight -- the weights stream
+// once.  Larger: a wave owns 64x64, a workgroup 128x128.
+constexpr int kMxSmallRows = 64;
+
+hipError_t launch_mx_quant(const uint16_t *X, int rows, int K, bool fp8, uint8_t *P, hipStream_t s) {
+    const int nq = (K / 128 + 3) / 4;
+    const int64_t total = (int64_t)((rows + 15) / 16) * nq * 64;
+    if (fp8) hipLaunchKernelGGL(k_mx_quant<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, X, rows, K, P, total);
+    else hipLaunchKernelGGL(k_mx_quant<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, X, rows, K, P, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm(const uint8_t *A, const uint8_t *Bp, int M, int N, int K, void *C, int64_t ldc, int c_f32,
+                          hipStream_t s) {
+    MxArgs G{A, Bp, C, mx_code_bytes(M, K, true), mx_code_bytes(N, K, false), ldc, M, N, K, c_f32};
+    const int rbs = (M + 15) / 16, cbs = N / 16;
+    if (M <= 32) {
+        hipLaunchKernelGGL((k_mx_gemm<2, 1, 1, 4, 8>), dim3((unsigned)((cbs + 3) / 4)), dim3(256), 0, s, G);
+    } else if (M <= kMxSmallRows) {
+        hipLaunchKernelGGL((k_mx_gemm<4, 1, 1, 4, 8>), dim3((unsigned)((cbs + 3) / 4)), dim3(256), 0, s, G);
+    } else {
+        dim3 grid((unsigned)((cbs + 7) / 8), (unsigned)((rbs + 7) / 8));
+        hipLaunchKernelGGL((k_mx_gemm<4, 4, 2, 2, 2>), grid, dim3(256), 0, s, G);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dsv4

@@ -98,6 +98,10 @@ hipError_t launch_out_proj(const uint16_t *o, int T, int H, int d, int groups, i
                            hipStream_t s);
 hipError_t launch_pack_b(const uint16_t *W, uint16_t *P, int batch, int N, int K, hipStream_t s);
 // Dump / reload of one request's cache (state, then its entry and index blocks).
+int64_t mx_pack_bytes(int rows, int K, bool fp8);
+hipError_t launch_mx_quant(const uint16_t *X, int rows, int K, bool fp8, uint8_t *P, hipStream_t s);
+hipError_t launch_mx_gemm(const uint8_t *A, const uint8_t *Bp, int M, int N, int K, void *C, int64_t ldc, int c_f32,
+                          hipStream_t s);
 int64_t cache_dump_bytes(const Lay &L, int nb);
 hipError_t launch_cache_xfer(const Lay &L, const dsv4_cache &C, int r, int nb, uint8_t *buf, bool to_buf,
                              hipStream_t s);

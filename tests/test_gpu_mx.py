@@ -1,0 +1,219 @@
+"""GPU parity of the indexer's low-precision linear layers (MXFP4 weights,
+MXFP8 activations) against the CPU oracle, through the C ABI.
+
+Tolerances, from the arithmetic: both sides quantise the same bf16 values with
+the same rules, so the codes and scales agree exactly (checked directly on the
+packed weights) and the products of codes are exact; what differs is only the
+summation -- the matrix cores' against the oracle's fp64.  One scaled 128-term
+step of the matrix core lands within about 1.2e-4 of the step's sum of
+|products| from the exact sum (measured on single instructions with random
+E4M3 / E2M1 codes and scales: the instruction's internal rounding, coarser than
+a sequential fp32 sum), and the steps are added in fp32.  So |gpu - ref| is
+held below 2^-12 of sum_k |x_q w_q|.  Where the GPU rounds to bf16 (the query path's d_c summary) the two
+agree exactly except near a rounding boundary."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_compressed_02_amd import binding as B
+from long_context_compressed_02_amd import synth
+from oracle import oracle as O
+from tests import helpers as Hh
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2.0 ** -12
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def _f64(t):
+    return t.to(torch.float64).cpu().numpy()
+
+
+def _pack(w):
+    N, K = w.shape
+    wp = torch.empty(B.dsv4_mx_pack_bytes(N, K, False), dtype=torch.uint8, device=DEV)
+    B.dsv4_mx_pack_weight(w, wp)
+    return wp
+
+
+def _linear(x, wp, N, out_dtype=torch.float32):
+    M, K = x.shape
+    ws = torch.empty(max(B.dsv4_mx_pack_bytes(M, K, True), 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty((M, N), dtype=out_dtype, device=DEV)
+    B.dsv4_mx_linear(x, wp, N, ws, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_f32(out, x, w, rows=None):
+    """out fp32 against the oracle in fp64 with the summation bound above."""
+    xs = _f64(x) if rows is None else _f64(x[rows])
+    ref = O.mx_linear(xs, _f64(w))
+    mag = np.abs(O.mxfp8_rows(xs)) @ np.abs(O.mxfp4_rows(_f64(w))).T
+    g = _f64(out) if rows is None else _f64(out[rows])
+    err = np.abs(g - ref)
+    bad = err > TOL * mag + 1e-37
+    print(f"  max err / bound {np.max(err / (TOL * mag + 1e-37)):.3f}", flush=True)
+    assert not bad.any(), (np.argwhere(bad)[:5], g[bad][:5], ref[bad][:5])
+
+
+def test_mx_weight_pack_layout():
+    """The packed MXFP4 weights decode, through the documented layout, to exactly
+    the oracle's MXFP4 rows (codes, nibble order and scales)."""
+    g = np.random.default_rng(3)
+    N, K = 48, 384                                   # 3 row blocks, 3 k-steps (a partial group of 4)
+    w = g.standard_normal((N, K)).astype(np.float32) * g.lognormal(0, 2, (N, 1)).astype(np.float32)
+    w[5] = 0.0                                        # a zero row
+    w[7, 40:72] *= 1e-30                              # tiny blocks
+    wt = _bf16(w)
+    wp = _pack(wt).cpu().numpy()
+    nks, nq = K // 128, (K // 128 + 3) // 4
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    dec = np.zeros((N, K))
+    code_bytes = (N // 16) * nks * 1024
+    for rb in range(N // 16):
+        for ks in range(nks):
+            for lane in range(64):
+                n, k0 = 16 * rb + lane % 16, 128 * ks + 32 * (lane // 16)
+                by = wp[(rb * nks + ks) * 1024 + 16 * lane:][:16]
+                sc = wp[code_bytes + (rb * nq + ks // 4) * 256 + 4 * lane + ks % 4]
+                for i in range(16):
+                    for half in range(2):
+                        c = (by[i] >> (4 * half)) & 15
+                        v = (-1.0 if c & 8 else 1.0) * mags[c & 7]
+                        dec[n, k0 + 2 * i + half] = v * 2.0 ** (int(sc) - 127)
+    assert np.array_equal(dec, O.mxfp4_rows(_f64(wt)))
+
+
+@pytest.mark.parametrize("K", [128, 384, 1024])
+def test_mx_linear_small_ragged(K):
+    g = np.random.default_rng([5, K])
+    N = 48                                            # 3 column blocks: a ragged column tile
+    w = _bf16(g.standard_normal((N, K)) / np.sqrt(K))
+    wp = _pack(w)
+    for M in (1, 20, 37, 64, 300):                    # every tiling, ragged row counts
+        x = g.standard_normal((M, K)).astype(np.float32) * g.lognormal(0, 2, (M, 1)).astype(np.float32)
+        x[M // 2] = 0.0                               # a zero row
+        if M > 2:
+            x[1, :32] *= 1e30                         # saturating / extreme blocks
+            x[2, 32:64] *= 1e-30
+        xt = _bf16(x)
+        out = _linear(xt, wp, N)
+        _check_f32(out, xt, w)
+        assert (out[M // 2] == 0).all()
+
+
+def test_mx_linear_batch_invariance_and_bf16_out():
+    g = np.random.default_rng(9)
+    N, K = 256, 1024
+    w = _bf16(g.standard_normal((N, K)) / 32)
+    wp = _pack(w)
+    x = _bf16(g.standard_normal((300, K)))
+    big = _linear(x, wp, N)
+    for M, off in ((1, 17), (20, 100), (64, 200)):
+        part = _linear(x[off:off + M].contiguous(), wp, N)
+        assert torch.equal(part.view(torch.int32), big[off:off + M].view(torch.int32)), M
+    # bf16 output: the fp32 result rounded to nearest even
+    bo = _linear(x, wp, N, torch.bfloat16)
+    assert torch.equal(bo.view(torch.int16), big.to(torch.bfloat16).view(torch.int16))
+
+
+def test_mx_linear_argument_checks():
+    w = torch.zeros((48, 256), dtype=torch.bfloat16, device=DEV)
+    wp = _pack(w)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(B.dsv4_mx_pack_bytes(4, 256, True), dtype=torch.uint8, device=DEV)
+    out = torch.empty((4, 48), dtype=torch.float32, device=DEV)
+    for bad_k in (200, 0):                                    # K not a positive multiple of 128
+        st = B.lib().dsv4_mx_linear(x.data_ptr(), 4, bad_k, wp.data_ptr(), 48, ws.data_ptr(), ws.numel(),
+                                    out.data_ptr(), B.DSV4_DT_F32, None)
+        assert st == B.DSV4_ERR_INVALID_ARG
+    st = B.lib().dsv4_mx_linear(x.data_ptr(), 4, 256, wp.data_ptr(), 40, ws.data_ptr(), ws.numel(), out.data_ptr(),
+                                B.DSV4_DT_F32, None)
+    assert st == B.DSV4_ERR_INVALID_ARG                       # N not a multiple of 16
+    st = B.lib().dsv4_mx_linear(x.data_ptr(), 4, 256, wp.data_ptr(), 48, ws.data_ptr(), ws.numel() - 1,
+                                out.data_ptr(), B.DSV4_DT_F32, None)
+    assert st == B.DSV4_ERR_WORKSPACE
+    st = B.lib().dsv4_mx_linear(x.data_ptr(), 4, 256, wp.data_ptr(), 48, ws.data_ptr() + 16, ws.numel(),
+                                out.data_ptr(), B.DSV4_DT_F32, None)
+    assert st == B.DSV4_ERR_WORKSPACE                         # misaligned workspace
+    assert B.lib().dsv4_mx_linear(x.data_ptr(), 0, 256, wp.data_ptr(), 48, None, 0, None, B.DSV4_DT_F32,
+                                  None) == B.DSV4_OK            # empty batch
+    torch.cuda.synchronize()
+
+
+def _q_proj(cfg, x, dc, wdq_p, wuq_p, act):
+    T, hidden = x.shape
+    ws = torch.empty(B.dsv4_index_q_proj_ws_bytes(cfg, T, hidden, dc), dtype=torch.uint8, device=DEV)
+    qI = torch.empty((T, cfg.idx_heads, cfg.idx_dim), dtype=act, device=DEV)
+    B.dsv4_index_q_proj(cfg, x, dc, wdq_p, wuq_p, ws, qI)
+    torch.cuda.synchronize()
+    cq = ws[: T * dc * 2].view(torch.bfloat16).view(T, dc)
+    return cq, qI
+
+
+def _check_q_proj(x, cq, qI, wdq, wuq, rows):
+    """Stage 1: the GPU's bf16 summary against the oracle's fp64 sum: equal to it
+    rounded to bf16 but for a few elements near a rounding boundary (or, after
+    cancellation, near zero), and always within half a bf16 step plus the
+    summation bound.  Stage 2 from the GPU's summary
+    (so a one-step difference upstream does not blur it): the summation bound."""
+    xs = _f64(x[rows])
+    ref1 = O.mx_linear(xs, _f64(wdq))
+    ref1b = torch.from_numpy(ref1).to(torch.bfloat16).to(torch.float64).numpy()
+    c = _f64(cq[rows])
+    diff = c != ref1b
+    assert diff.mean() <= 1e-2, diff.mean()
+    # the GPU's sum within the summation bound, then rounded to bf16 (half a step)
+    assert (np.abs(c - ref1) <= 2.0 ** -8 * np.abs(ref1) + TOL * (np.abs(O.mxfp8_rows(xs)) @
+                                                                      np.abs(O.mxfp4_rows(_f64(wdq))).T)).all()
+    q = _f64(qI[rows]).reshape(len(rows), -1)
+    ref2 = O.mx_linear(c, _f64(wuq))
+    mag = np.abs(O.mxfp8_rows(c)) @ np.abs(O.mxfp4_rows(_f64(wuq))).T
+    ratio = np.abs(q - ref2) / (TOL * mag + 1e-37)
+    print(f"  summaries differing: {diff.sum()} of {diff.size}; stage-2 err / bound {ratio.max():.3f}", flush=True)
+    assert ratio.max() <= 1.0
+
+
+def test_index_q_proj_tiny():
+    """Tiny indexer (4 heads x 32) on hidden 256 -> d_c 128, both tilings."""
+    cfg, oc = Hh.cfgs(dict(synth.TINY_CSA.shape()), act=B.DSV4_DT_F32)
+    assert (oc.idx_heads, oc.idx_dim) == (4, 32)
+    hidden, dc = 256, 128
+    g = np.random.default_rng(11)
+    wdq = _bf16(g.standard_normal((dc, hidden)) / 16)
+    wuq = _bf16(g.standard_normal((4 * 32, dc)) / 11)
+    wdq_p, wuq_p = _pack(wdq), _pack(wuq)
+    for T in (3, 100):
+        x = _bf16(g.standard_normal((T, hidden)))
+        cq, qI = _q_proj(cfg, x, dc, wdq_p, wuq_p, torch.float32)
+        _check_q_proj(x, cq, qI, wdq, wuq, list(range(T)))
+
+
+def test_index_q_proj_production_shape():
+    """x [T, 7168] -> d_c 1024 -> 64 x 128, at a decode batch (32) and a prefill
+    chunk (8192 tokens, sampled rows), and bitwise the same for the same tokens
+    in both."""
+    cfg, oc = Hh.cfgs(dict(synth.CSA_DECODE_128K.shape()), act=B.DSV4_DT_F32)
+    hidden, dc = 7168, 1024
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    wdq = (torch.randn((dc, hidden), generator=g, device=DEV) / hidden ** 0.5).to(torch.bfloat16)
+    wuq = (torch.randn((cfg.idx_heads * cfg.idx_dim, dc), generator=g, device=DEV) / dc ** 0.5).to(torch.bfloat16)
+    wdq_p, wuq_p = _pack(wdq), _pack(wuq)
+    x = torch.randn((8192, hidden), generator=g, device=DEV).to(torch.bfloat16)
+    cq, qI = _q_proj(cfg, x, dc, wdq_p, wuq_p, torch.float32)
+    rows = [0, 1, 777, 4096, 8191]
+    _check_q_proj(x, cq, qI, wdq, wuq, rows)
+    cq_s, qI_s = _q_proj(cfg, x[4000:4032].contiguous(), dc, wdq_p, wuq_p, torch.float32)
+    _check_q_proj(x[4000:4032], cq_s, qI_s, wdq, wuq, [0, 31])
+    assert torch.equal(qI_s.view(torch.int32), qI[4000:4032].view(torch.int32))
+    assert torch.equal(cq_s.view(torch.int16), cq[4000:4032].view(torch.int16))
+    # bf16 query output (the act dtype the scorer takes at bf16): the fp32 result rounded
+    cfgb, _ = Hh.cfgs(dict(synth.CSA_DECODE_128K.shape()), act=B.DSV4_DT_BF16)
+    _, qIb = _q_proj(cfgb, x[4000:4032].contiguous(), dc, wdq_p, wuq_p, torch.bfloat16)
+    assert torch.equal(qIb.view(torch.int16), qI_s.to(torch.bfloat16).view(torch.int16))
