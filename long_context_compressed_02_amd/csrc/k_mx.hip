@@ -140,20 +140,44 @@ struct MxArgs {
     int64_t ldc;
     int M, N, K;
     int c_f32;
+    int tiles_x, tiles_y;   // column / row tiles
+    int chunk_w;            // column tiles per chunk of the tile order
 };
+
+// Workgroup -> tile.  Workgroups are dealt to the 8 XCDs in turn (id % 8), and
+// each XCD has its own L2 (4 MB).  The tiles are ordered in column chunks --
+// chunk_w column tiles, whose weights fit one L2 -- and row-major inside a
+// chunk; XCD x takes the x-th run of consecutive tiles in that order.  So the
+// workgroups sharing an L2 sweep a chunk's column tiles over a few row tiles:
+// each row tile's activations are fetched into one L2 per chunk, and the
+// chunk's weights stay resident there.
+__device__ __forceinline__ bool mx_tile(const MxArgs &G, int id, int &ty, int &tx) {
+    const int tiles = G.tiles_x * G.tiles_y;
+    const int per = (tiles + 7) / 8;
+    const int t = (id % 8) * per + id / 8;
+    if (t >= tiles) return false;
+    const int chunk = t / (G.chunk_w * G.tiles_y);
+    const int r = t - chunk * G.chunk_w * G.tiles_y;
+    const int w = min(G.chunk_w, G.tiles_x - chunk * G.chunk_w);   // the last chunk may be narrower
+    ty = r / w;
+    tx = chunk * G.chunk_w + r % w;
+    return true;
+}
 
 // WM x WN 16x16 blocks per wave, WGM x WGN waves per workgroup (4 in all), D
 // k-steps of loads in flight.
 template <int WM, int WN, int WGM, int WGN, int D>
 __global__ __launch_bounds__(256) void k_mx_gemm(MxArgs G) {
     static_assert(WGM * WGN == 4, "four waves");
+    int ty, tx;
+    if (!mx_tile(G, blockIdx.x, ty, tx)) return;      // (whole workgroup: the grid is rounded up to 8)
     const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     const int nks = G.K / 128, nq = (nks + 3) / 4;
     const int rbs = (G.M + 15) / 16, cbs = G.N / 16;
-    const int rb0 = blockIdx.y * (WGM * WM) + wm * WM;
-    const int cb0 = blockIdx.x * (WGN * WN) + wn * WN;
+    const int rb0 = ty * (WGM * WM) + wm * WM;
+    const int cb0 = tx * (WGN * WN) + wn * WN;
     // blocks past the matrix read the last one (their results are not stored)
     const uint8_t *ap[WM];
     const uint8_t *bp[WN];
@@ -254,18 +278,25 @@ hipError_t launch_mx_quant(const uint16_t *X, int rows, int K, bool fp8, uint8_t
     return hipGetLastError();
 }
 
+template <int WM, int WN, int WGM, int WGN, int D>
+static void launch_tiled(MxArgs G, hipStream_t s) {
+    const int rbs = (G.M + 15) / 16, cbs = G.N / 16;
+    G.tiles_x = (cbs + WGN * WN - 1) / (WGN * WN);
+    G.tiles_y = (rbs + WGM * WM - 1) / (WGM * WM);
+    // weights of one column tile (codes and scales), chunks of at most 4 MB
+    const int64_t tile_b = (int64_t)WGN * WN * (G.K / 128) * 1024 + (int64_t)WGN * WN * ((G.K / 128 + 3) / 4) * 256;
+    const int64_t nchunks = (tile_b * G.tiles_x + (4 << 20) - 1) / (4 << 20);
+    G.chunk_w = (int)((G.tiles_x + nchunks - 1) / nchunks);
+    const int tiles = G.tiles_x * G.tiles_y;
+    hipLaunchKernelGGL((k_mx_gemm<WM, WN, WGM, WGN, D>), dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0, s, G);
+}
+
 hipError_t launch_mx_gemm(const uint8_t *A, const uint8_t *Bp, int M, int N, int K, void *C, int64_t ldc, int c_f32,
                           hipStream_t s) {
-    MxArgs G{A, Bp, C, mx_code_bytes(M, K, true), mx_code_bytes(N, K, false), ldc, M, N, K, c_f32};
-    const int rbs = (M + 15) / 16, cbs = N / 16;
-    if (M <= 32) {
-        hipLaunchKernelGGL((k_mx_gemm<2, 1, 1, 4, 8>), dim3((unsigned)((cbs + 3) / 4)), dim3(256), 0, s, G);
-    } else if (M <= kMxSmallRows) {
-        hipLaunchKernelGGL((k_mx_gemm<4, 1, 1, 4, 8>), dim3((unsigned)((cbs + 3) / 4)), dim3(256), 0, s, G);
-    } else {
-        dim3 grid((unsigned)((cbs + 7) / 8), (unsigned)((rbs + 7) / 8));
-        hipLaunchKernelGGL((k_mx_gemm<4, 4, 2, 2, 2>), grid, dim3(256), 0, s, G);
-    }
+    MxArgs G{A, Bp, C, mx_code_bytes(M, K, true), mx_code_bytes(N, K, false), ldc, M, N, K, c_f32, 0, 0, 0};
+    if (M <= 32) launch_tiled<2, 1, 1, 4, 8>(G, s);
+    else if (M <= kMxSmallRows) launch_tiled<4, 1, 1, 4, 8>(G, s);
+    else launch_tiled<4, 4, 2, 2, 2>(G, s);
     return hipGetLastError();
 }
 
