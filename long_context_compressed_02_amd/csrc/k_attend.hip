@@ -658,6 +658,19 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     const int qi = (u8 / A.nhg) * 8 + x8;
     const int hg = u8 % A.nhg;
     if (qi >= A.nq) return;
+    // (CSA) the top-k indices of this wave's first resolution batch depend on
+    // the query row alone: read them now, beside the request and position,
+    // instead of one round trip later (the row has topk entries; positions
+    // past it are clamped, and only positions inside the list are used)
+    int32_t jpre[RES];
+    if constexpr (CSA) {
+#pragma unroll
+        for (int u = 0; u < RES; ++u) {
+            const int e = 64 * u + lane;
+            const int p = (sw + kSubsets * (e >> 5)) * kChunk + (e & 31);
+            jpre[u] = A.topk[(int64_t)qi * L.topk + (p < L.topk ? p : L.topk - 1)];
+        }
+    }
     const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
     if (!Q.ok) return;
     const int head = hg * 16 + c16;
@@ -718,7 +731,7 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
 #pragma unroll
                     for (int u = 0; u < RES; ++u) {
                         const int64_t pc = p[u] < n_ent ? p[u] : (n_ent > 0 ? n_ent - 1 : 0);
-                        j[u] = A.topk[(int64_t)Q.qrow * L.topk + pc];
+                        j[u] = e0 == 0 ? jpre[u] : A.topk[(int64_t)Q.qrow * L.topk + pc];
                     }
                 }
 #pragma unroll
