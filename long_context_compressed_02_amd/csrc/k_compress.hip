@@ -173,12 +173,28 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
     __shared__ float pooled[D + 128];
     __shared__ float2 cs_tab[DR / 2];                // cos/sin of position t (window record and entry)
     const int b = blockIdx.x;
-    const int r = req[b];
-    const int64_t t = pos[b];
-    if (r < 0 || r >= C.n_req || t < 0 || t >= (int64_t)C.max_blocks * kBlockTokens) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const bool csa = L.kind == DSV4_CSA;
     const int dI = csa ? L.dI : 0;
+    // the new token's channels depend on the batch slot alone: loaded first,
+    // beside the request and position (one memory round trip less), channel
+    // c = tid + 256u of [kv D][gate D][kI dI][gI dI]
+    auto in_tok = [&](int c) {
+        if (c < D) return load_act(kv, (int64_t)b * D + c, L.act);
+        if (c < 2 * D) return load_act(gate, (int64_t)b * D + c - D, L.act);
+        if (c < 2 * D + dI) return load_act(kI, (int64_t)b * dI + c - 2 * D, L.act);
+        return load_act(gI, (int64_t)b * dI + c - 2 * D - dI, L.act);
+    };
+    constexpr int U = (kStageFloats + 255) / 256;
+    float vn[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = tid + 256 * u;
+        vn[u] = c < L.pend_tok_floats ? in_tok(c) : 0.0f;
+    }
+    const int r = req[b];
+    const int64_t t = pos[b];
+    if (r < 0 || r >= C.n_req || t < 0 || t >= (int64_t)C.max_blocks * kBlockTokens) return;
     uint8_t *st = state_ptr(L, C, r);
     float *pend = (float *)(st + L.pend_off);
     const int ptf = L.pend_tok_floats;               // [kv D][gate D][kI dI][gI dI]
@@ -200,14 +216,7 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
         cs_tab[tid - 192] = make_float2(c, sn);
     }
     // 2. one batch of loads into LDS: token slot s of the window (the new one
-    // last), channel c = tid + 256u
-    auto in_tok = [&](int c) {
-        if (c < D) return load_act(kv, (int64_t)b * D + c, L.act);
-        if (c < 2 * D) return load_act(gate, (int64_t)b * D + c - D, L.act);
-        if (c < 2 * D + dI) return load_act(kI, (int64_t)b * dI + c - 2 * D, L.act);
-        return load_act(gI, (int64_t)b * dI + c - 2 * D - dI, L.act);
-    };
-    constexpr int U = (kStageFloats + 255) / 256;
+    // last; its channels were loaded above), channel c = tid + 256u
     {
         const int nold = staged ? n - 1 : 0;         // older window tokens staged
         float v[kStageWin][U];
@@ -221,12 +230,6 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
                     v[s][u] = c < ptf ? src[c] : 0.0f;
                 }
             }
-        }
-        float vn[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = tid + 256 * u;
-            vn[u] = c < ptf ? in_tok(c) : 0.0f;
         }
 #pragma unroll
         for (int s = 0; s < kStageWin; ++s)
