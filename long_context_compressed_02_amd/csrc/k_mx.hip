@@ -64,21 +64,25 @@ __device__ __forceinline__ int mx8_exponent(float amax) {
 // One thread per (16-row block, group of four k-steps, lane (g, c)):
 // quantises row c's block g (k = 32g .. 32g+31) of each of the four k-steps,
 // writes the codes where the operand order puts them and the lane's scale word.
-template <bool F8>
+// STEP1 (small inputs): one thread per (16-row block, k-step, lane) instead,
+// writing its scale byte alone -- four times the threads, one memory round
+// trip each (the threads of the padding k-steps of the last group write 0x7f).
+template <bool F8, bool STEP1>
 __global__ __launch_bounds__(256) void k_mx_quant(const uint16_t *X, int rows, int K, uint8_t *P, int64_t total) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     const int lane = (int)(i & 63), g = lane >> 4;
     const int nks = K / 128, nq = (nks + 3) / 4;
     const int64_t t = i >> 6;
-    const int kq = (int)(t % nq);
-    const int64_t rb = t / nq;
+    const int kq = STEP1 ? (int)(t % (4 * nq)) / 4 : (int)(t % nq);
+    const int64_t rb = STEP1 ? t / (4 * nq) : t / nq;
     const int64_t row = rb * 16 + (lane & 15);
     const bool live = row < rows;
     uint8_t *scales = P + mx_code_bytes(rows, K, F8);
     uint32_t sw = 0x7f7f7f7fu;
+    const int j_lo = STEP1 ? (int)(t % 4) : 0, j_hi = STEP1 ? j_lo + 1 : 4;
 #pragma unroll 1
-    for (int j = 0; j < 4; ++j) {
+    for (int j = j_lo; j < j_hi; ++j) {
         const int ks = 4 * kq + j;
         if (ks >= nks) break;
         u32x4 raw[4] = {};
@@ -129,7 +133,10 @@ __global__ __launch_bounds__(256) void k_mx_quant(const uint16_t *X, int rows, i
             *(u32x4 *)(P + (rb * nks + ks) * 1024 + 16 * lane) = c;
         }
     }
-    ((uint32_t *)(scales + (rb * nq + kq) * 256))[lane] = sw;
+    if constexpr (STEP1)
+        scales[(rb * nq + kq) * 256 + 4 * lane + j_lo] = (uint8_t)(sw >> (8 * j_lo));
+    else
+        ((uint32_t *)(scales + (rb * nq + kq) * 256))[lane] = sw;
 }
 
 struct MxArgs {
@@ -272,9 +279,14 @@ constexpr int kMxSmallRows = 64;
 
 hipError_t launch_mx_quant(const uint16_t *X, int rows, int K, bool fp8, uint8_t *P, hipStream_t s) {
     const int nq = (K / 128 + 3) / 4;
-    const int64_t total = (int64_t)((rows + 15) / 16) * nq * 64;
-    if (fp8) hipLaunchKernelGGL(k_mx_quant<true>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, X, rows, K, P, total);
-    else hipLaunchKernelGGL(k_mx_quant<false>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, X, rows, K, P, total);
+    const int64_t rb = (rows + 15) / 16;
+    const bool step1 = rows <= 256;                  // small inputs: more threads, one round trip
+    const int64_t total = rb * nq * 64 * (step1 ? 4 : 1);
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (fp8 && step1) hipLaunchKernelGGL((k_mx_quant<true, true>), grid, dim3(256), 0, s, X, rows, K, P, total);
+    else if (fp8) hipLaunchKernelGGL((k_mx_quant<true, false>), grid, dim3(256), 0, s, X, rows, K, P, total);
+    else if (step1) hipLaunchKernelGGL((k_mx_quant<false, true>), grid, dim3(256), 0, s, X, rows, K, P, total);
+    else hipLaunchKernelGGL((k_mx_quant<false, false>), grid, dim3(256), 0, s, X, rows, K, P, total);
     return hipGetLastError();
 }
 
