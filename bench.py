@@ -601,8 +601,8 @@ def decode_mix_main(a):
                                 if pair else f"V4 HCA layer decode, batch {Bsz} x {ctxs[0] // 1024}K"),
                    "batch": Bsz, "ctx": ctxs, "topk": k if pair else None, "heads": H, "d": d, "policy": a.policy},
         "roofline": roof,
-        "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items()},
-        "launches_per_step": {n_: v["launches"] / steps for n_, v in kern.items()},
+        "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items() if v["launches"]},
+        "launches_per_step": {n_: v["launches"] / steps for n_, v in kern.items() if v["launches"]},
         "attend_TFLOPs": round(att_tf, 1), "attend_GBps": round(att_gbs, 1),
         "setup_s": round(t_setup, 1),
     }
