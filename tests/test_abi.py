@@ -154,3 +154,50 @@ def test_status_strings_and_timers():
     B.dsv4_timer_enable(B.DSV4_K_ATTEND, True)
     assert B.dsv4_timer_read(B.DSV4_K_ATTEND) == (0.0, 0)
     B.dsv4_timer_enable(B.DSV4_K_ATTEND, False)
+
+
+def test_mx_pack_sizes_follow_the_documented_layout():
+    """Packed bytes = (16-row blocks) x (128-wide k-steps) x (1 KB FP4 | 2 KB FP8)
+    + (16-row blocks) x (groups of four k-steps) x 256 B of scale words."""
+    def expect(rows, K, fp8):
+        rb, nks = (rows + 15) // 16, K // 128
+        return rb * nks * (2048 if fp8 else 1024) + rb * ((nks + 3) // 4) * 256
+    for rows, K, fp8 in [(8192, 7168, 1), (1024, 7168, 0), (8192, 1024, 0), (1, 128, 1), (17, 384, 0), (0, 256, 1)]:
+        assert B.dsv4_mx_pack_bytes(rows, K, bool(fp8)) == expect(rows, K, fp8)
+    assert B.dsv4_mx_pack_bytes(1024, 7168, False) == 3899392         # the 7168 -> 1024 query map
+    for rows, K in [(-1, 128), (16, 100), (16, 0)]:
+        with pytest.raises(B.Dsv4Error) as e:
+            B.dsv4_mx_pack_bytes(rows, K, True)
+        assert e.value.status == B.DSV4_ERR_INVALID_ARG
+
+
+def test_mx_linear_rejects_bad_arguments_before_launch():
+    L = B.lib()
+    ws_ok = B.dsv4_mx_pack_bytes(4, 256, True)
+    call = lambda M, K, N, ws, wsb, dt: L.dsv4_mx_linear(FAKE, M, K, FAKE, N, ws, wsb, FAKE, dt, None)
+    assert call(4, 200, 48, FAKE, ws_ok, B.DSV4_DT_F32) == B.DSV4_ERR_INVALID_ARG      # K % 128
+    assert call(4, 256, 40, FAKE, ws_ok, B.DSV4_DT_F32) == B.DSV4_ERR_INVALID_ARG      # N % 16
+    assert call(-1, 256, 48, FAKE, ws_ok, B.DSV4_DT_F32) == B.DSV4_ERR_INVALID_ARG     # M < 0
+    assert call(4, 256, 48, FAKE, ws_ok, 7) == B.DSV4_ERR_INVALID_ARG                  # output dtype
+    assert call(4, 256, 48, FAKE, ws_ok - 1, B.DSV4_DT_F32) == B.DSV4_ERR_WORKSPACE    # small workspace
+    assert call(4, 256, 48, FAKE + 16, ws_ok, B.DSV4_DT_F32) == B.DSV4_ERR_WORKSPACE   # misaligned
+    assert call(4, 256, 48, None, 0, B.DSV4_DT_F32) == B.DSV4_ERR_WORKSPACE            # none
+    assert call(0, 256, 48, None, 0, B.DSV4_DT_F32) == B.DSV4_OK                       # empty batch
+    assert L.dsv4_mx_linear(FAKE + 8, 4, 256, FAKE, 48, FAKE, ws_ok, FAKE, B.DSV4_DT_F32, None) == \
+        B.DSV4_ERR_INVALID_ARG                                                          # x misaligned
+    assert L.dsv4_mx_pack_weight(FAKE, 40, 256, FAKE, 1 << 30, None) == B.DSV4_ERR_INVALID_ARG
+    assert L.dsv4_mx_pack_weight(FAKE, 48, 256, FAKE, 16, None) == B.DSV4_ERR_WORKSPACE
+
+
+def test_index_q_proj_workspace_and_checks():
+    cfg = B.make_cfg()                                        # 64 index heads x 128
+    T, hidden, dc = 32, 7168, 1024
+    need = B.dsv4_index_q_proj_ws_bytes(cfg, T, hidden, dc)
+    cq = (T * dc * 2 + 255) // 256 * 256
+    assert need == cq + max(B.dsv4_mx_pack_bytes(T, hidden, True), B.dsv4_mx_pack_bytes(T, dc, True))
+    L = B.lib()
+    args = lambda ws, wsb, hid=hidden, d=dc: (ctypes.byref(cfg), FAKE, T, hid, d, FAKE, FAKE, ws, wsb, FAKE, None)
+    assert L.dsv4_index_q_proj(*args(FAKE, need - 1)) == B.DSV4_ERR_WORKSPACE
+    assert L.dsv4_index_q_proj(*args(FAKE + 128, need)) == B.DSV4_ERR_WORKSPACE
+    assert L.dsv4_index_q_proj(*args(FAKE, need, hid=7000)) == B.DSV4_ERR_INVALID_ARG
+    assert L.dsv4_index_q_proj(*args(FAKE, need, d=1000)) == B.DSV4_ERR_INVALID_ARG
