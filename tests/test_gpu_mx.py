@@ -95,7 +95,7 @@ def test_mx_linear_small_ragged(K):
     N = 48                                            # 3 column blocks: a ragged column tile
     w = _bf16(g.standard_normal((N, K)) / np.sqrt(K))
     wp = _pack(w)
-    for M in (1, 20, 37, 64, 300):                    # every tiling, ragged row counts
+    for M in (1, 20, 37, 64, 256, 257, 300):          # every tiling and quantiser split, ragged rows
         x = g.standard_normal((M, K)).astype(np.float32) * g.lognormal(0, 2, (M, 1)).astype(np.float32)
         x[M // 2] = 0.0                               # a zero row
         if M > 2:
