@@ -66,7 +66,7 @@ def main():
     if a.batch is None:
         a.batch = 8192 if a.workload == "index_q" else 32
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1", "n_gpus": a.gpus}))
         sys.exit(2)
     if a.workload == "prefill":
         return prefill_main(a)
