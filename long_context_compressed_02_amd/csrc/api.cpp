@@ -65,15 +65,15 @@ dsv4_status check_cache(const Lay &L, const dsv4_cache *C, int kind) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 int num_cus() {
-    static int cus = 0;
-    if (!cus) {
+    // (a function-local static: initialised once, thread-safe, on the device
+    // current at the first call)
+    static const int cus = [] {
         int dev = 0;
         hipDeviceProp_t prop;
         if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-            cus = prop.multiProcessorCount;
-        else
-            cus = 256;
-    }
+            return prop.multiProcessorCount;
+        return 256;
+    }();
     return cus;
 }
 
