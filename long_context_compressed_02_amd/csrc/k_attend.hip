@@ -43,6 +43,8 @@
 
 #include "launch.h"
 
+#include <mutex>
+
 namespace dsv4 {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1125,16 +1127,31 @@ int64_t attend_lds_max(const Lay &L, int64_t list_max) {
     return lo > hi ? lo : hi;
 }
 
+// Raise a kernel's dynamic-LDS limit to at least `bytes`.  The limit only
+// grows (under a lock: callers on several threads never lower it under a
+// launch that needs more); one record per kernel, the last 16 kernels.
+static hipError_t raise_lds_limit(const void *fn, int64_t bytes) {
+    static std::mutex mu;
+    static const void *fns[16] = {};
+    static int64_t lim[16] = {};
+    std::lock_guard<std::mutex> lk(mu);
+    int i = 0;
+    while (i < 16 && fns[i] && fns[i] != fn) ++i;
+    if (i == 16) i = 15;                             // (more kernels than slots: reuse the last)
+    if (fns[i] == fn && lim[i] >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    if (fns[i] != fn) lim[i] = 0;
+    fns[i] = fn;
+    lim[i] = bytes > lim[i] ? bytes : lim[i];
+    return hipSuccess;
+}
+
 template <int D, int DR, int NSW, bool CSA, bool PREFILL>
 static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
     const int64_t lds = attend_lds_bytes<D, DR, NSW>(attend_list_max(A.L, A.C, CSA));
-    static int64_t attr = -1;
-    if (attr < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_attend<D, DR, NSW, CSA, PREFILL>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = lds;
-    }
+    hipError_t e = raise_lds_limit((const void *)k_attend<D, DR, NSW, CSA, PREFILL>, lds);
+    if (e != hipSuccess) return e;
     const int groups = (A.nq + 7) / 8;
     hipLaunchKernelGGL((k_attend<D, DR, NSW, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kParts * NSW),
                        (size_t)lds, s, A);
@@ -1144,13 +1161,8 @@ static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
 template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_lo(const AttnArgs &A, hipStream_t s) {
     const int64_t lds = attend_lo_lds_bytes<D, DR>(attend_list_max(A.L, A.C, CSA));
-    static int64_t attr = -1;
-    if (attr < lds) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_attend_lo<D, DR, CSA, PREFILL>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr = lds;
-    }
+    hipError_t e = raise_lds_limit((const void *)k_attend_lo<D, DR, CSA, PREFILL>, lds);
+    if (e != hipSuccess) return e;
     const int groups = (A.nq + 7) / 8;
     hipLaunchKernelGGL((k_attend_lo<D, DR, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kSubsets), (size_t)lds,
                        s, A);
