@@ -421,6 +421,9 @@ dsv4_status dsv4_cache_write_entries(const dsv4_cfg *cfg, const dsv4_cache *cach
  * Blocks the table does not map are dumped as zeros and skipped on reload.
  *   buf_dev  device memory of at least dsv4_cache_dump_bytes bytes, 16-byte aligned
  *   (a host copy of it -- disk -- is the caller's)
+ * n_tokens >= 1 with ceil(n_tokens / 128) <= the cache's max_blocks, and
+ * 0 <= req < n_req; DSV4_ERR_INVALID_ARG otherwise, and for a missing, short
+ * or misaligned buffer (nothing is copied then).
  */
 dsv4_status dsv4_cache_dump_bytes(const dsv4_cfg *cfg, int32_t kind, int32_t n_tokens, int64_t *out);
 dsv4_status dsv4_cache_dump(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t n_tokens,

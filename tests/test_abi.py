@@ -201,3 +201,38 @@ def test_index_q_proj_workspace_and_checks():
     assert L.dsv4_index_q_proj(*args(FAKE + 128, need)) == B.DSV4_ERR_WORKSPACE
     assert L.dsv4_index_q_proj(*args(FAKE, need, hid=7000)) == B.DSV4_ERR_INVALID_ARG
     assert L.dsv4_index_q_proj(*args(FAKE, need, d=1000)) == B.DSV4_ERR_INVALID_ARG
+
+
+def test_cache_dump_sizes_and_checks():
+    """Dump size = state bytes + ceil(n/128) x (entry block + index block);
+    bad requests, lengths and buffers are rejected before any copy."""
+    cfg = B.make_cfg()
+    for kind in (B.DSV4_CSA, B.DSV4_HCA):
+        lay = B.dsv4_get_layout(cfg, kind)
+        for n in (1, 128, 129, 131072):
+            nb = (n + 127) // 128
+            assert B.dsv4_cache_dump_bytes(cfg, kind, n) == lay.state_bytes + nb * (
+                lay.entry_block_bytes + lay.index_block_bytes)
+        with pytest.raises(B.Dsv4Error) as e:
+            B.dsv4_cache_dump_bytes(cfg, kind, 0)
+        assert e.value.status == B.DSV4_ERR_INVALID_ARG
+    L = B.lib()
+    c = _fake_cache()                                         # 4 requests, 16 blocks each
+    need = B.dsv4_cache_dump_bytes(cfg, B.DSV4_CSA, 700)
+    ok = lambda req, n, buf, nbytes, f=L.dsv4_cache_dump: f(ctypes.byref(cfg), ctypes.byref(c), req, n, buf, nbytes,
+                                                             None)
+    for f in (L.dsv4_cache_dump, L.dsv4_cache_load):
+        assert ok(0, 0, FAKE, need, f) == B.DSV4_ERR_INVALID_ARG           # no tokens
+        assert ok(4, 700, FAKE, need, f) == B.DSV4_ERR_INVALID_ARG         # request out of range
+        assert ok(-1, 700, FAKE, need, f) == B.DSV4_ERR_INVALID_ARG
+        assert ok(0, 16 * 128 + 1, FAKE, 1 << 40, f) == B.DSV4_ERR_INVALID_ARG   # past the block table
+        assert ok(0, 700, FAKE, need - 16, f) == B.DSV4_ERR_INVALID_ARG    # buffer too small
+        assert ok(0, 700, FAKE + 8, need, f) == B.DSV4_ERR_INVALID_ARG     # buffer misaligned
+        assert ok(0, 700, None, need, f) == B.DSV4_ERR_INVALID_ARG
+
+
+def test_projection_empty_batches_are_no_ops():
+    L = B.lib()
+    cfg = B.make_cfg()
+    assert L.dsv4_out_proj(ctypes.byref(cfg), 16, 1024, 7168, None, None, None, None, None, 0, None) == B.DSV4_OK
+    assert L.dsv4_index_q_proj(ctypes.byref(cfg), None, 0, 7168, 1024, None, None, None, 0, None, None) == B.DSV4_OK
