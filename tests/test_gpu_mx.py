@@ -217,3 +217,43 @@ def test_index_q_proj_production_shape():
     cfgb, _ = Hh.cfgs(dict(synth.CSA_DECODE_128K.shape()), act=B.DSV4_DT_BF16)
     _, qIb = _q_proj(cfgb, x[4000:4032].contiguous(), dc, wdq_p, wuq_p, torch.bfloat16)
     assert torch.equal(qIb.view(torch.int16), qI_s.to(torch.bfloat16).view(torch.int16))
+
+
+def test_index_q_proj_feeds_the_indexer():
+    """The query path's output, in its [T][heads][dims] bf16 layout, is what the
+    decode indexer takes: the top-k of the path's queries equals the oracle's
+    selection computed from the same queries (read back) over the same keys."""
+    k = 1024
+    shape = dict(synth.CSA_DECODE_128K.shape())
+    cfg, oc = Hh.cfgs(shape, topk=k)                          # bf16 activations, FP8 index rows
+    ctx = [5000, 40001]
+    bt, nb, mb = Hh.block_table(ctx, extra_blocks=3, seed=4)
+    cache = B.LayerCache(cfg, B.DSV4_CSA, len(ctx), mb, nb, bt)
+    keys = []
+    for r, c in enumerate(ctx):
+        n = c // 4
+        kv = synth.index_keys(synth.CSA_DECODE_128K, 70 + r, n)[:n]
+        keys.append(O.store_index_rows(kv, oc))
+        B.dsv4_cache_write_entries(cfg, cache, B.DSV4_TARGET_INDEX_KEY, Hh.i32([r] * n), Hh.i32(range(n)),
+                                   torch.from_numpy(kv).to(DEV))
+    hidden, dc = 7168, 1024
+    g = torch.Generator(device=DEV)
+    g.manual_seed(23)
+    wdq = (torch.randn((dc, hidden), generator=g, device=DEV) / hidden ** 0.5).to(torch.bfloat16)
+    wuq = (torch.randn((oc.idx_heads * oc.idx_dim, dc), generator=g, device=DEV) / dc ** 0.5).to(torch.bfloat16)
+    x = torch.randn((len(ctx), hidden), generator=g, device=DEV).to(torch.bfloat16)
+    _, qI = _q_proj(cfg, x, dc, _pack(wdq), _pack(wuq), torch.bfloat16)
+    w = torch.rand((len(ctx), oc.idx_heads), generator=g, device=DEV) / 8
+    out = torch.empty((len(ctx), k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(B.dsv4_workspace_bytes(cfg, len(ctx), cache.c.max_blocks * 32), dtype=torch.uint8, device=DEV)
+    pos = [c - 1 for c in ctx]
+    B.dsv4_index_topk_decode(cfg, cache, qI, w, Hh.i32(range(len(ctx))), Hh.i32(pos), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    qx = qI.to(torch.float64).cpu().numpy()
+    wx = w.to(torch.float64).cpu().numpy()
+    swaps = 0
+    for r in range(len(ctx)):
+        idx, s = O.csa_select(pos[r], qx[r], wx[r], keys[r], oc)
+        swaps += Hh.topk_match(got[r], idx, s, k)
+    assert swaps <= 2
