@@ -66,24 +66,30 @@ typedef int32_t dsv4_status;
 #define DSV4_HCA 1
 
 /* storage formats */
-#define DSV4_STORE_FP32 0        /* records / index keys as fp32 (reference-precision mode) */
+#define DSV4_STORE_FP32 0        /* records / index keys as fp32 (reference-precision mode: plain
+                                    fp32 kernels, both decode policies run the same one) */
 #define DSV4_STORE_FP8 1         /* records: E4M3 non-RoPE dims + one fp32 scale + BF16 RoPE dims;
                                     index keys / queries: E4M3 + one fp32 scale per row */
 #define DSV4_STORE_MXFP4 2       /* index keys / queries only: OCP MXFP4 -- E2M1 codes, one E8M0
                                     (power-of-two) scale per 32 consecutive dims */
 
-/* activation dtypes */
+/* activation dtypes (DSV4_DT_F64: read-back output only) */
 #define DSV4_DT_F32 0
 #define DSV4_DT_BF16 1
+#define DSV4_DT_F64 2
 
 /* decode kernel policy (the two kernels give bitwise identical results) */
 #define DSV4_POLICY_AUTO 0
-#define DSV4_POLICY_HI 1         /* one workgroup per query, all heads: for a saturated GPU */
-#define DSV4_POLICY_LO 2         /* one workgroup per (query, 16-head group): for an unsaturated GPU */
+#define DSV4_POLICY_HI 1         /* for a saturated GPU: per (query, 16-head group) one workgroup of
+                                    2 waves (one per half of the dims) taking the record subsets in
+                                    turn, so that several workgroups share a compute unit */
+#define DSV4_POLICY_LO 2         /* for an unsaturated GPU: per (query, 16-head group) one workgroup
+                                    of 4 waves, one per record subset, over all dims */
 
-/* cache-write targets */
+/* cache-write / read-back targets */
 #define DSV4_TARGET_ENTRY 0
 #define DSV4_TARGET_INDEX_KEY 1
+#define DSV4_TARGET_WINDOW 2     /* read-back only: the window-ring record of a position */
 
 /* Raw tokens covered by one classic-cache block: lcm(4, 128). */
 #define DSV4_BLOCK_TOKENS 128
@@ -405,6 +411,30 @@ dsv4_status dsv4_index_q_proj(const dsv4_cfg *cfg, const void *x, int32_t T, int
 dsv4_status dsv4_cache_write_entries(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t target,
                                      const int32_t *req_dev, const int32_t *entry_dev, int32_t n,
                                      const float *values_dev, void *stream);
+
+/*
+ * Dequantised read-back of stored vectors (tests, inspection, a host copy of
+ * a prefix): item i of request req_dev[i] is decoded from its storage format
+ * into out_dev[i][0..dim), fp32 or fp64 (out_dtype DSV4_DT_F32 / DSV4_DT_F64;
+ * fp64 holds every stored value exactly, an E4M3 code times its fp32 scale
+ * included):
+ *   DSV4_TARGET_ENTRY      entry idx_dev[i] of the classic cache, d values as
+ *                          stored (post-RoPE): E4M3 code * record scale for the
+ *                          first d - d_rope dims, the BF16 (or fp32) values after
+ *   DSV4_TARGET_INDEX_KEY  CSA index key idx_dev[i], idx_dim values (E4M3 * key
+ *                          scale, E2M1 * 2^(E8M0 - 127) per 32 dims, or fp32)
+ *   DSV4_TARGET_WINDOW     the window-ring record of position idx_dev[i] (slot
+ *                          idx mod window; whether that slot still holds the
+ *                          position is the caller's to know), d values
+ * Sources: vastsailsolution.com V4 article, the classic-cache paragraph (blocks
+ * of compressed entries), the state-cache paragraph (window records) and the
+ * mixed-precision paragraph (BF16 RoPE dims, FP8 rest).  Items whose request,
+ * index or block is out of range are skipped (their output left untouched).
+ *   out_dev  [n][dim] of out_dtype, device, 16-byte aligned
+ */
+dsv4_status dsv4_cache_read_entries(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t target,
+                                    const int32_t *req_dev, const int32_t *idx_dev, int32_t n, void *out_dev,
+                                    int32_t out_dtype, void *stream);
 
 /*
  * Dump and reload of one request's cache (vastsailsolution.com V4 article,

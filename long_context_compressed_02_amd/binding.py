@@ -21,9 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libdsv4attn.so")
 DSV4_OK, DSV4_ERR_INVALID_ARG, DSV4_ERR_UNSUPPORTED, DSV4_ERR_WORKSPACE, DSV4_ERR_LAUNCH, DSV4_ERR_HIP = range(6)
 DSV4_CSA, DSV4_HCA = 0, 1
 DSV4_STORE_FP32, DSV4_STORE_FP8, DSV4_STORE_MXFP4 = 0, 1, 2
-DSV4_DT_F32, DSV4_DT_BF16 = 0, 1
+DSV4_DT_F32, DSV4_DT_BF16, DSV4_DT_F64 = 0, 1, 2
 DSV4_POLICY_AUTO, DSV4_POLICY_HI, DSV4_POLICY_LO = 0, 1, 2
-DSV4_TARGET_ENTRY, DSV4_TARGET_INDEX_KEY = 0, 1
+DSV4_TARGET_ENTRY, DSV4_TARGET_INDEX_KEY, DSV4_TARGET_WINDOW = 0, 1, 2
 DSV4_BLOCK_TOKENS = 128
 DSV4_K_COMPRESS, DSV4_K_INDEX_SCORE, DSV4_K_TOPK, DSV4_K_ATTEND, DSV4_K_PROJ, DSV4_K_MX, DSV4_K_COUNT = range(7)
 
@@ -35,7 +35,7 @@ EXPORTS = [
     "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
     "dsv4_out_proj_pack", "dsv4_cache_dump_bytes", "dsv4_cache_dump", "dsv4_cache_load",
     "dsv4_mx_pack_bytes", "dsv4_mx_pack_weight", "dsv4_mx_linear", "dsv4_index_q_proj_ws_bytes",
-    "dsv4_index_q_proj",
+    "dsv4_index_q_proj", "dsv4_cache_read_entries",
 ]
 
 
@@ -90,6 +90,7 @@ def lib():
             "dsv4_csa_attend_prefill": [cp, kp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp],
             "dsv4_hca_attend_prefill": [cp, kp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp],
             "dsv4_cache_write_entries": [cp, kp, i32, vp, vp, i32, vp, vp],
+            "dsv4_cache_read_entries": [cp, kp, i32, vp, vp, i32, vp, i32, vp],
             "dsv4_state_write_tokens": [cp, kp, i32, i32, i32, vp, vp, vp, vp, vp],
             "dsv4_topk_rows_ws_bytes": [i32, i32, i32, ctypes.POINTER(i64)],
             "dsv4_topk_rows": [vp, i64, vp, i32, i32, i32, vp, vp, i64, vp],
@@ -234,6 +235,14 @@ def dsv4_hca_attend_prefill(cfg, cache: LayerCache, q, cu_seqlens, req, pos0, to
 def dsv4_cache_write_entries(cfg, cache: LayerCache, target, req, entry, values, stream=None):
     _ck("dsv4_cache_write_entries", lib().dsv4_cache_write_entries(
         ctypes.byref(cfg), ctypes.byref(cache.c), target, _p(req), _p(entry), req.shape[0], _p(values),
+        _stream(stream)))
+
+
+def dsv4_cache_read_entries(cfg, cache: LayerCache, target, req, idx, out, stream=None):
+    """out: float32 or float64 device tensor [n, dim] receiving the decoded stored values."""
+    dt = {torch.float32: DSV4_DT_F32, torch.float64: DSV4_DT_F64}[out.dtype]
+    _ck("dsv4_cache_read_entries", lib().dsv4_cache_read_entries(
+        ctypes.byref(cfg), ctypes.byref(cache.c), target, _p(req), _p(idx), req.shape[0], _p(out), dt,
         _stream(stream)))
 
 

@@ -112,8 +112,6 @@ dsv4_status make_layout(const dsv4_cfg *c, int32_t kind, Lay *out) {
     if (!(c->softmax_scale > 0.0f) || !isfinite(c->softmax_scale)) return DSV4_ERR_INVALID_ARG;
     const bool shape_built = (c->d == 512 && c->d_rope == 64) || (c->d == 64 && c->d_rope == 16);
     if (!shape_built) return DSV4_ERR_UNSUPPORTED;
-    if (c->kv_store != DSV4_STORE_FP8 || (c->idx_store != DSV4_STORE_FP8 && c->idx_store != DSV4_STORE_MXFP4))
-        return DSV4_ERR_UNSUPPORTED;
 
     Lay L;
     memset(&L, 0, sizeof(L));
@@ -243,10 +241,14 @@ static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, cons
     const int64_t need = index_ws_bytes(L, nq, nmax, &W, ws);
     if (need > ws_bytes) return DSV4_ERR_WORKSPACE;
     if (W.s_max > kTkMaxSeg) return DSV4_ERR_UNSUPPORTED;
-    if (L.epb < 16) return DSV4_ERR_UNSUPPORTED;   // scoring reads 16-key runs inside one block
-    hipError_t e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
-    if (e != hipSuccess) return DSV4_ERR_LAUNCH;
-    {
+    hipError_t e;
+    if (L.idx_store == DSV4_STORE_FP32) {          // fp32 rows: the queries are scored as given
+        Timed tm(DSV4_K_INDEX_SCORE, s);
+        e = launch_score_f32(L, *cache, qI, w, req_q, pos_q, nq, W, s);
+    } else {
+        if (L.epb < 16) return DSV4_ERR_UNSUPPORTED;   // scoring reads 16-key runs inside one block
+        e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
+        if (e != hipSuccess) return DSV4_ERR_LAUNCH;
         Timed tm(DSV4_K_INDEX_SCORE, s);
         e = prefill ? launch_score_prefill(L, *cache, req_q, pos_q, nq, W, s)
                     : launch_score_decode(L, *cache, req_q, pos_q, nq, W, s);
@@ -380,6 +382,10 @@ static dsv4_status attend_common(const dsv4_cfg *cfg, const dsv4_cache *cache, i
     A.out = out;
     A.nq = nq;
     A.nhg = (L.H + 15) / 16;
+    if (L.kv_store == DSV4_STORE_FP32) {           // fp32 records: one kernel for both policies
+        Timed tm(DSV4_K_ATTEND, S(stream));
+        return hip_status(launch_attend_f32(A, kind == DSV4_CSA, prefill, S(stream)));
+    }
     if (attend_lds_max(L, attend_list_max(L, *cache, kind == DSV4_CSA)) > kLdsMax) return DSV4_ERR_UNSUPPORTED;
     const bool hi = pick_hi(policy, nq, A.nhg);
     Timed tm(DSV4_K_ATTEND, S(stream));
@@ -430,6 +436,25 @@ dsv4_status dsv4_cache_write_entries(const dsv4_cfg *cfg, const dsv4_cache *cach
     if (n == 0) return DSV4_OK;
     if (!req_dev || !entry_dev || !values_dev) return DSV4_ERR_INVALID_ARG;
     return hip_status(launch_write_entries(L, *cache, target, req_dev, entry_dev, n, values_dev, S(stream)));
+}
+
+dsv4_status dsv4_cache_read_entries(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t target,
+                                    const int32_t *req_dev, const int32_t *idx_dev, int32_t n, void *out_dev,
+                                    int32_t out_dtype, void *stream) {
+    if (!cache) return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, cache->kind, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, cache->kind)) != DSV4_OK) return st;
+    if (target != DSV4_TARGET_ENTRY && target != DSV4_TARGET_INDEX_KEY && target != DSV4_TARGET_WINDOW)
+        return DSV4_ERR_INVALID_ARG;
+    if (target == DSV4_TARGET_INDEX_KEY && cache->kind != DSV4_CSA) return DSV4_ERR_INVALID_ARG;
+    if (out_dtype != DSV4_DT_F32 && out_dtype != DSV4_DT_F64) return DSV4_ERR_INVALID_ARG;
+    if (n < 0) return DSV4_ERR_INVALID_ARG;
+    if (n == 0) return DSV4_OK;
+    if (!req_dev || !idx_dev || !out_dev || !aligned16(out_dev)) return DSV4_ERR_INVALID_ARG;
+    return hip_status(launch_read_entries(L, *cache, target, req_dev, idx_dev, n, out_dev,
+                                          out_dtype == DSV4_DT_F64, S(stream)));
 }
 
 dsv4_status dsv4_state_write_tokens(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t req, int32_t pos0,

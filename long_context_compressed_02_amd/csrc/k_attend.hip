@@ -1099,6 +1099,105 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- fp32 records
+// Records stored as d fp32 values (the reference-precision storage mode): one
+// wave per (query, head), lane l holding dims [l*VPL, l*VPL + VPL).  The
+// records are taken one at a time in list order (selected entries ascending,
+// then the window); each logit is the wave's fixed-order sum of its fp32
+// products, and an online softmax (base 2) folds it in.  Nothing depends on
+// the batch or on the decode policy: both policies run this kernel.
+template <int D, int DR, bool CSA, bool PREFILL>
+__global__ __launch_bounds__(256) void k_attend_f32(AttnArgs A) {
+    constexpr int VPL = D / 64;
+    constexpr int DN = D - DR;
+    const Lay &L = A.L;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= (int64_t)A.nq * L.H) return;
+    const int qi = (int)(item / L.H), head = (int)(item % L.H);
+    const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
+    if (!Q.ok) return;
+    const int d0 = lane * VPL;
+    // the query head, rotated at t on its last DR dims (pairs stay in a lane)
+    float q[VPL];
+    const int64_t qb = ((int64_t)Q.qrow * L.H + head) * D + d0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) q[v] = load_act(A.q, qb + v, L.act);
+    if constexpr (VPL >= 2) {
+#pragma unroll
+        for (int v = 0; v < VPL; v += 2)
+            if (d0 + v >= DN) {
+                float c, s;
+                rope_cs(L, Q.t, (d0 + v - DN) / 2, c, s);
+                const float a = q[v], b = q[v + 1];
+                q[v] = a * c - b * s;
+                q[v + 1] = a * s + b * c;
+            }
+    } else {
+        const float other = __shfl_xor(q[0], 1);
+        if (d0 >= DN) {
+            float c, s;
+            rope_cs(L, Q.t, (d0 - DN) / 2, c, s);
+            q[0] = (lane & 1) == 0 ? q[0] * c - other * s : other * s + q[0] * c;
+        }
+    }
+    const float tau2 = L.tau * 1.4426950408889634f;
+    float m = -INFINITY, l = 0.0f, o[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) o[v] = 0.0f;
+    for (int64_t p = 0; p < Q.n_list; ++p) {
+        const int32_t lc = record_loc<CSA, PREFILL>(A, Q, p);
+        if (lc == kMasked) continue;                       // (wave-uniform)
+        const float *rec = (const float *)loc_addr<PREFILL>(A, Q, lc) + d0;
+        float x[VPL], dot = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            x[v] = rec[v];
+            dot = __builtin_fmaf(q[v], x[v], dot);
+        }
+        // wave sum, fixed tree: row-local shifts, then across rows
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) dot = dot + __shfl_xor(dot, o2);
+        const float lg = tau2 * dot;
+        const float mn = fmaxf(m, lg);
+        const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        const float pe = __builtin_amdgcn_exp2f(lg - mn);
+        l = l * alpha + pe;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) o[v] = o[v] * alpha + pe * x[v];
+        m = mn;
+    }
+    const float z = A.sinks[head] * 1.4426950408889634f;
+    const float M = fmaxf(m, z);
+    const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    const float den = l * f + (z == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(z - M));
+    const float cf = den > 0.0f ? f / den : 0.0f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const float r = o[v] * cf;
+        if (L.act == DSV4_DT_BF16) ((uint16_t *)A.out)[qb + v] = bf16_bits(r);
+        else ((float *)A.out)[qb + v] = r;
+    }
+}
+
+template <int D, int DR>
+static hipError_t launch_f32_t(const AttnArgs &A, bool csa, bool prefill, hipStream_t s) {
+    const dim3 g((unsigned)(((int64_t)A.nq * A.L.H + 3) / 4));
+    if (csa) {
+        if (prefill) hipLaunchKernelGGL((k_attend_f32<D, DR, true, true>), g, dim3(256), 0, s, A);
+        else hipLaunchKernelGGL((k_attend_f32<D, DR, true, false>), g, dim3(256), 0, s, A);
+    } else {
+        if (prefill) hipLaunchKernelGGL((k_attend_f32<D, DR, false, true>), g, dim3(256), 0, s, A);
+        else hipLaunchKernelGGL((k_attend_f32<D, DR, false, false>), g, dim3(256), 0, s, A);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_f32(const AttnArgs &A, bool csa, bool prefill, hipStream_t s) {
+    if (A.L.d == 512) return launch_f32_t<512, 64>(A, csa, prefill, s);
+    return launch_f32_t<64, 16>(A, csa, prefill, s);
+}
+
 // ---------------------------------------------------------------- launchers
 int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa) {
     return (csa ? (int64_t)L.topk : (int64_t)C.max_blocks * L.epb) + L.W;
@@ -1128,29 +1227,24 @@ int64_t attend_lds_max(const Lay &L, int64_t list_max) {
 }
 
 // Raise a kernel's dynamic-LDS limit to at least `bytes`.  The limit only
-// grows (under a lock: callers on several threads never lower it under a
-// launch that needs more); one record per kernel, the last 16 kernels.
-static hipError_t raise_lds_limit(const void *fn, int64_t bytes) {
-    static std::mutex mu;
-    static const void *fns[16] = {};
-    static int64_t lim[16] = {};
-    std::lock_guard<std::mutex> lk(mu);
-    int i = 0;
-    while (i < 16 && fns[i] && fns[i] != fn) ++i;
-    if (i == 16) i = 15;                             // (more kernels than slots: reuse the last)
-    if (fns[i] == fn && lim[i] >= bytes) return hipSuccess;
+// grows, under one lock shared by all kernels, so callers on several threads
+// never lower it beneath a launch that needs more.  `lim` is the kernel's own
+// record (a static of its launcher's template instance).
+static std::mutex g_lds_mu;
+static hipError_t raise_lds_limit(const void *fn, int64_t bytes, int64_t &lim) {
+    std::lock_guard<std::mutex> lk(g_lds_mu);
+    if (lim >= bytes) return hipSuccess;
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    if (fns[i] != fn) lim[i] = 0;
-    fns[i] = fn;
-    lim[i] = bytes > lim[i] ? bytes : lim[i];
+    lim = bytes;
     return hipSuccess;
 }
 
 template <int D, int DR, int NSW, bool CSA, bool PREFILL>
 static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
+    static int64_t lim = 0;
     const int64_t lds = attend_lds_bytes<D, DR, NSW>(attend_list_max(A.L, A.C, CSA));
-    hipError_t e = raise_lds_limit((const void *)k_attend<D, DR, NSW, CSA, PREFILL>, lds);
+    hipError_t e = raise_lds_limit((const void *)k_attend<D, DR, NSW, CSA, PREFILL>, lds, lim);
     if (e != hipSuccess) return e;
     const int groups = (A.nq + 7) / 8;
     hipLaunchKernelGGL((k_attend<D, DR, NSW, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kParts * NSW),
@@ -1160,8 +1254,9 @@ static hipError_t launch_gr(const AttnArgs &A, hipStream_t s) {
 
 template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_lo(const AttnArgs &A, hipStream_t s) {
+    static int64_t lim = 0;
     const int64_t lds = attend_lo_lds_bytes<D, DR>(attend_list_max(A.L, A.C, CSA));
-    hipError_t e = raise_lds_limit((const void *)k_attend_lo<D, DR, CSA, PREFILL>, lds);
+    hipError_t e = raise_lds_limit((const void *)k_attend_lo<D, DR, CSA, PREFILL>, lds, lim);
     if (e != hipSuccess) return e;
     const int groups = (A.nq + 7) / 8;
     hipLaunchKernelGGL((k_attend_lo<D, DR, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kSubsets), (size_t)lds,

@@ -272,6 +272,62 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     if (lane == 0) wr[(int64_t)q * nwr + k0 / kKeysPerWave] = make_uint2(kmn, kmx);
 }
 
+// ---------------------------------------------------------------- fp32 index rows
+// Index keys stored as fp32 (the reference-precision storage mode) and the
+// queries taken as given: grid (nwr / 4, n), one wave per 256 keys of a query
+// (the score record the top-k passes read), lane l scoring keys k0 + 4l + c.
+// Per key the head dot products are fp32 fma chains in dim order, ReLU and the
+// head weights folded in head order; the workgroup's query rows and weights
+// sit in LDS.  Decode and prefill queries take the same kernel.
+__global__ __launch_bounds__(256) void k_index_score_f32(Lay L, dsv4_cache C, const void *qI, const float *w,
+                                                         const int32_t *req, const int32_t *pos, float *scores,
+                                                         int64_t ld, uint2 *wr, int nwr) {
+    __shared__ float qs[64 * 128];
+    __shared__ float ws_[64];
+    const int q = blockIdx.y, lane = threadIdx.x & 63;
+    const int HI = L.HI, dI = L.dI;
+    for (int i = threadIdx.x; i < HI * dI; i += 256) qs[i] = load_act(qI, (int64_t)q * HI * dI + i, L.act);
+    if (threadIdx.x < HI) ws_[threadIdx.x] = w ? w[(int64_t)q * HI + threadIdx.x] : 1.0f;
+    __syncthreads();
+    const int r = req[q];
+    const int t = pos[q];
+    if (r < 0 || r >= C.n_req || t < 0 || (int64_t)t >= (int64_t)C.max_blocks * kBlockTokens) return;
+    const int N = (t + 1) / L.m;
+    const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kKeysPerWave;
+    if (k0 >= N) return;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll 1
+    for (int c = 0; c < 4; ++c) {
+        const int j = k0 + 4 * lane + c;
+        if (j >= N) break;
+        const int64_t bid = block_id(C.block_table, C.max_blocks, C.n_blocks, r, ((int64_t)j * L.m) / kBlockTokens);
+        float v = 0.0f;
+        if (bid >= 0) {
+            const float *key =
+                (const float *)((const uint8_t *)C.index_keys + bid * L.index_block_bytes + (j % L.epb) * L.key_bytes);
+            float acc = 0.0f;
+            for (int h = 0; h < HI; ++h) {
+                float dot = 0.0f;
+                for (int e = 0; e < dI; ++e) dot = __builtin_fmaf(qs[h * dI + e], key[e], dot);
+                acc = __builtin_fmaf(fmaxf(dot, 0.0f), ws_[h], acc);
+            }
+            v = acc;
+        }
+        scores[(int64_t)q * ld + j] = v;
+        if (fabsf(v) < INFINITY) {
+            const uint32_t u = score_key(v);
+            mn = min(mn, u);
+            mx = max(mx, u);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    }
+    if (lane == 0) wr[(int64_t)q * nwr + k0 / kKeysPerWave] = make_uint2(mn, mx);
+}
+
 // ---------------------------------------------------------------- prefill scoring
 // The queries of a prefill chunk read the same keys.  A workgroup scores
 // kPfRows consecutive query rows (kPfWaveRows per wave) against kPfKeys keys,
@@ -1309,6 +1365,13 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
     }
 #undef DSV4_SCORE_HB
 #undef DSV4_SCORE
+    return hipGetLastError();
+}
+
+hipError_t launch_score_f32(const Lay &L, const dsv4_cache &C, const void *qI, const float *w, const int32_t *req,
+                            const int32_t *pos, int n, const IndexWs &ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_index_score_f32, dim3((unsigned)(ws.nwr / 4), n), dim3(256), 0, s, L, C, qI, w, req, pos,
+                       ws.scores, ws.ld, ws.wr, ws.nwr);
     return hipGetLastError();
 }
 

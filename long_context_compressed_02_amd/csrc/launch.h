@@ -62,6 +62,10 @@ hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t 
 // in index order share their key loads).
 hipError_t launch_score_prefill(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
                                 int n, const IndexWs &ws, hipStream_t s);
+// fp32 index rows (reference-precision storage): scores from the query rows
+// as given, into the same workspace records the top-k passes read.
+hipError_t launch_score_f32(const Lay &L, const dsv4_cache &C, const void *qI, const float *w, const int32_t *req,
+                            const int32_t *pos, int n, const IndexWs &ws, hipStream_t s);
 hipError_t launch_topk(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos, int n,
                        const IndexWs &ws, int32_t *out, hipStream_t s);
 hipError_t launch_topk_rows(const float *scores, int64_t ld, const int32_t *nvis, int n, int64_t max_n, int k,
@@ -86,6 +90,8 @@ struct AttnArgs {
     int nhg;                // head groups (ceil(H/16))
 };
 hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s);
+// fp32 records (reference-precision storage): one kernel for both policies.
+hipError_t launch_attend_f32(const AttnArgs &A, bool csa, bool prefill, hipStream_t s);
 // Longest record list one attention query can have, and the LDS the attention
 // kernels need for it (the per-query locators live in LDS).
 int64_t attend_list_max(const Lay &L, const dsv4_cache &C, bool csa);
@@ -103,6 +109,9 @@ hipError_t launch_mx_quant(const uint16_t *X, int rows, int K, bool fp8, uint8_t
 hipError_t launch_mx_gemm(const uint8_t *A, const uint8_t *Bp, int M, int N, int K, void *C, int64_t ldc, int c_f32,
                           hipStream_t s);
 int64_t cache_dump_bytes(const Lay &L, int nb);
+// Dequantised read-back of stored entries, index keys or window records.
+hipError_t launch_read_entries(const Lay &L, const dsv4_cache &C, int target, const int32_t *req, const int32_t *idx,
+                               int n, void *out, bool f64, hipStream_t s);
 hipError_t launch_cache_xfer(const Lay &L, const dsv4_cache &C, int r, int nb, uint8_t *buf, bool to_buf,
                              hipStream_t s);
 

@@ -12,18 +12,40 @@ from oracle import oracle as O
 DEV = "cuda"
 
 
-# the oracle's storage mode for each of the library's index-row formats
-IDX_MODE = {B.DSV4_STORE_FP8: 1, B.DSV4_STORE_MXFP4: 2}
+# the oracle's storage mode for each of the library's storage formats
+IDX_MODE = {B.DSV4_STORE_FP32: 0, B.DSV4_STORE_FP8: 1, B.DSV4_STORE_MXFP4: 2}
+KV_MODE = {B.DSV4_STORE_FP32: 0, B.DSV4_STORE_FP8: 1}
 
 
-def cfgs(shape: dict, act=B.DSV4_DT_BF16, topk=None, idx_store=B.DSV4_STORE_FP8):
+def cfgs(shape: dict, act=B.DSV4_DT_BF16, topk=None, idx_store=B.DSV4_STORE_FP8, kv_store=B.DSV4_STORE_FP8):
     """The library's cfg and the oracle's cfg for the same shape."""
     sh = dict(shape)
     if topk is not None:
         sh["topk"] = topk
-    lib_cfg = B.make_cfg(act_dtype=act, idx_store=idx_store, **sh)
-    ocfg = O.OCfg(idx_mode=IDX_MODE[idx_store], **sh)
+    lib_cfg = B.make_cfg(act_dtype=act, idx_store=idx_store, kv_store=kv_store, **sh)
+    ocfg = O.OCfg(idx_mode=IDX_MODE[idx_store], kv_mode=KV_MODE[kv_store], **sh)
     return lib_cfg, ocfg
+
+
+def read_back(cfg, cache, target, r, idxs) -> np.ndarray:
+    """Stored vectors of request r decoded by the library's read-back call
+    (entries, index keys or window records), exact, float64 [len(idxs), dim]."""
+    idxs = list(idxs)
+    dim = cfg.idx_dim if target == B.DSV4_TARGET_INDEX_KEY else cfg.d
+    out = torch.full((max(1, len(idxs)), dim), float("nan"), dtype=torch.float64, device=DEV)
+    if idxs:
+        B.dsv4_cache_read_entries(cfg, cache, target, i32([r] * len(idxs)), i32(idxs), out)
+        torch.cuda.synchronize()
+    return out[:len(idxs)].cpu().numpy()
+
+
+def attend_on_selection(t, q, sinks, ents, sel, window_of, oc):
+    """The oracle's attention of the query at t over the given entry
+    selection (rows of ents, -1 padding ignored) followed by its window."""
+    sel = [int(j) for j in sel if j >= 0]
+    win = [window_of(u) for u in O.window_tokens(t, oc)]
+    recs = np.concatenate([np.asarray(ents)[sel].reshape(-1, oc.d), np.asarray(win).reshape(-1, oc.d)])
+    return O.attend(O.query_rot(q, t, oc), sinks, recs, oc.tau)
 
 
 def block_table(ctx_tokens, extra_blocks=0, seed=0, max_blocks=None):

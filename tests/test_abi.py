@@ -57,6 +57,38 @@ def test_layout_tiny_shape():
     assert lay.record_bytes == 128 and lay.index_key_bytes == 32
 
 
+def test_layout_fp32_storage():
+    """Reference-precision storage: a record is d fp32 values, an index key
+    idx_dim fp32 values; the tiny shape's records fill 256 bytes exactly."""
+    cfg = B.make_cfg(d=64, d_rope=16, n_heads=8, window=16, idx_heads=4, idx_dim=32, topk=32,
+                     kv_store=B.DSV4_STORE_FP32, idx_store=B.DSV4_STORE_FP32, act_dtype=B.DSV4_DT_F32)
+    lay = B.dsv4_get_layout(cfg, B.DSV4_CSA)
+    assert lay.record_bytes == 64 * 4 and lay.index_key_bytes == 32 * 4
+    assert lay.entry_block_bytes == 32 * 256
+    assert lay.index_block_bytes >= 32 * 128 and lay.index_block_bytes % 256 == 0
+    big = B.dsv4_get_layout(B.make_cfg(kv_store=B.DSV4_STORE_FP32, idx_store=B.DSV4_STORE_FP32), B.DSV4_CSA)
+    assert big.record_bytes == 2048 and big.index_key_bytes == 512
+
+
+def test_read_entries_rejects_bad_arguments_before_launch():
+    L = B.lib()
+    cfg = B.make_cfg()
+    c = _fake_cache()
+    h = _fake_cache(B.DSV4_HCA)
+    p = ctypes.c_void_p(FAKE)
+    rd = lambda cache, target, n, out=p, dt=B.DSV4_DT_F32: L.dsv4_cache_read_entries(
+        ctypes.byref(cfg), ctypes.byref(cache), target, p, p, n, out, dt, None)
+    assert rd(c, 9, 4) == B.DSV4_ERR_INVALID_ARG                     # unknown target
+    assert rd(h, B.DSV4_TARGET_INDEX_KEY, 4) == B.DSV4_ERR_INVALID_ARG   # HCA has no index keys
+    assert rd(c, B.DSV4_TARGET_ENTRY, -1) == B.DSV4_ERR_INVALID_ARG
+    assert rd(c, B.DSV4_TARGET_ENTRY, 4, None) == B.DSV4_ERR_INVALID_ARG
+    assert rd(c, B.DSV4_TARGET_ENTRY, 4, ctypes.c_void_p(FAKE + 4)) == B.DSV4_ERR_INVALID_ARG   # unaligned out
+    assert rd(c, B.DSV4_TARGET_ENTRY, 4, dt=B.DSV4_DT_BF16) == B.DSV4_ERR_INVALID_ARG   # fp32 / fp64 only
+    assert rd(c, B.DSV4_TARGET_WINDOW, 0) == B.DSV4_OK              # empty: nothing to do
+    assert rd(c, B.DSV4_TARGET_WINDOW, 0, dt=B.DSV4_DT_F64) == B.DSV4_OK
+    assert L.dsv4_cache_read_entries(ctypes.byref(cfg), None, 0, p, p, 4, p, 0, None) == B.DSV4_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("d", 0, B.DSV4_ERR_INVALID_ARG),
     ("d_rope", 24, B.DSV4_ERR_INVALID_ARG),

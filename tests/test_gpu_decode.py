@@ -56,6 +56,58 @@ def test_cache_write_entries(shape, kind):
             assert np.array_equal(Hh.key_rows(cache, r, js, bth), O.store_index_rows(kv, oc))
 
 
+@pytest.mark.parametrize("store", ["fp8", "mxfp4", "fp32"])
+@pytest.mark.parametrize("shape", [PROD, TINY], ids=["d512", "d64"])
+def test_cache_read_entries(shape, store):
+    """The read-back call decodes entries, index keys and window records
+    exactly (fp64 output): equal to the oracle's storage of the same fp32
+    values where both sides take the same fp32 decisions (codes, scales, fp32
+    values), to one code step on the RoPE dims (rotated in fp32 / fp64), and
+    its fp32 output is the fp64 one rounded."""
+    kv_store = B.DSV4_STORE_FP32 if store == "fp32" else B.DSV4_STORE_FP8
+    idx_store = {"fp8": B.DSV4_STORE_FP8, "mxfp4": B.DSV4_STORE_MXFP4, "fp32": B.DSV4_STORE_FP32}[store]
+    cfg, oc = Hh.cfgs(shape, idx_store=idx_store, kv_store=kv_store)
+    ctx = [3000, 700]
+    cache, bth = _new_cache(cfg, B.DSV4_CSA, ctx, seed=8)
+    rng = np.random.default_rng(8)
+    dn = oc.d - oc.d_rope
+    for r, c in enumerate(ctx):
+        n = c // 4
+        vals = rng.standard_normal((n, oc.d), dtype=np.float32) * np.float32(2.0)
+        kv = rng.standard_normal((n, oc.idx_dim), dtype=np.float32)
+        B.dsv4_cache_write_entries(cfg, cache, B.DSV4_TARGET_ENTRY, Hh.i32([r] * n), Hh.i32(range(n)),
+                                   torch.from_numpy(vals).to(Hh.DEV))
+        B.dsv4_cache_write_entries(cfg, cache, B.DSV4_TARGET_INDEX_KEY, Hh.i32([r] * n), Hh.i32(range(n)),
+                                   torch.from_numpy(kv).to(Hh.DEV))
+        w0 = c - oc.window
+        tok = [Hh.act_tensor(rng.standard_normal((oc.window, m), dtype=np.float32), B.DSV4_DT_BF16)
+               for m in (oc.d, oc.d, oc.idx_dim, oc.idx_dim)]
+        B.dsv4_state_write_tokens(cfg, cache, r, w0, *[a[0] for a in tok])
+        js = list(range(0, n, 7)) + [n - 1]
+        ents = Hh.read_back(cfg, cache, B.DSV4_TARGET_ENTRY, r, js)
+        ref = O.entries_from_values("csa", vals[js], js, oc)
+        assert np.array_equal(ents[:, :dn], ref[:, :dn])
+        Hh.assert_records_close(ents, ref, oc.d_rope) if kv_store == B.DSV4_STORE_FP8 else \
+            np.testing.assert_allclose(ents, ref, rtol=1e-6, atol=1e-6)
+        keys = Hh.read_back(cfg, cache, B.DSV4_TARGET_INDEX_KEY, r, js)
+        assert np.array_equal(keys, O.store_index_rows(kv[js], oc))
+        pw = list(range(w0, c))
+        wrec = Hh.read_back(cfg, cache, B.DSV4_TARGET_WINDOW, r, pw)
+        wref = O.window_records(tok[0][1], np.array(pw), oc)
+        assert np.array_equal(wrec[:, :dn], wref[:, :dn]) or kv_store == B.DSV4_STORE_FP32
+        Hh.assert_records_close(wrec, wref, oc.d_rope) if kv_store == B.DSV4_STORE_FP8 else \
+            np.testing.assert_allclose(wrec, wref, rtol=1e-6, atol=1e-6)
+        if kv_store == B.DSV4_STORE_FP8:           # the byte decoders of the tests agree
+            assert np.array_equal(ents, Hh.entry_rows(cache, r, js, bth))
+            assert np.array_equal(wrec, Hh.window_rows(cache, r, pw))
+        if idx_store != B.DSV4_STORE_FP32:
+            assert np.array_equal(keys, Hh.key_rows(cache, r, js, bth))
+        # fp32 output: the fp64 values rounded
+        out32 = torch.empty((len(js), oc.d), dtype=torch.float32, device=Hh.DEV)
+        B.dsv4_cache_read_entries(cfg, cache, B.DSV4_TARGET_ENTRY, Hh.i32([r] * len(js)), Hh.i32(js), out32)
+        assert np.array_equal(out32.cpu().numpy(), ents.astype(np.float32))
+
+
 @pytest.mark.parametrize("shape", [PROD, TINY], ids=["d512", "d64"])
 def test_cache_write_index_keys_mxfp4(shape):
     """MXFP4 index keys: codes and block exponents are fp32 decisions on both
@@ -149,7 +201,7 @@ def test_compress_decode_equals_prefill_and_oracle(shape, kind, idx):
 
 # ------------------------------------------------------------------ indexer + top-k
 @pytest.mark.parametrize("k", [256, 1024])
-@pytest.mark.parametrize("idx", [B.DSV4_STORE_FP8, B.DSV4_STORE_MXFP4], ids=["fp8", "mxfp4"])
+@pytest.mark.parametrize("idx", [B.DSV4_STORE_FP8, B.DSV4_STORE_MXFP4, B.DSV4_STORE_FP32], ids=["fp8", "mxfp4", "fp32"])
 def test_index_topk_decode(k, idx):
     cfg, oc = Hh.cfgs(PROD, topk=k, idx_store=idx)
     ctx = [3, 1000, 4099, 20001, 4000, 160004]   # query position t = ctx - 1 (the last: two top-k segments)
@@ -179,10 +231,10 @@ def test_index_topk_decode(k, idx):
 
 
 # ------------------------------------------------------------------ attention
-def _fill_attention_case(kind, ctx, seed, act=B.DSV4_DT_BF16, shape=PROD):
+def _fill_attention_case(kind, ctx, seed, act=B.DSV4_DT_BF16, shape=PROD, kv_store=B.DSV4_STORE_FP8):
     """Caches with directly written entries and raw window tokens; returns the
     cache, oracle stored entries per request, window records per request."""
-    cfg, oc = Hh.cfgs(shape, act=act)
+    cfg, oc = Hh.cfgs(shape, act=act, kv_store=kv_store)
     cache, bth = _new_cache(cfg, kind, ctx, seed=seed)
     m = oc.m_csa if kind == B.DSV4_CSA else oc.m_hca
     kname = "csa" if kind == B.DSV4_CSA else "hca"
@@ -220,15 +272,28 @@ def _random_topk(n_vis, k, seed):
     return out
 
 
+def _sinks(profile):
+    """Per-head sink logits: N(0,1), or the limits mixed over the heads --
+    -inf (no sink: plain softmax), +30 (a dominating sink: the output shrinks
+    towards 0) and N(0,1) -- in every 16-head group."""
+    z = synth.sinks(synth.CSA_DECODE_128K).copy()
+    if profile == "limits":
+        h = np.arange(z.shape[0])
+        z[h % 4 == 0] = -np.inf
+        z[h % 4 == 1] = 30.0
+    return z
+
+
+@pytest.mark.parametrize("sink_profile", ["normal", "limits"])
 @pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
-def test_attend_decode_parity_and_invariance(kind):
+def test_attend_decode_parity_and_invariance(kind, sink_profile):
     ctx = [5, 130, 1000, 5000, 128, 4097]
     cfg, oc, cache, ents, wins = _fill_attention_case(kind, ctx, seed=4)
     nq = len(ctx)
     pos = [c - 1 for c in ctx]
     q, _, _ = synth.decode_queries(synth.CSA_DECODE_128K, nq, sub=4)
     qt, qx = Hh.act_tensor(q, B.DSV4_DT_BF16)
-    sinks = synth.sinks(synth.CSA_DECODE_128K)
+    sinks = _sinks(sink_profile)
     st = torch.from_numpy(sinks).to(Hh.DEV)
     csa = kind == B.DSV4_CSA
     topk = np.stack([_random_topk(O.n_visible("csa", p, oc), oc.topk, 100 + i) for i, p in enumerate(pos)])
@@ -271,3 +336,42 @@ def test_attend_decode_parity_and_invariance(kind):
         err = Hh.rel_err_per_head(got[r], ref)
         assert err.max() <= 2e-2, (r, err.max())
         assert np.median(err) <= 4e-3, (r, np.median(err))
+
+
+@pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
+def test_attend_decode_fp32_storage(kind):
+    """Records stored as fp32 (the reference-precision mode) at the production
+    head shape: both policies give the same bytes, and every head is within
+    1e-4 of the oracle (sinks at their limits included)."""
+    ctx = [5, 130, 1000, 4097]
+    cfg, oc, cache, ents, wins = _fill_attention_case(kind, ctx, seed=6, act=B.DSV4_DT_F32,
+                                                      kv_store=B.DSV4_STORE_FP32)
+    nq = len(ctx)
+    pos = [c - 1 for c in ctx]
+    q, _, _ = synth.decode_queries(synth.CSA_DECODE_128K, nq, sub=6)
+    qt, qx = Hh.act_tensor(q, B.DSV4_DT_F32)
+    sinks = _sinks("limits")
+    st = torch.from_numpy(sinks).to(Hh.DEV)
+    csa = kind == B.DSV4_CSA
+    topk = np.stack([_random_topk(O.n_visible("csa", p, oc), oc.topk, 200 + i) for i, p in enumerate(pos)])
+    tk = Hh.i32(topk)
+    outs = []
+    for policy in (B.DSV4_POLICY_LO, B.DSV4_POLICY_HI):
+        o = torch.empty((nq, oc.n_heads, oc.d), dtype=torch.float32, device=Hh.DEV)
+        if csa:
+            B.dsv4_csa_attend_decode(cfg, cache, qt, Hh.i32(range(nq)), Hh.i32(pos), tk, st, o, policy)
+        else:
+            B.dsv4_hca_attend_decode(cfg, cache, qt, Hh.i32(range(nq)), Hh.i32(pos), st, o, policy)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    got = outs[0].double().cpu().numpy()
+    for r, t in enumerate(pos):
+        win = lambda u: wins[r][u]
+        if csa:
+            ref = Hh.attend_on_selection(t, qx[r], sinks, ents[r], topk[r], win, oc)
+        else:
+            ref = O.hca_query(t, qx[r], sinks, ents[r], win, oc)
+        err = Hh.rel_err_per_head(got[r], ref)
+        print(f"  fp32 {kind} r{r}: max rel err {err.max():.2e}", flush=True)
+        assert err.max() <= 1e-4, (r, err.max())

@@ -5,8 +5,8 @@ invariance at full size (bitwise).
   decode_128k_b32   CSA + HCA decode step, batch 32 x 128K context, V4-Pro shape,
                     top-1024 (the benchmark's configuration)
   hca_decode_64k    HCA decode, batch 16 x 64K context
-  pair_1m_mixed     CSA + HCA at contexts 1M / 512K / 64K / 4K: oracle at the 1M
-                    and 4K queries; the same queries alone, reordered, with both
+  pair_1m_mixed     CSA + HCA at contexts 1M / 512K / 64K / 4K: oracle at all
+                    four queries; the same queries alone, reordered, with both
                     decode kernels, and 16 times over in a batch of 64 (half of the
                     copies sharing the original's cache blocks, half on copied
                     blocks at other addresses) must give the same bytes
@@ -79,16 +79,21 @@ def _bf(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
 
 
+def _oracle_csa_on(req, t, q, sinks, sel, oc):
+    """CSA output of the query at position t over the entry selection sel
+    (ascending, -1 padding ignored) and the window."""
+    sel = [int(j) for j in sel if j >= 0]
+    ents = O.entries_from_values("csa", req.ents[sel], sel, oc)
+    pos = np.arange(max(0, t - oc.window + 1), t + 1)
+    win = O.window_records(_bf(req.win[0][pos - req.w0]), pos, oc)
+    return O.attend(O.query_rot(q, t, oc), sinks, np.concatenate([ents, win]), oc.tau)
+
+
 def _oracle_csa(req, t, q, qI, w, sinks, oc):
     """Top-k and CSA output of the query at position t (the cache holds tokens < t+1)."""
     keys = O.store_index_rows(req.keys[: (t + 1) // oc.m_csa], oc)
     idx, s = O.csa_select(t, qI, w, keys, oc)
-    sel = [int(j) for j in idx if j >= 0]
-    ents = O.entries_from_values("csa", req.ents[sel], sel, oc)
-    pos = np.arange(max(0, t - oc.window + 1), t + 1)
-    win = O.window_records(_bf(req.win[0][pos - req.w0]), pos, oc)
-    o = O.attend(O.query_rot(q, t, oc), sinks, np.concatenate([ents, win]), oc.tau)
-    return idx, s, o
+    return idx, s, _oracle_csa_on(req, t, q, sinks, idx, oc)
 
 
 def _oracle_hca(req, t, q, sinks, oc):
@@ -99,17 +104,22 @@ def _oracle_hca(req, t, q, sinks, oc):
     return O.attend(O.query_rot(q, t, oc), sinks, np.concatenate([ents, win]), oc.tau)
 
 
-def _check(got_tk, got_o, idx, s, o, k, label):
+def _check(got_tk, got_o, idx, s, o, k, label, on_gpu_sel=None):
+    """Top-k against the oracle (tie band), then the output against the
+    oracle's attention; where a near-tie swap changed the attended set, the
+    reference is the oracle's attention over the GPU's own selection
+    (on_gpu_sel() computes it), a valid answer as the selection is."""
+    swaps = 0
     if idx is not None:
         swaps = Hh.topk_match(got_tk, idx, s, k)
         print(f"  {label}: top-{k} {'equal' if not swaps else f'{swaps} tie swaps'}", flush=True)
-        if swaps:   # a near-tie swap changes the attended set: compare the attention elsewhere
-            return swaps
+        if swaps:
+            o = on_gpu_sel()
     err = Hh.rel_err_per_head(got_o, o)
     print(f"  {label}: max rel err {err.max():.2e}, median {np.median(err):.2e}", flush=True)
     assert err.max() <= 2e-2, (label, err.max())
     assert np.median(err) <= 4e-3, (label, np.median(err))
-    return 0
+    return swaps
 
 
 def _layer_pair(cfg, oc, ctxs, rows):
@@ -182,7 +192,8 @@ def test_decode_128k_b32():
         d.winh = [np.concatenate([a[1:], new[4 + i][r:r + 1]]) for i, a in enumerate(d.winh)]
         d.w0 += 1
         idx, s, o = _oracle_csa(d, t, qx[r], qIx[r], w1[r].astype(np.float64), sinks, oc)
-        swaps += _check(gtk[r], go[r], idx, s, o, oc.topk, f"csa r{r}")
+        swaps += _check(gtk[r], go[r], idx, s, o, oc.topk, f"csa r{r}",
+                        lambda: _oracle_csa_on(d, t, qx[r], sinks, gtk[r], oc))
         oh_ref = _oracle_hca(d, t, qhx[r], sinks, oc)
         _check(None, gh[r], None, None, oh_ref, 0, f"hca r{r}")
     assert swaps <= 2
@@ -346,11 +357,12 @@ def test_pair_1m_mixed_batch_invariance():
     print("pair_1m: oracle", flush=True)
     gtk, go, gh = tk4.cpu().numpy(), o4.double().cpu().numpy(), h4.double().cpu().numpy()
     swaps = 0
-    for i in (0, 3):
+    for i in range(4):
         idx, s, o = _oracle_csa(reqs[i], pos[i], qx[i], qIx[i], wq[i].astype(np.float64), sinks, oc)
-        swaps += _check(gtk[i], go[i], idx, s, o, oc.topk, f"csa {i}")
+        swaps += _check(gtk[i], go[i], idx, s, o, oc.topk, f"csa {i}",
+                        lambda: _oracle_csa_on(reqs[i], pos[i], qx[i], sinks, gtk[i], oc))
         _check(None, gh[i], None, None, _oracle_hca(reqs[i], pos[i], qhx[i], sinks, oc), 0, f"hca {i}")
-    assert swaps <= 1
+    assert swaps <= 2
 
 
 # ------------------------------------------------------------------ config: prefill chunk 8192 on a 256K prefix
@@ -419,12 +431,16 @@ def test_prefill_8k_on_256k():
         t = Pn + i
         nv = (t + 1) // oc.m_csa
         idx, s = O.csa_select(t, qIx[n_], wx[n_], keys_all[:nv], oc)
-        sel = idx[idx >= 0].astype(np.int64)
-        old, new_ = sel[sel < n_pre], sel[sel >= n_pre]
-        ents = np.concatenate([O.entries_from_values("csa", pre.ents[old], old, oc), ents_new[new_ - n_pre]])
         pos = np.arange(t - oc.window + 1, t + 1)
-        o = O.attend(O.query_rot(qx[n_], t, oc), sinks, np.concatenate([ents, wrec[pos - t0]]), oc.tau)
-        swaps += _check(gtk[n_], go[n_], idx, s, o, k, f"csa prefill {i}")
+
+        def attend_sel(sel, t=t, n_=n_, pos=pos):
+            sel = np.asarray(sel)
+            sel = sel[sel >= 0].astype(np.int64)
+            old, new_ = sel[sel < n_pre], sel[sel >= n_pre]
+            ents = np.concatenate([O.entries_from_values("csa", pre.ents[old], old, oc), ents_new[new_ - n_pre]])
+            return O.attend(O.query_rot(qx[n_], t, oc), sinks, np.concatenate([ents, wrec[pos - t0]]), oc.tau)
+        swaps += _check(gtk[n_], go[n_], idx, s, attend_sel(idx), k, f"csa prefill {i}",
+                        lambda: attend_sel(gtk[n_]))
         nvh = (t + 1) // oc.m_hca
         oh = O.attend(O.query_rot(qhx[n_], t, oc), sinks, np.concatenate([hents[:nvh], wrech[pos - t0]]), oc.tau)
         _check(None, gh[n_], None, None, oh, 0, f"hca prefill {i}")

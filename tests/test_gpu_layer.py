@@ -11,31 +11,47 @@ from tests import helpers as Hh
 
 pytestmark = pytest.mark.gpu
 
-# Top-k sets computed end to end (keys made by each side's own compressor) can
-# also differ where a stored index-key code flipped at a rounding boundary: one
-# E4M3 step in one of 128 key dims moves a score by ~1e-3 of its size at most.
-E2E_BAND = 2e-3
-# MXFP4 keys: one E2M1 step is up to a quarter of the block's largest value,
-# so a flipped code moves its key's score by up to ~10% (such flips need a
-# pre-rounding value within ~1e-7 of a boundary: in practice none occur).
-E2E_BAND_MX = 0.1
+# Top-k is checked against the oracle's selection over the index keys the GPU
+# stored (read back through the library): the stored keys are compared with
+# the oracle's own compressor separately, so the selection is held to the
+# 1e-6 tie band whatever rounding boundary a pooled key sits on.  The
+# attention output of every query is compared with the oracle's attention over
+# the GPU's own selection (a valid answer whenever the selection is).
+STORES = {"fp32": (B.DSV4_STORE_FP32, B.DSV4_STORE_FP32), "fp8": (B.DSV4_STORE_FP8, B.DSV4_STORE_FP8),
+          "mxfp4": (B.DSV4_STORE_FP8, B.DSV4_STORE_MXFP4)}
+# output bar per storage: fp32 records are the reference-precision mode
+BAR = {"fp32": (1e-4, 2e-5), "fp8": (2e-2, 5e-3), "mxfp4": (2e-2, 5e-3)}
 
 
-def _check_topk_e2e(got, ref, scores, k, band=E2E_BAND):
-    """Returns positions whose lists differ (each difference within the band)."""
-    return Hh.topk_match(got, ref, scores, k, band_rel=band)
+def _check_stored_keys(got, ref, idx_store):
+    if idx_store == B.DSV4_STORE_MXFP4:
+        Hh.assert_mx_rows_close(got, ref)
+    elif idx_store == B.DSV4_STORE_FP8:
+        Hh.assert_records_close(got, ref, 0)
+    else:
+        assert np.allclose(got, ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
 
 
-@pytest.mark.parametrize("idx_store", [B.DSV4_STORE_FP8, B.DSV4_STORE_MXFP4], ids=["fp8", "mxfp4"])
-def test_tiny_layer_prefill_then_decode(idx_store):
+def _check_stored_entries(got, ref, kv_store, d_rope):
+    if kv_store == B.DSV4_STORE_FP8:
+        Hh.assert_records_close(got, ref, d_rope)
+    else:
+        assert np.allclose(got, ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("store", ["fp32", "fp8", "mxfp4"])
+def test_tiny_layer_prefill_then_decode(store):
     """Tiny CSA layer (hidden 256, 8 heads of 64, RoPE 16, window 16, indexer
     4x32, top-32): prefill of 1024 tokens then 16 decode steps, inputs projected
-    from seeded hidden states, FP8/BF16 storage, index rows FP8 or MXFP4."""
+    from seeded hidden states; storage fp32 (records and index rows: the
+    reference-precision mode, held to 1e-4), FP8/BF16, or FP8/BF16 records
+    with MXFP4 index rows."""
     w = synth.TINY_CSA
     act = B.DSV4_DT_F32
     shape = w.shape()
-    cfg, oc = Hh.cfgs(shape, act=act, idx_store=idx_store)
-    band = E2E_BAND_MX if idx_store == B.DSV4_STORE_MXFP4 else E2E_BAND
+    kv_store, idx_store = STORES[store]
+    cfg, oc = Hh.cfgs(shape, act=act, idx_store=idx_store, kv_store=kv_store)
+    bar, med_bar = BAR[store]
     P = synth.tiny_hidden(w, steps=16)
     T0, T = w.ctx[0], w.ctx[0] + 16
     x = P["x"].astype(np.float64)
@@ -72,23 +88,27 @@ def test_tiny_layer_prefill_then_decode(idx_store):
     torch.cuda.synchronize()
     got_out = torch.cat([out_pre] + outs_dec).double().cpu().numpy()
     got_tk = torch.cat([tk_pre] + tks_dec).cpu().numpy()
-    # ---- oracle, token by token
+    # ---- the stored cache against the oracle's compressor
     ents = O.entries_from_pool("csa", kv, gate, range(T // 4), oc)
     keys = O.index_keys_from_pool(kI, gI, range(T // 4), oc)
     wrec = O.window_records(kv, np.arange(T), oc)
-    differing = 0
-    errs = []
+    keys_gpu = Hh.read_back(cfg, cache, B.DSV4_TARGET_INDEX_KEY, 0, range(T // 4))
+    _check_stored_keys(keys_gpu, keys, idx_store)
+    _check_stored_entries(Hh.read_back(cfg, cache, B.DSV4_TARGET_ENTRY, 0, range(T // 4)), ents, kv_store, oc.d_rope)
+    _check_stored_entries(Hh.read_back(cfg, cache, B.DSV4_TARGET_WINDOW, 0, range(T - w.window, T)),
+                          wrec[T - w.window:], kv_store, oc.d_rope)
+    # ---- every query: selection over the GPU's keys, attention over the GPU's selection
+    swaps, errs = 0, []
     for t in range(T):
-        o, idx, s = O.csa_query(t, q[t], qI[t], wt[t].astype(np.float64), sinks, ents, keys, lambda u: wrec[u],
-                                oc, return_scores=True)
-        d = _check_topk_e2e(got_tk[t], idx, s, w.topk, band)
-        differing += d > 0
-        if d == 0:
-            errs.append(Hh.rel_err_per_head(got_out[t], o).max())
-    assert differing <= T // 100, differing
+        idx, s = O.csa_select(t, qI[t], wt[t].astype(np.float64), keys_gpu, oc)
+        swaps += Hh.topk_match(got_tk[t], idx, s, w.topk) > 0
+        o = Hh.attend_on_selection(t, q[t], sinks, ents, got_tk[t], lambda u: wrec[u], oc)
+        errs.append(Hh.rel_err_per_head(got_out[t], o).max())
+    print(f"  tiny {store}: {swaps} queries with tie swaps; max rel err {max(errs):.2e}", flush=True)
+    assert swaps <= T // 50, swaps
     errs = np.array(errs)
-    assert errs.max() <= 2e-2, errs.max()
-    assert np.median(errs) <= 5e-3, np.median(errs)
+    assert errs.max() <= bar, errs.max()
+    assert np.median(errs) <= med_bar, np.median(errs)
 
 
 @pytest.mark.parametrize("kind,idx_store", [(B.DSV4_CSA, B.DSV4_STORE_FP8), (B.DSV4_HCA, B.DSV4_STORE_FP8),
@@ -101,7 +121,6 @@ def test_prefill_chunk_on_prefix(kind, idx_store):
     k = 512
     act = B.DSV4_DT_BF16
     cfg, oc = Hh.cfgs(synth.CSA_PREFILL_8K.shape(), act=act, topk=k, idx_store=idx_store)
-    band = E2E_BAND_MX if idx_store == B.DSV4_STORE_MXFP4 else E2E_BAND
     csa = kind == B.DSV4_CSA
     kname = "csa" if csa else "hca"
     m = oc.m_csa if csa else oc.m_hca
@@ -156,6 +175,9 @@ def test_prefill_chunk_on_prefix(kind, idx_store):
     Hh.assert_records_close(Hh.entry_rows(cache, 0, js_new, bth), ents[ne:], oc.d_rope)
     if csa:
         keys = np.concatenate([keys_pre, O.index_keys_from_pool(ex[2], ex[3], js_new, oc, token0=t0)])
+        keys_gpu = Hh.read_back(cfg, cache, B.DSV4_TARGET_INDEX_KEY, 0, range(nall))
+        _check_stored_keys(keys_gpu[ne:], keys[ne:], idx_store)
+        assert np.array_equal(keys_gpu[:ne], keys_pre)   # written from given values: exact
         gtk = tk.cpu().numpy()
     wrec = O.window_records(ex[0], np.arange(t0, T), oc)
     window_of = lambda u: wrec[u - t0]
@@ -164,12 +186,9 @@ def test_prefill_chunk_on_prefix(kind, idx_store):
     for i in sample:
         t = Pn + i
         if csa:
-            o, idx, s = O.csa_query(t, qx[i], qIx[i], wq[i].astype(np.float64), sinks, ents, keys, window_of, oc,
-                                    return_scores=True)
-            d = _check_topk_e2e(gtk[i], idx, s, k, band)
-            diffs += d > 0
-            if d:
-                continue
+            idx, s = O.csa_select(t, qIx[i], wq[i].astype(np.float64), keys_gpu, oc)
+            diffs += Hh.topk_match(gtk[i], idx, s, k) > 0
+            o = Hh.attend_on_selection(t, qx[i], sinks, ents, gtk[i], window_of, oc)
         else:
             o = O.hca_query(t, qx[i], sinks, ents, window_of, oc)
         err = Hh.rel_err_per_head(got[i], o)

@@ -417,6 +417,81 @@ def test_planted_key_is_selected_first():
     assert 77 in idx.tolist() and np.argmax(s) == 77
 
 
+def _np_rotate(x, pos, d_rope, base=10000.0):
+    """Interleaved-pair rotation of the last d_rope dims, written out with
+    numpy's cos/sin (independent of the oracle's C routine)."""
+    y = np.array(x, dtype=np.float64)
+    n = y.shape[-1]
+    for i in range(d_rope // 2):
+        th = base ** (-2.0 * i / d_rope)
+        c, s = np.cos(pos * th), np.sin(pos * th)
+        a, b = y[n - d_rope + 2 * i].copy(), y[n - d_rope + 2 * i + 1].copy()
+        y[n - d_rope + 2 * i] = a * c - b * s
+        y[n - d_rope + 2 * i + 1] = a * s + b * c
+    return y
+
+
+@pytest.mark.parametrize("kind,m", [("csa", 4), ("hca", 128)])
+def test_entry_rope_position_is_block_end(kind, m):
+    """A compressed entry is rotated at the last token of its block, m*j + m-1
+    (the reading of the partial-RoPE paragraph, which leaves the position
+    open).  Checked through both oracle paths that store entries -- directly
+    supplied vectors and pooled tokens -- against a numpy rotation; the first
+    and one-past-last token of the block give visibly different vectors, so
+    the pin fails for either of those readings."""
+    cfg = O.OCfg(d=32, d_rope=16, n_heads=1, m_csa=4, w_csa=8, m_hca=128, kv_mode=0)
+    rng = np.random.default_rng(31)
+    js = [0, 1, 5, 37]
+    vals = rng.normal(size=(len(js), 32))
+    got = O.entries_from_values(kind, vals, js, cfg)
+    for i, j in enumerate(js):
+        ref = _np_rotate(vals[i], m * j + m - 1, 16)
+        assert np.allclose(got[i], ref, rtol=0, atol=1e-6 * np.abs(ref).max()), (kind, j)
+        for wrong in (m * j, m * j + m):
+            alt = _np_rotate(vals[i], wrong, 16)
+            assert np.abs(got[i] - alt).max() > 1e-3, (kind, j, wrong)
+    # pooled entries: equal gates make the pooled vector the window's mean
+    # (numpy), which is then rotated at the block end
+    w = cfg.w_csa if kind == "csa" else m
+    T = m * (max(js) + 1)
+    kv = rng.normal(size=(T, 32))
+    gate = np.zeros((T, 32))
+    pooled = O.entries_from_pool(kind, kv, gate, js, cfg)
+    for i, j in enumerate(js):
+        lo = max(0, m * j + m - w)
+        ref = _np_rotate(kv[lo:m * j + m].mean(axis=0), m * j + m - 1, 16)
+        assert np.allclose(pooled[i], ref, rtol=0, atol=1e-6 * np.abs(ref).max()), (kind, j)
+        assert np.abs(pooled[i] - _np_rotate(kv[lo:m * j + m].mean(axis=0), m * j, 16)).max() > 1e-3
+
+
+def test_csa_layer_attends_entries_at_block_end_positions():
+    """Composition at m = 4: with no raw window and every entry selected, a
+    query at t attends exactly the rotated entries; the expected output is
+    written out with numpy (mean-pooled entries rotated at 4j+3, the query
+    rotated at t, softmax over tau * q.k with no sink)."""
+    d, H = 32, 2
+    cfg = O.OCfg(d=d, d_rope=16, n_heads=H, window=0, m_csa=4, w_csa=8, idx_heads=2, idx_dim=16,
+                 topk=64, kv_mode=0, idx_mode=0)
+    rng = np.random.default_rng(33)
+    T = 24
+    kv = rng.normal(size=(T, d))
+    gate = np.zeros((T, d))
+    kI, gI = rng.normal(size=(T, 16)), np.zeros((T, 16))
+    q = rng.normal(size=(T, H, d))
+    qI = rng.normal(size=(T, 2, 16))
+    pos = [7, 15, 23]
+    outs, _ = O.csa_layer(kv, gate, kI, gI, q[pos], qI[pos], None, np.full(H, -np.inf), pos, cfg)
+    for n, t in enumerate(pos):
+        ents = np.stack([_np_rotate(kv[max(0, 4 * j - 4):4 * j + 4].mean(axis=0), 4 * j + 3, 16)
+                         for j in range((t + 1) // 4)])
+        for h in range(H):
+            qr = _np_rotate(q[t, h], t, 16)
+            lg = cfg.tau * ents @ qr
+            p = np.exp(lg - lg.max())
+            ref = (p[:, None] * ents).sum(0) / p.sum()
+            assert np.allclose(outs[n, h], ref, rtol=0, atol=1e-6), (t, h)
+
+
 def test_window_membership():
     cfg = O.OCfg(window=128)
     assert list(O.window_tokens(0, cfg)) == [0]
