@@ -258,6 +258,23 @@ dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
                                    const int32_t *pos_dev, int32_t B, int32_t *topk_dev,
                                    void *ws_dev, int64_t ws_bytes, void *stream);
 
+/*
+ * dsv4_index_topk_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with the workspace taken
+ * from a library-held device array of DSV4_NOALLOC_SCRATCH_BYTES per GPU
+ * (each GPU the library runs on keeps its copy until the process ends).  It
+ * calls no allocating routine.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  DSV4_ERR_WORKSPACE when the call would need
+ * more than the array (dsv4_workspace_bytes(cfg, B, max_blocks*128/m) >
+ * DSV4_NOALLOC_SCRATCH_BYTES); nothing is launched then.
+ */
+#define DSV4_NOALLOC_SCRATCH_BYTES (32 << 20)
+dsv4_status dsv4_index_topk_decode_noalloc(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *qI,
+                                           const float *w_dev, const int32_t *req_dev, const int32_t *pos_dev,
+                                           int32_t B, int32_t *topk_dev, void *stream);
+
 /* Same for the packed queries of a prefill chunk (positions pos0 + offset);
  * topk_dev is [total_tokens][k]. */
 dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache,

@@ -35,8 +35,9 @@ EXPORTS = [
     "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
     "dsv4_out_proj_pack", "dsv4_cache_dump_bytes", "dsv4_cache_dump", "dsv4_cache_load",
     "dsv4_mx_pack_bytes", "dsv4_mx_pack_weight", "dsv4_mx_linear", "dsv4_index_q_proj_ws_bytes",
-    "dsv4_index_q_proj", "dsv4_cache_read_entries",
+    "dsv4_index_q_proj", "dsv4_cache_read_entries", "dsv4_index_topk_decode_noalloc",
 ]
+DSV4_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Dsv4Error(RuntimeError):
@@ -84,6 +85,7 @@ def lib():
             "dsv4_compress_kv_decode": [cp, kp, vp, vp, vp, vp, vp, vp, i32, vp],
             "dsv4_compress_kv_prefill": [cp, kp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp],
             "dsv4_index_topk_decode": [cp, kp, vp, vp, vp, vp, i32, vp, vp, i64, vp],
+            "dsv4_index_topk_decode_noalloc": [cp, kp, vp, vp, vp, vp, i32, vp, vp],
             "dsv4_index_topk_prefill": [cp, kp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i64, vp],
             "dsv4_csa_attend_decode": [cp, kp, vp, vp, vp, vp, vp, vp, i32, i32, vp],
             "dsv4_hca_attend_decode": [cp, kp, vp, vp, vp, vp, vp, i32, i32, vp],
@@ -195,6 +197,12 @@ def dsv4_index_topk_decode(cfg, cache: LayerCache, qI, w, req, pos, topk_out, ws
     _ck("dsv4_index_topk_decode", lib().dsv4_index_topk_decode(
         ctypes.byref(cfg), ctypes.byref(cache.c), _p(qI), _p(w), _p(req), _p(pos), req.shape[0], _p(topk_out),
         _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dsv4_index_topk_decode_noalloc(cfg, cache: LayerCache, qI, w, req, pos, topk_out, stream=None):
+    _ck("dsv4_index_topk_decode_noalloc", lib().dsv4_index_topk_decode_noalloc(
+        ctypes.byref(cfg), ctypes.byref(cache.c), _p(qI), _p(w), _p(req), _p(pos), req.shape[0], _p(topk_out),
+        _stream(stream)))
 
 
 def dsv4_index_topk_prefill(cfg, cache: LayerCache, qI, w, cu_seqlens, req, pos0, total_tokens, topk_out, ws,

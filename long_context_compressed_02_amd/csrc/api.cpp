@@ -31,8 +31,8 @@ struct Timed {
     int id;
     hipStream_t s;
     hipEvent_t a = nullptr, b = nullptr;
-    Timed(int id_, hipStream_t s_) : id(id_), s(s_) {
-        if (g_timers[id].on) {
+    Timed(int id_, hipStream_t s_) : id(id_), s(s_) {   // id -1: never timed
+        if (id >= 0 && g_timers[id].on) {
             hipEventCreate(&a);
             hipEventCreate(&b);
             hipEventRecord(a, s);
@@ -235,7 +235,8 @@ dsv4_status dsv4_compress_kv_prefill(const dsv4_cfg *cfg, const dsv4_cache *cach
 
 static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, const void *qI, const float *w,
                                      const int32_t *req_q, const int32_t *pos_q, int nq, int32_t *topk_dev,
-                                     uint8_t *ws, int64_t ws_bytes, hipStream_t s, bool prefill) {
+                                     uint8_t *ws, int64_t ws_bytes, hipStream_t s, bool prefill,
+                                     bool timed = true) {
     const int64_t nmax = (int64_t)cache->max_blocks * L.epb;
     IndexWs W;
     const int64_t need = index_ws_bytes(L, nq, nmax, &W, ws);
@@ -243,18 +244,18 @@ static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, cons
     if (W.s_max > kTkMaxSeg) return DSV4_ERR_UNSUPPORTED;
     hipError_t e;
     if (L.idx_store == DSV4_STORE_FP32) {          // fp32 rows: the queries are scored as given
-        Timed tm(DSV4_K_INDEX_SCORE, s);
+        Timed tm(timed ? DSV4_K_INDEX_SCORE : -1, s);
         e = launch_score_f32(L, *cache, qI, w, req_q, pos_q, nq, W, s);
     } else {
         if (L.epb < 16) return DSV4_ERR_UNSUPPORTED;   // scoring reads 16-key runs inside one block
         e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
         if (e != hipSuccess) return DSV4_ERR_LAUNCH;
-        Timed tm(DSV4_K_INDEX_SCORE, s);
+        Timed tm(timed ? DSV4_K_INDEX_SCORE : -1, s);
         e = prefill ? launch_score_prefill(L, *cache, req_q, pos_q, nq, W, s)
                     : launch_score_decode(L, *cache, req_q, pos_q, nq, W, s);
     }
     if (e != hipSuccess) return DSV4_ERR_LAUNCH;
-    Timed tm(DSV4_K_TOPK, s);
+    Timed tm(timed ? DSV4_K_TOPK : -1, s);
     return hip_status(launch_topk(L, *cache, req_q, pos_q, nq, W, topk_dev, s));
 }
 
@@ -273,6 +274,57 @@ dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
     if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
     return index_topk_common(L, cache, qI, w_dev, req_dev, pos_dev, B, topk_dev, (uint8_t *)ws_dev, ws_bytes,
                              S(stream), false);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free decode indexer: its workspace is a file-scope device
+// array of kNoAllocScratch bytes, one copy per GPU (held until the process
+// ends).  Host code never uses the array's name as an address: each device's
+// address is taken once with hipGetSymbolAddress (with that device current)
+// and kept.  Every call on a GPU shares that GPU's array, so calls that
+// overlap on one GPU race; nothing in it needs to start at zero (every byte
+// a call reads was written earlier in the same call).
+namespace {
+constexpr int64_t kNoAllocScratch = (int64_t)DSV4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+dsv4_status scratch_of_current_device(uint8_t **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSV4_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSV4_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = (uint8_t *)g_scratch_ptr[dev];
+    return DSV4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dsv4_status dsv4_index_topk_decode_noalloc(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *qI,
+                                           const float *w_dev, const int32_t *req_dev, const int32_t *pos_dev,
+                                           int32_t B, int32_t *topk_dev, void *stream) {
+    Lay L;
+    dsv4_status st = make_layout(cfg, DSV4_CSA, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, DSV4_CSA)) != DSV4_OK) return st;
+    if (B < 0) return DSV4_ERR_INVALID_ARG;
+    if (B == 0) return DSV4_OK;
+    if (B > kMaxGridRows) return DSV4_ERR_UNSUPPORTED;
+    if (!qI || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
+    const int64_t need = index_ws_bytes(L, B, (int64_t)cache->max_blocks * L.epb, nullptr, nullptr);
+    if (need > kNoAllocScratch) return DSV4_ERR_WORKSPACE;
+    uint8_t *ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != DSV4_OK) return st;
+    return index_topk_common(L, cache, qI, w_dev, req_dev, pos_dev, B, topk_dev, ws, kNoAllocScratch, S(stream),
+                             false, false);
 }
 
 dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *qI,
