@@ -16,6 +16,7 @@ starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -50,6 +51,11 @@ def parse():
                          "for about 12 s (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (traffic calibration under --pmc)")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="decode: layer pairs in rotation (step s runs layer s %% L); 4 keeps each step's caches "
+                         "out of the 256 MB Infinity Cache, 1 measures a warm cache")
+    ap.add_argument("--calibrate", type=int, default=1,
+                    help="measure the device's copy / read bandwidth and matrix-core rates (1) or not (0)")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "hca_decode", "pair_1m", "out_proj", "index_q"],
                     help="decode: the CSA+HCA decode step, batch 32 at 128K (the headline); prefill: one "
@@ -85,37 +91,57 @@ def main():
     w = synth.CSA_DECODE_128K
     Bsz, ctx = a.batch, a.ctx
     steps, warm = a.steps, a.warmup
-    total_new = steps + warm
+    R = max(1, a.layers)
+    n_graph = warm + steps                        # steps captured as graphs (warm-up, then the timed K)
+    n_eager = 2 * steps                           # two eager passes with the per-kernel timers on
+    n_total = n_graph + n_eager
     mx = a.idx_store == "mxfp4"
     cfg = B.make_cfg(idx_store=B.DSV4_STORE_MXFP4 if mx else B.DSV4_STORE_FP8, **w.shape())
     policy = {"auto": B.DSV4_POLICY_AUTO, "hi": B.DSV4_POLICY_HI, "lo": B.DSV4_POLICY_LO}[a.policy]
     H, d, HI_, dI, k = w.n_heads, w.d, w.idx_heads, w.idx_dim, w.topk
 
     # ---------------------------------------------------------------- caches
-    need_blocks = (ctx + total_new + 127) // 128
+    # R layer pairs (CSA + HCA), each with its own pools at its own addresses:
+    # step s runs layer s % R at position ctx + s // R, as a model's decode
+    # walks its layers, so a layer's cache was last touched R-1 layer-steps
+    # earlier (R >= 3 puts more than the 256 MB Infinity Cache in between).
+    pos_max = ctx + (n_total + R - 1) // R + 1
+    need_blocks = (pos_max + 127) // 128
     bt = torch.arange(Bsz * need_blocks, dtype=torch.int32, device=dev).view(Bsz, need_blocks)
     # interleave requests' blocks so physical placement is not contiguous per request
     perm = torch.from_numpy(synth.permutation(w.wid, Bsz * need_blocks)).to(dev).to(torch.int32)
     bt = perm[bt.view(-1).long()].view(Bsz, need_blocks).contiguous()
-    csa = B.LayerCache(cfg, B.DSV4_CSA, Bsz, need_blocks, Bsz * need_blocks, bt)
-    hca = B.LayerCache(cfg, B.DSV4_HCA, Bsz, need_blocks, Bsz * need_blocks, bt)
     n_csa, n_hca = ctx // 4, ctx // 128
     t_setup = time.time()
-    for r in range(Bsz):
-        rr = torch.full((n_csa,), r, dtype=torch.int32, device=dev)
-        B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_ENTRY, rr, torch.arange(n_csa, dtype=torch.int32, device=dev),
-                                   torch.from_numpy(synth.entries(w, r, n_csa, 0)).to(dev))
-        B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_INDEX_KEY, rr,
-                                   torch.arange(n_csa, dtype=torch.int32, device=dev),
-                                   torch.from_numpy(synth.index_keys(w, r, n_csa)).to(dev))
-        rh = torch.full((n_hca,), r, dtype=torch.int32, device=dev)
-        B.dsv4_cache_write_entries(cfg, hca, B.DSV4_TARGET_ENTRY, rh, torch.arange(n_hca, dtype=torch.int32, device=dev),
-                                   torch.from_numpy(synth.entries(w, r, n_hca, 1)).to(dev))
-        kv, gate, kI, gI = synth.window_tokens(w, r, 128, 0)
-        bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
-        B.dsv4_state_write_tokens(cfg, csa, r, ctx - 128, bf(kv), bf(gate), bf(kI), bf(gI))
-        kv, gate, _, _ = synth.window_tokens(w, r, 128, 1)
-        B.dsv4_state_write_tokens(cfg, hca, r, ctx - 128, bf(kv), bf(gate))
+    layers = []
+    for li in range(R):
+        csa = B.LayerCache(cfg, B.DSV4_CSA, Bsz, need_blocks, Bsz * need_blocks, bt)
+        hca = B.LayerCache(cfg, B.DSV4_HCA, Bsz, need_blocks, Bsz * need_blocks, bt)
+        if li == 0:
+            for r in range(Bsz):
+                rr = torch.full((n_csa,), r, dtype=torch.int32, device=dev)
+                ar = torch.arange(n_csa, dtype=torch.int32, device=dev)
+                B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_ENTRY, rr, ar,
+                                           torch.from_numpy(synth.entries(w, r, n_csa, 0)).to(dev))
+                B.dsv4_cache_write_entries(cfg, csa, B.DSV4_TARGET_INDEX_KEY, rr, ar,
+                                           torch.from_numpy(synth.index_keys(w, r, n_csa)).to(dev))
+                rh = torch.full((n_hca,), r, dtype=torch.int32, device=dev)
+                B.dsv4_cache_write_entries(cfg, hca, B.DSV4_TARGET_ENTRY, rh,
+                                           torch.arange(n_hca, dtype=torch.int32, device=dev),
+                                           torch.from_numpy(synth.entries(w, r, n_hca, 1)).to(dev))
+                kv, gate, kI, gI = synth.window_tokens(w, r, 128, 0)
+                bf = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+                B.dsv4_state_write_tokens(cfg, csa, r, ctx - 128, bf(kv), bf(gate), bf(kI), bf(gI))
+                kv, gate, _, _ = synth.window_tokens(w, r, 128, 1)
+                B.dsv4_state_write_tokens(cfg, hca, r, ctx - 128, bf(kv), bf(gate))
+        else:                                     # the same contents at other addresses
+            c0, h0 = layers[0]
+            csa.entries.copy_(c0.entries)
+            csa.index_keys.copy_(c0.index_keys)
+            csa.state.copy_(c0.state)
+            hca.entries.copy_(h0.entries)
+            hca.state.copy_(h0.state)
+        layers.append((csa, hca))
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
@@ -124,92 +150,149 @@ def main():
     g.manual_seed(1234)
     rn = lambda *s: torch.randn(*s, generator=g, device=dev, dtype=torch.float32)
     steps_in = []
-    for s in range(total_new):
+    for s in range(n_total):
         steps_in.append(dict(
             kv=rn(Bsz, d).bfloat16(), gate=rn(Bsz, d).bfloat16(), kI=rn(Bsz, dI).bfloat16(), gI=rn(Bsz, dI).bfloat16(),
             kvh=rn(Bsz, d).bfloat16(), gateh=rn(Bsz, d).bfloat16(),
             q=rn(Bsz, H, d).bfloat16(), qh=rn(Bsz, H, d).bfloat16(),
             qI=rn(Bsz, HI_, dI).bfloat16(), w=rn(Bsz, HI_) / 8.0,
-            pos=torch.full((Bsz,), ctx + s, dtype=torch.int32, device=dev)))
+            pos=torch.full((Bsz,), ctx + s // R, dtype=torch.int32, device=dev)))
     req = torch.arange(Bsz, dtype=torch.int32, device=dev)
     sinks = torch.from_numpy(synth.sinks(w)).to(dev)
     ws = torch.empty(B.dsv4_workspace_bytes(cfg, Bsz, need_blocks * 32), dtype=torch.uint8, device=dev)
     topk = torch.empty((Bsz, k), dtype=torch.int32, device=dev)
     out_c = torch.empty((Bsz, H, d), dtype=torch.bfloat16, device=dev)
     out_h = torch.empty((Bsz, H, d), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
 
-    def step(s):
+    def step(s, stream, layer=None):
         x = steps_in[s]
+        csa, hca = layers[s % R if layer is None else layer]
         B.dsv4_compress_kv_decode(cfg, csa, x["kv"], x["gate"], x["kI"], x["gI"], req, x["pos"], stream)
         B.dsv4_index_topk_decode(cfg, csa, x["qI"], x["w"], req, x["pos"], topk, ws, stream)
         B.dsv4_csa_attend_decode(cfg, csa, x["q"], req, x["pos"], topk, sinks, out_c, policy, stream)
         B.dsv4_compress_kv_decode(cfg, hca, x["kvh"], x["gateh"], None, None, req, x["pos"], stream)
         B.dsv4_hca_attend_decode(cfg, hca, x["qh"], req, x["pos"], sinks, out_h, policy, stream)
 
-    for s in range(warm):
-        step(s)
-    torch.cuda.synchronize()
     for kid in range(B.DSV4_K_COUNT):
         B.dsv4_timer_enable(kid, False)
         B.dsv4_timer_read(kid, True)
-    # timed region (no per-kernel events: wall clock of K steps)
+    # the read-only calls once, eagerly, before capture (module load, LDS limits)
+    x0, (c0, h0) = steps_in[0], layers[0]
+    p_prev = torch.full((Bsz,), ctx - 1, dtype=torch.int32, device=dev)
+    cur = torch.cuda.current_stream()
+    B.dsv4_index_topk_decode(cfg, c0, x0["qI"], x0["w"], req, p_prev, topk, ws, cur)
+    B.dsv4_csa_attend_decode(cfg, c0, x0["q"], req, p_prev, topk, sinks, out_c, policy, cur)
+    B.dsv4_hca_attend_decode(cfg, h0, x0["qh"], req, p_prev, sinks, out_h, policy, cur)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- one hipGraph per step
+    graphs = []
+    cap = torch.cuda.Stream()
+    for s in range(n_graph):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            step(s, torch.cuda.current_stream())
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    for s in range(warm):
+        graphs[s].replay()
+    torch.cuda.synchronize()
+    # timed region: the K steps, each one graph replay, in order (state advances)
+    stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for s in range(warm, total_new):
-        step(s)
+    for s in range(warm, n_graph):
+        graphs[s].replay()
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
 
-    # per-kernel durations over a second pass of the same steps, HIP events
-    # recorded by the library on the launch stream around each kernel
-    for kid in range(B.DSV4_K_COUNT):
-        B.dsv4_timer_enable(kid, True)
-    for s in range(warm, total_new):
-        step(s)
-    torch.cuda.synchronize()
-    kern = {}
+    # median over >= 100 replays, each timed on its own: the K step graphs
+    # cycled (cold rotation; positions repeat, so the cache contents drift but
+    # every replay does a step's work), and one layer's step replayed back to
+    # back (warm: its data stays in the Infinity Cache)
+    def replay_median(order):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i, s in enumerate(order):
+            graphs[s].replay()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(len(order))]))
+    n_rep = max(100, steps)
+    timed = list(range(warm, n_graph))
+    med_cold = replay_median([timed[i % len(timed)] for i in range(n_rep)])
+    med_warm = replay_median([timed[0]] * n_rep)
+
+    # per-kernel durations: eager steps continuing the timeline with the
+    # library's HIP-event timers on the launch stream -- K rotating steps
+    # (cold), then K steps on one layer (warm)
     names = {B.DSV4_K_COMPRESS: "compress", B.DSV4_K_INDEX_SCORE: "index_score", B.DSV4_K_TOPK: "topk",
              B.DSV4_K_ATTEND: "attend"}
-    for kid, nm in names.items():
-        ms, n = B.dsv4_timer_read(kid, True)
-        B.dsv4_timer_enable(kid, False)
-        kern[nm] = dict(total_ms=ms, launches=n, avg_us=1e3 * ms / max(n, 1))
+
+    def timer_pass(ss, layer):
+        for kid in range(B.DSV4_K_COUNT):
+            B.dsv4_timer_enable(kid, True)
+        for s in ss:
+            step(s, stream, layer)
+        torch.cuda.synchronize()
+        out = {}
+        for kid, nm in names.items():
+            ms, n = B.dsv4_timer_read(kid, True)
+            out[nm] = dict(total_ms=ms, launches=n, avg_us=1e3 * ms / max(n, 1))
+        for kid in range(B.DSV4_K_COUNT):
+            B.dsv4_timer_enable(kid, False)
+        return out
+    kern = timer_pass(range(n_graph, n_graph + steps), None)
+    kern_warm = timer_pass(range(n_graph + steps, n_total), 0)
 
     if a.calib_copy_mib:
+        # a copy of known size through the calibration library's copy kernel
+        # (the traffic counters' calibration under rocprofv3 --pmc)
         src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        calib_lib().dsv4calib_copy_gbs(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                       src.numel(), 0)
         torch.cuda.synchronize()
+        del src, dst
+    cal = calibrate() if a.calibrate else None
 
     # ---------------------------------------------------------------- roofline
-    # algorithmic work per step (positions ctx+s, averaged over the timed steps)
-    n_vis = np.mean([(ctx + s + 1) // 4 for s in range(warm, total_new)])
-    n_h = np.mean([(ctx + s + 1) // 128 for s in range(warm, total_new)])
+    # algorithmic work per step (positions of the eager cold pass, averaged)
+    tpos = [ctx + s // R for s in range(n_graph, n_graph + steps)]
+    n_vis = np.mean([(t + 1) // 4 for t in tpos])
+    n_h = np.mean([(t + 1) // 128 for t in tpos])
     row_b = (dI // 2 if mx else dI) + 4                 # E2M1 codes + 4 E8M0 bytes, or E4M3 codes + fp32 scale
     score_bytes = Bsz * n_vis * (row_b + 4) + Bsz * HI_ * row_b       # keys+scales read, scores written, queries
-    score_flops = Bsz * n_vis * HI_ * dI * 2
     rec_b = (d - 64) + 2 * 64 + 4                        # 580 B per stored record
     csa_recs = Bsz * (k + 128)
     hca_recs = Bsz * (n_h + 128)
     attend_bytes_step = (csa_recs + hca_recs) * rec_b + 2 * (2 * Bsz * H * d * 2)
     attend_flops_step = (csa_recs + hca_recs) * H * 4 * d
     per_launch = {
-        "index_score": dict(bound="hbm", work=score_bytes, unit="GB/s", peak=HBM_PEAK_GBS),
-        "attend": dict(bound="mfma", work=attend_flops_step / 2, unit="TFLOP/s", peak=BF16_PEAK_TFLOPS),
+        "index_score": dict(bound="hbm", work=score_bytes, unit="GB/s", peak=HBM_PEAK_GBS,
+                            measured=None if cal is None else cal["read_GBps"]),
+        "attend": dict(bound="mfma", work=attend_flops_step / 2, unit="TFLOP/s", peak=BF16_PEAK_TFLOPS,
+                       measured=None if cal is None else max(cal["bf16_TFLOPs"], cal["bf16_32x32_TFLOPs"])),
     }
-    dom = max(kern, key=lambda n_: kern[n_]["total_ms"])
-    if dom not in per_launch:
-        dom = "index_score"
-    pl = per_launch[dom]
-    avg_s = kern[dom]["avg_us"] * 1e-6
-    achieved = pl["work"] / avg_s / (1e9 if pl["unit"] == "GB/s" else 1e12)
-    roof = {"kernel": {"index_score": "k_index_score_decode", "attend": "k_attend"}[dom], "bound": pl["bound"],
-            "achieved": round(achieved, 2), "peak": pl["peak"], "unit": pl["unit"],
-            "frac": round(achieved / pl["peak"], 4),
-            "traffic": measured_traffic() if dom == "attend" and (Bsz, ctx) == (32, 131072) else None}
+
+    def roofline(kn):
+        dom = max(kn, key=lambda n_: kn[n_]["total_ms"])
+        if dom not in per_launch:
+            dom = "index_score"
+        pl = per_launch[dom]
+        achieved = pl["work"] / (kn[dom]["avg_us"] * 1e-6) / (1e9 if pl["unit"] == "GB/s" else 1e12)
+        kname = {"index_score": "k_index_score_decode", "attend": "k_attend_lo"}[dom]
+        out = {"kernel": kname, "bound": pl["bound"], "achieved": round(achieved, 2), "peak": pl["peak"],
+               "unit": pl["unit"], "frac": round(achieved / pl["peak"], 4),
+               "traffic": measured_traffic(dom) if (Bsz, ctx, R, mx) == (32, 131072, 4, False) else None}
+        if pl["measured"]:
+            out["peak_measured"] = round(pl["measured"], 1)
+            out["frac_measured"] = round(achieved / pl["measured"], 4)
+        return out
+    roof = roofline(kern)
     step_bytes = score_bytes + attend_bytes_step
     value = Bsz / (ms_step * 1e-3)
 
@@ -224,15 +307,22 @@ def main():
         "dtype": "mxfp4/fp8/bf16" if mx else "fp8/bf16", "data": "synthetic",
         "config": {"workload": f"V4-Pro CSA+HCA layer-pair decode, batch {Bsz} x {ctx // 1024}K ctx "
                                f"({ctx // 4} CSA / {ctx // 128} HCA entries per request), top-{k}, "
-                               f"{H} heads x d {d}, window 128" + (", MXFP4 indexer" if mx else ""),
+                               f"{H} heads x d {d}, window 128" + (", MXFP4 indexer" if mx else "") +
+                               f"; {R} layer pairs in rotation (each step's caches cold), one hipGraph per step",
                    "batch": Bsz, "ctx": ctx, "topk": k, "heads": H, "d": d, "policy": a.policy,
-                   "idx_store": a.idx_store},
+                   "idx_store": a.idx_store, "layers_in_rotation": R},
         "roofline": roof,
         "cpu_baseline": cpu,
         "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern.items()},
         "launches_per_step": {n_: v["launches"] / steps for n_, v in kern.items()},
+        "graph_replay_median_us": {"cold": round(1e3 * med_cold, 2), "warm": round(1e3 * med_warm, 2),
+                                   "replays": n_rep},
+        "warm": {"queries_per_s": round(Bsz / (med_warm * 1e-3), 1),
+                 "breakdown_us": {n_: round(v["avg_us"], 2) for n_, v in kern_warm.items()},
+                 "roofline": roofline(kern_warm)},
         "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "attend_TFLOPs": round(attend_flops_step / (kern["attend"]["total_ms"] / steps * 1e-3) / 1e12, 1),
+        "calibration": cal,
         "setup_s": round(t_setup, 1),
     }
     print(json.dumps(res), flush=True)
@@ -610,24 +700,75 @@ def decode_mix_main(a):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "k_attend_decode_128k_b32_hbm_traffic.txt")
-ATTEND_SRC = os.path.join(HERE, "long_context_compressed_02_amd", "csrc", "k_attend.hip")
+CSRC = os.path.join(HERE, "long_context_compressed_02_amd", "csrc")
+# per kernel: the committed traffic summary of the headline workload and the
+# source whose SHA-256 it records
+TRAFFIC = {
+    "attend": (os.path.join(HERE, "profiles", "k_attend_decode_128k_b32_hbm_traffic.txt"),
+               os.path.join(CSRC, "k_attend.hip"), "k_attend_src_sha256"),
+    "index_score": (os.path.join(HERE, "profiles", "k_index_score_decode_128k_b32_hbm_traffic.txt"),
+                    os.path.join(CSRC, "k_index.hip"), "k_index_src_sha256"),
+}
 
 
-def measured_traffic():
-    """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, calibrated on a
-    plain copy) from the committed rocprofv3 summary of this workload -- only
-    if the summary was taken on the attention source as it is now."""
+def measured_traffic(kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a plain
+    copy) from the committed rocprofv3 summary of this workload -- only if the
+    summary was taken on the kernel's source as it is now."""
+    summary, source, key = TRAFFIC[kernel]
     try:
-        text = open(TRAFFIC_SUMMARY).read()
-        src = open(ATTEND_SRC, "rb").read()
+        text = open(summary).read()
+        src = open(source, "rb").read()
     except OSError:
         return None
     m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    h = re.search(r"k_attend_src_sha256: ([0-9a-f]+)", text)
+    h = re.search(key + r": ([0-9a-f]+)", text)
     if not m or not h or hashlib.sha256(src).hexdigest() != h.group(1):
         return None
     return int(m.group(1))
+
+
+_calib = None
+
+
+def calib_lib():
+    global _calib
+    if _calib is None:
+        path = os.path.join(HERE, "long_context_compressed_02_amd", "libdsv4calib.so")
+        L = ctypes.CDLL(path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.dsv4calib_copy_gbs.argtypes = [vp, vp, i64, i32]
+        L.dsv4calib_read_gbs.argtypes = [vp, i64, vp, i32]
+        L.dsv4calib_mfma_tflops.argtypes = [i32, i32, i32, vp, i32]
+        for f in (L.dsv4calib_copy_gbs, L.dsv4calib_read_gbs, L.dsv4calib_mfma_tflops):
+            f.restype = ctypes.c_double
+        _calib = L
+    return _calib
+
+
+def calibrate():
+    """The device's own rates: a 1 GiB copy and a 1 GiB read (best of 5), and
+    back-to-back matrix instructions from every SIMD (bf16 16x16x32, fp8 and
+    fp4 16x16x128, bf16 32x32x16, fp8 32x32x64; best of 3).  The measured bf16
+    peak a kernel is priced against is the faster bf16 shape."""
+    import torch
+    L = calib_lib()
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    copy = L.dsv4calib_copy_gbs(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, 5)
+    read = L.dsv4calib_read_gbs(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()), 5)
+    del src, dst
+    blocks = 1024
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    tf = [L.dsv4calib_mfma_tflops(kd, blocks, 256, ctypes.c_void_p(out.data_ptr()), 3) for kd in (0, 1, 2, 3, 4)]
+    torch.cuda.synchronize()
+    return {"copy_GBps": round(copy, 1), "read_GBps": round(read, 1), "bf16_TFLOPs": round(tf[0], 1),
+            "fp8_TFLOPs": round(tf[1], 1), "fp4_TFLOPs": round(tf[2], 1), "bf16_32x32_TFLOPs": round(tf[3], 1),
+            "fp8_32x32_TFLOPs": round(tf[4], 1),
+            "spec": {"hbm_GBps": HBM_PEAK_GBS, "bf16_TFLOPs": BF16_PEAK_TFLOPS, "fp8_TFLOPs": FP8_PEAK_TFLOPS,
+                     "fp4_TFLOPs": FP4_PEAK_TFLOPS}}
 
 
 def cpu_baseline(w, nreq, t, idx_mode=1, budget_s=12.0, max_queries=2000):
