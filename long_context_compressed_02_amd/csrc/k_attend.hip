@@ -191,6 +191,15 @@ __device__ __forceinline__ void state_clear(AttnState<N> &s) {
     for (int i = 0; i < N; ++i) s.O[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// The running max of a subset's online softmax moves only when a chunk's
+// largest logit exceeds it by more than 8 (base-2 units), so most chunks keep
+// alpha = 1 and skip rescaling the accumulators; the weights 2^(l - m) then
+// stay below 2^8, well inside bf16 and fp32.  The result is the same softmax
+// (the common factor cancels in the final normalisation).
+__device__ __forceinline__ float lazy_max(float m, float cmax) {
+    return (m == -INFINITY || cmax > m + 8.0f) ? fmaxf(m, cmax) : m;
+}
+
 // fold(a, b): the two partial softmaxes rescaled to their common max.
 __device__ __forceinline__ void fold_scales(float ma, float la, float mb, float lb, float &m, float &l,
                                             float &fa, float &fb) {
@@ -462,7 +471,7 @@ __global__ __launch_bounds__(64 * kParts * NSW) __attribute__((amdgpu_waves_per_
     #pragma unroll
                 for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, lg[rb][i]);
             cmax = head_max(cmax);
-            const float m_new = fmaxf(S.m, cmax);
+            const float m_new = lazy_max(S.m, cmax);
             float p[2][4];
             float alpha = 1.0f;
             if (m_new == -INFINITY) {
@@ -980,7 +989,7 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, lg[rb][i]);
         cmax = head_max(cmax);
-        const float m_new = fmaxf(S.m, cmax);
+        const float m_new = lazy_max(S.m, cmax);
         float p[2][4];
         float alpha = 1.0f;
         if (m_new == -INFINITY) {
