@@ -419,6 +419,34 @@ dsv4_status dsv4_index_q_proj(const dsv4_cfg *cfg, const void *x, int32_t T, int
                               void *stream);
 
 /*
+ * The per-token projections that feed the compressors and the indexer's head
+ * weights, on the same low-precision path as dsv4_index_q_proj (the pages name
+ * the indexer's activations FP4 and the prefill configuration "FP4 weights,
+ * FP8 activations": rqlyzj.com FP4 QAT section, xiaoyuzhoufm.com 2.1; the
+ * compressors take a kv vector and gate logits per token and, for CSA, the
+ * indexer's key-side vector and gate: vastsailsolution.com V4 article, CSA and
+ * HCA sections).  x is quantised to MXFP8 once; then, each as dsv4_mx_linear
+ * (no split-K, a token's outputs bitwise the same in any batch):
+ *   kv   = x . Wkv^T   [T][d]        gate = x . Wg^T   [T][d]
+ *   kI   = x . WkI^T   [T][idx_dim]  gI   = x . WgI^T  [T][idx_dim]   (CSA only)
+ *   w    = x . Ww^T    [T][idx_heads] fp32                           (CSA, optional)
+ * kv, gate, kI, gI in cfg->act_dtype (bf16 rounds to nearest even): the
+ * inputs of dsv4_compress_kv_{decode,prefill}; w the head weights of
+ * dsv4_index_topk_{decode,prefill}.
+ *   kind       DSV4_CSA or DSV4_HCA (HCA: wki_p, wgi_p, ww_p, kI, gI, w NULL)
+ *   x          [T][hidden] bf16; hidden a multiple of 128, T <= 2^20
+ *   w*_p       weights [rows][hidden] bf16 packed by dsv4_mx_pack_weight
+ *   ww_p, w    both NULL (no head-weight projection) or both set; idx_heads a
+ *              multiple of 16 for it (DSV4_ERR_UNSUPPORTED otherwise)
+ *   ws         at least dsv4_kv_proj_ws_bytes bytes, 256-byte aligned
+ */
+dsv4_status dsv4_kv_proj_ws_bytes(const dsv4_cfg *cfg, int32_t T, int32_t hidden, int64_t *out);
+dsv4_status dsv4_kv_proj(const dsv4_cfg *cfg, int32_t kind, const void *x, int32_t T, int32_t hidden,
+                         const void *wkv_p, const void *wg_p, const void *wki_p, const void *wgi_p, const void *ww_p,
+                         void *kv, void *gate, void *kI, void *gI, float *w, void *ws, int64_t ws_bytes,
+                         void *stream);
+
+/*
  * Cache fill (benchmarks, tests, reloading a saved prefix).  Writes n entries
  * (target DSV4_TARGET_ENTRY: a KV record, RoPE at the entry's block-end
  * position m*j+m-1 then stored; DSV4_TARGET_INDEX_KEY: a CSA index key,

@@ -35,7 +35,8 @@ EXPORTS = [
     "dsv4_timer_enable", "dsv4_timer_read", "dsv4_topk_rows_ws_bytes", "dsv4_topk_rows", "dsv4_out_proj",
     "dsv4_out_proj_pack", "dsv4_cache_dump_bytes", "dsv4_cache_dump", "dsv4_cache_load",
     "dsv4_mx_pack_bytes", "dsv4_mx_pack_weight", "dsv4_mx_linear", "dsv4_index_q_proj_ws_bytes",
-    "dsv4_index_q_proj", "dsv4_cache_read_entries", "dsv4_index_topk_decode_noalloc",
+    "dsv4_index_q_proj", "dsv4_cache_read_entries", "dsv4_index_topk_decode_noalloc", "dsv4_kv_proj_ws_bytes",
+    "dsv4_kv_proj",
 ]
 DSV4_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -106,6 +107,8 @@ def lib():
             "dsv4_mx_linear": [vp, i32, i32, vp, i32, vp, i64, vp, i32, vp],
             "dsv4_index_q_proj_ws_bytes": [cp, i32, i32, i32, ctypes.POINTER(i64)],
             "dsv4_index_q_proj": [cp, vp, i32, i32, i32, vp, vp, vp, i64, vp, vp],
+            "dsv4_kv_proj_ws_bytes": [cp, i32, i32, ctypes.POINTER(i64)],
+            "dsv4_kv_proj": [cp, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp],
             "dsv4_timer_enable": [i32, i32],
             "dsv4_timer_read": [i32, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)],
         }
@@ -338,6 +341,20 @@ def dsv4_index_q_proj(cfg, x, dc: int, wdq_p, wuq_p, ws, qI, stream=None):
     _ck("dsv4_index_q_proj", lib().dsv4_index_q_proj(ctypes.byref(cfg), _p(x), x.shape[0], x.shape[1], dc,
                                                      _p(wdq_p), _p(wuq_p), _p(ws), ws.numel() * ws.element_size(),
                                                      _p(qI), _stream(stream)))
+
+
+def dsv4_kv_proj_ws_bytes(cfg, T: int, hidden: int) -> int:
+    out = ctypes.c_int64()
+    _ck("dsv4_kv_proj_ws_bytes", lib().dsv4_kv_proj_ws_bytes(ctypes.byref(cfg), T, hidden, ctypes.byref(out)))
+    return out.value
+
+
+def dsv4_kv_proj(cfg, kind: int, x, wkv_p, wg_p, wki_p, wgi_p, ww_p, kv, gate, kI, gI, w, ws, stream=None):
+    """x bf16 [T, hidden]; packed weights (None where absent); outputs as documented."""
+    T, hidden = x.shape
+    _ck("dsv4_kv_proj", lib().dsv4_kv_proj(
+        ctypes.byref(cfg), kind, _p(x), T, hidden, _p(wkv_p), _p(wg_p), _p(wki_p), _p(wgi_p), _p(ww_p), _p(kv),
+        _p(gate), _p(kI), _p(gI), _p(w), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dsv4_timer_enable(kernel_id: int, on: bool = True):

@@ -666,6 +666,49 @@ dsv4_status dsv4_index_q_proj(const dsv4_cfg *cfg, const void *x, int32_t T, int
     return mx_linear(cq, T, dc, wuq_p, nq, act, qI, nq, cfg->act_dtype == DSV4_DT_F32, S(stream));
 }
 
+dsv4_status dsv4_kv_proj_ws_bytes(const dsv4_cfg *cfg, int32_t T, int32_t hidden, int64_t *out) {
+    if (!cfg || !out || T < 0) return DSV4_ERR_INVALID_ARG;
+    if (!mx_shape_ok(T, 16, hidden)) return DSV4_ERR_INVALID_ARG;
+    *out = mx_pack_bytes(T, hidden, true);
+    return DSV4_OK;
+}
+
+dsv4_status dsv4_kv_proj(const dsv4_cfg *cfg, int32_t kind, const void *x, int32_t T, int32_t hidden,
+                         const void *wkv_p, const void *wg_p, const void *wki_p, const void *wgi_p, const void *ww_p,
+                         void *kv, void *gate, void *kI, void *gI, float *w, void *ws, int64_t ws_bytes,
+                         void *stream) {
+    Lay L;
+    dsv4_status st = make_layout(cfg, kind, &L);
+    if (st != DSV4_OK) return st;
+    if (T < 0 || !mx_shape_ok(T, L.d, hidden)) return DSV4_ERR_INVALID_ARG;
+    const bool csa = kind == DSV4_CSA;
+    if (csa ? (!wki_p || !wgi_p || !kI || !gI) : (wki_p || wgi_p || kI || gI || ww_p || w)) return DSV4_ERR_INVALID_ARG;
+    if ((ww_p == nullptr) != (w == nullptr)) return DSV4_ERR_INVALID_ARG;
+    if (ww_p && L.HI % 16) return DSV4_ERR_UNSUPPORTED;          // the products take whole 16-row blocks
+    if (T == 0) return DSV4_OK;
+    if (!x || !wkv_p || !wg_p || !kv || !gate) return DSV4_ERR_INVALID_ARG;
+    const void *ptrs[] = {x, wkv_p, wg_p, wki_p, wgi_p, ww_p, kv, gate, kI, gI, w};
+    for (const void *q : ptrs)
+        if ((uintptr_t)q & 15) return DSV4_ERR_INVALID_ARG;
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < mx_pack_bytes(T, hidden, true)) return DSV4_ERR_WORKSPACE;
+    if ((T + 127) / 128 > 65535) return DSV4_ERR_UNSUPPORTED;
+    const int of32 = L.act == DSV4_DT_F32;
+    hipStream_t s = S(stream);
+    Timed tm(DSV4_K_MX, s);
+    // x quantised to MXFP8 once, then one product per projection
+    uint8_t *act = (uint8_t *)ws;
+    if (launch_mx_quant((const uint16_t *)x, T, hidden, true, act, s) != hipSuccess) return DSV4_ERR_LAUNCH;
+    struct P { const void *wp; void *out; int n; int f32; } prods[] = {
+        {wkv_p, kv, L.d, of32}, {wg_p, gate, L.d, of32}, {wki_p, kI, L.dI, of32}, {wgi_p, gI, L.dI, of32},
+        {ww_p, w, L.HI, 1}};
+    for (const P &p : prods) {
+        if (!p.wp) continue;
+        if (launch_mx_gemm(act, (const uint8_t *)p.wp, T, p.n, hidden, p.out, p.n, p.f32, s) != hipSuccess)
+            return DSV4_ERR_LAUNCH;
+    }
+    return DSV4_OK;
+}
+
 dsv4_status dsv4_timer_enable(int32_t kernel_id, int32_t on) {
     if (kernel_id < 0 || kernel_id >= DSV4_K_COUNT) return DSV4_ERR_INVALID_ARG;
     g_timers[kernel_id].on = on != 0;

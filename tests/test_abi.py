@@ -268,3 +268,25 @@ def test_projection_empty_batches_are_no_ops():
     cfg = B.make_cfg()
     assert L.dsv4_out_proj(ctypes.byref(cfg), 16, 1024, 7168, None, None, None, None, None, 0, None) == B.DSV4_OK
     assert L.dsv4_index_q_proj(ctypes.byref(cfg), None, 0, 7168, 1024, None, None, None, 0, None, None) == B.DSV4_OK
+
+
+def test_kv_proj_workspace_and_checks():
+    """The projections' workspace is the MXFP8 copy of x; argument errors come
+    back before anything is launched."""
+    L = B.lib()
+    cfg = B.make_cfg()
+    assert B.dsv4_kv_proj_ws_bytes(cfg, 32, 7168) == B.dsv4_mx_pack_bytes(32, 7168, True)
+    p = ctypes.c_void_p(FAKE)
+    ws_need = B.dsv4_kv_proj_ws_bytes(cfg, 4, 256)
+    kp = lambda kind, wki, wgi, ww, kI, gI, w, ws_bytes=ws_need, x=p: L.dsv4_kv_proj(
+        ctypes.byref(cfg), kind, x, 4, 256, p, p, wki, wgi, ww, p, p, kI, gI, w, p, ws_bytes, None)
+    assert kp(B.DSV4_HCA, p, p, None, p, p, None) == B.DSV4_ERR_INVALID_ARG       # HCA: no index projections
+    assert kp(B.DSV4_CSA, None, None, None, None, None, None) == B.DSV4_ERR_INVALID_ARG
+    assert kp(B.DSV4_CSA, p, p, p, p, p, None) == B.DSV4_ERR_INVALID_ARG          # ww without w
+    assert kp(B.DSV4_CSA, p, p, p, p, p, p, ws_need - 16) == B.DSV4_ERR_WORKSPACE
+    assert kp(B.DSV4_CSA, p, p, p, p, p, p, x=ctypes.c_void_p(FAKE + 8)) == B.DSV4_ERR_INVALID_ARG
+    tiny = B.make_cfg(d=64, d_rope=16, n_heads=8, window=16, idx_heads=4, idx_dim=32, topk=32)
+    assert L.dsv4_kv_proj(ctypes.byref(tiny), B.DSV4_CSA, p, 4, 256, p, p, p, p, p, p, p, p, p, p, p, ws_need,
+                          None) == B.DSV4_ERR_UNSUPPORTED                          # 4 head weights: not whole blocks
+    assert L.dsv4_kv_proj(ctypes.byref(cfg), B.DSV4_CSA, p, 4, 200, p, p, p, p, None, p, p, p, p, None, p,
+                          ws_need, None) == B.DSV4_ERR_INVALID_ARG                 # hidden not a multiple of 128

@@ -257,3 +257,133 @@ def test_index_q_proj_feeds_the_indexer():
         idx, s = O.csa_select(pos[r], qx[r], wx[r], keys[r], oc)
         swaps += Hh.topk_match(got[r], idx, s, k)
     assert swaps <= 2
+
+
+# ------------------------------------------------------------------ projections feeding the compressors
+def _kv_proj_case(shape, T, hidden, seed, kind=B.DSV4_CSA, with_w=True):
+    cfg, oc = Hh.cfgs(shape)
+    g = np.random.default_rng([31, seed])
+    s = 1.0 / np.sqrt(hidden)
+    csa = kind == B.DSV4_CSA
+    W = {"kv": _bf16(g.standard_normal((oc.d, hidden)) * s), "g": _bf16(g.standard_normal((oc.d, hidden)) * s)}
+    if csa:
+        W["kI"] = _bf16(g.standard_normal((oc.idx_dim, hidden)) * s)
+        W["gI"] = _bf16(g.standard_normal((oc.idx_dim, hidden)) * s)
+        if with_w:
+            W["w"] = _bf16(g.standard_normal((oc.idx_heads, hidden)) * s / 8)
+    P = {k: _pack(v) for k, v in W.items()}
+    x = _bf16(g.standard_normal((T, hidden)))
+    return cfg, oc, W, P, x
+
+
+def _kv_proj(cfg, kind, x, P, oc):
+    T, hidden = x.shape
+    csa = kind == B.DSV4_CSA
+    out = {"kv": torch.empty((T, oc.d), dtype=torch.bfloat16, device=DEV),
+           "g": torch.empty((T, oc.d), dtype=torch.bfloat16, device=DEV)}
+    if csa:
+        out["kI"] = torch.empty((T, oc.idx_dim), dtype=torch.bfloat16, device=DEV)
+        out["gI"] = torch.empty((T, oc.idx_dim), dtype=torch.bfloat16, device=DEV)
+        if "w" in P:
+            out["w"] = torch.empty((T, oc.idx_heads), dtype=torch.float32, device=DEV)
+    ws = torch.empty(B.dsv4_kv_proj_ws_bytes(cfg, T, hidden), dtype=torch.uint8, device=DEV)
+    B.dsv4_kv_proj(cfg, kind, x, P["kv"], P["g"], P.get("kI"), P.get("gI"), P.get("w"), out["kv"], out["g"],
+                   out.get("kI"), out.get("gI"), out.get("w"), ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_bf16(out, x, w):
+    """bf16 outputs: the fp32 result (within the summation bound) rounded to
+    nearest even -- at most half a bf16 step (2^-8 of the value) more."""
+    xs = _f64(x)
+    ref = O.mx_linear(xs, _f64(w))
+    mag = np.abs(O.mxfp8_rows(xs)) @ np.abs(O.mxfp4_rows(_f64(w))).T
+    err = np.abs(_f64(out) - ref)
+    bound = TOL * mag + 2.0 ** -8 * (np.abs(ref) + TOL * mag) + 1e-37
+    print(f"  max err / bound {np.max(err / bound):.3f}", flush=True)
+    assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
+def test_kv_proj_production_shape(kind):
+    """V4-Pro widths (hidden 7168 -> kv, gate 512; kI, gI 128; w 64 heads) on
+    MXFP4 weights and MXFP8 activations against the oracle's MX linear map; a
+    token's outputs are the same bytes alone and inside the batch."""
+    shape = synth.CSA_DECODE_128K.shape()
+    T, hidden = 300, 7168
+    cfg, oc, W, P, x = _kv_proj_case(shape, T, hidden, 1, kind)
+    out = _kv_proj(cfg, kind, x, P, oc)
+    for k, o in out.items():
+        print(f"  {k}:", end="", flush=True)
+        if k == "w":
+            _check_f32(o, x, W[k])
+        else:
+            _check_bf16(o, x, W[k])
+    for M, off in ((1, 0), (32, 100), (7, 293)):
+        part = _kv_proj(cfg, kind, x[off:off + M].contiguous(), P, oc)
+        for k in out:
+            assert torch.equal(part[k].view(torch.int16), out[k][off:off + M].view(torch.int16)), (k, M)
+
+
+def test_kv_proj_feeds_the_compressor_and_indexer():
+    """The projections' outputs go straight into the compressor (prefill of a
+    300-token chunk, then one decode step) and the decode indexer: the cache
+    holds the same bytes as when the same values come from the host, its
+    entries and index keys are the oracle's compression of those values (up to
+    rounding-boundary flips), and the top-k equals the oracle's selection with
+    the projected head weights."""
+    shape = dict(synth.CSA_DECODE_128K.shape())
+    T, hidden = 301, 1024
+    cfg, oc, W, P, x = _kv_proj_case(shape, T, hidden, 2)
+    out = _kv_proj(cfg, B.DSV4_CSA, x, P, oc)
+    C = T - 1
+    bt, nb, mb = Hh.block_table([T], seed=11)
+    caches = [B.LayerCache(cfg, B.DSV4_CSA, 1, mb, nb, bt) for _ in range(2)]
+    feeds = [out, {k: v.cpu().to(DEV) for k, v in out.items()}]   # the same values through host memory
+    cu, r0, p0 = Hh.i32([0, C]), Hh.i32([0]), Hh.i32([0])
+    for cache, f in zip(caches, feeds):
+        win = torch.empty((C + oc.window) * cache.layout.record_bytes, dtype=torch.uint8, device=DEV)
+        B.dsv4_compress_kv_prefill(cfg, cache, f["kv"][:C].contiguous(), f["g"][:C].contiguous(),
+                                   f["kI"][:C].contiguous(), f["gI"][:C].contiguous(), cu, r0, p0, C, win)
+        B.dsv4_compress_kv_decode(cfg, cache, f["kv"][C:], f["g"][C:], f["kI"][C:], f["gI"][C:], r0, Hh.i32([C]))
+    torch.cuda.synchronize()
+    for a in ("entries", "index_keys", "state"):
+        assert torch.equal(getattr(caches[0], a), getattr(caches[1], a)), a
+    vals = {k: _f64(v) for k, v in out.items()}
+    ne = T // oc.m_csa
+    ents = O.entries_from_pool("csa", vals["kv"], vals["g"], range(ne), oc)
+    keys = O.index_keys_from_pool(vals["kI"], vals["gI"], range(ne), oc)
+    Hh.assert_records_close(Hh.read_back(cfg, caches[0], B.DSV4_TARGET_ENTRY, 0, range(ne)), ents, oc.d_rope)
+    keys_gpu = Hh.read_back(cfg, caches[0], B.DSV4_TARGET_INDEX_KEY, 0, range(ne))
+    Hh.assert_records_close(keys_gpu, keys, 0)
+    # the indexer of the last token with the projected head weights
+    _, qI, _ = synth.decode_queries(synth.CSA_DECODE_128K, 1, sub=77)
+    qIt, qIx = Hh.act_tensor(qI, B.DSV4_DT_BF16)
+    oc_k = O.OCfg(**{**shape, "topk": 32})
+    cfg_k, _ = Hh.cfgs(shape, topk=32)
+    ws = torch.empty(B.dsv4_workspace_bytes(cfg_k, 1, mb * 32), dtype=torch.uint8, device=DEV)
+    tk = torch.empty((1, 32), dtype=torch.int32, device=DEV)
+    B.dsv4_index_topk_decode(cfg_k, caches[0], qIt, out["w"][C:].contiguous(), r0, Hh.i32([C]), tk, ws)
+    torch.cuda.synchronize()
+    idx, s = O.csa_select(C, qIx[0], vals["w"][C], keys_gpu, oc_k)
+    Hh.topk_match(tk.cpu().numpy()[0], idx, s, 32)
+
+
+def test_kv_proj_argument_checks():
+    shape = synth.CSA_DECODE_128K.shape()
+    cfg, oc, W, P, x = _kv_proj_case(shape, 4, 256, 3)
+    ws = torch.empty(B.dsv4_kv_proj_ws_bytes(cfg, 4, 256), dtype=torch.uint8, device=DEV)
+    o = {k: torch.empty((4, 512), dtype=torch.bfloat16, device=DEV) for k in ("kv", "g", "kI", "gI")}
+    wout = torch.empty((4, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(B.Dsv4Error):          # HCA takes no index-key projections
+        B.dsv4_kv_proj(cfg, B.DSV4_HCA, x, P["kv"], P["g"], P["kI"], P["gI"], None, o["kv"], o["g"], o["kI"],
+                       o["gI"], None, ws)
+    with pytest.raises(B.Dsv4Error):          # CSA needs them
+        B.dsv4_kv_proj(cfg, B.DSV4_CSA, x, P["kv"], P["g"], None, None, None, o["kv"], o["g"], None, None, None, ws)
+    with pytest.raises(B.Dsv4Error):          # head weights need both the packed weight and the output
+        B.dsv4_kv_proj(cfg, B.DSV4_CSA, x, P["kv"], P["g"], P["kI"], P["gI"], P["w"], o["kv"], o["g"], o["kI"],
+                       o["gI"], None, ws)
+    with pytest.raises(B.Dsv4Error):          # a short workspace
+        B.dsv4_kv_proj(cfg, B.DSV4_CSA, x, P["kv"], P["g"], P["kI"], P["gI"], P["w"], o["kv"], o["g"], o["kI"],
+                       o["gI"], wout, ws[:128])
