@@ -235,6 +235,7 @@ def main():
     def timer_pass(ss, layer):
         for kid in range(B.DSV4_K_COUNT):
             B.dsv4_timer_enable(kid, True)
+        hold_stream(stream, 1.0e-3 * len(ss))
         for s in ss:
             step(s, stream, layer)
         torch.cuda.synchronize()
@@ -570,6 +571,7 @@ def _timed_steps(step, steps, warm):
     ms_step = e0.elapsed_time(e1) / steps
     for kid in range(B.DSV4_K_COUNT):
         B.dsv4_timer_enable(kid, True)
+    hold_stream(stream, 1.0e-3 * steps)
     for s in range(warm, warm + steps):
         step(s)
     torch.cuda.synchronize()
@@ -711,6 +713,29 @@ TRAFFIC = {
 }
 
 
+_SPIN_PER_MS = None
+
+
+def hold_stream(stream, ms):
+    """Queue a spin kernel of about `ms` milliseconds on `stream` (torch's
+    bounded clock-wait kernel), so that the launches issued after it are all
+    queued before the GPU reaches them: per-launch HIP-event timers then see
+    back-to-back kernels, not the host's launch gaps."""
+    import torch
+    global _SPIN_PER_MS
+    with torch.cuda.stream(stream):
+        if _SPIN_PER_MS is None:
+            n = 1 << 20
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(n)
+            a.record()
+            torch.cuda._sleep(n)
+            b.record()
+            b.synchronize()
+            _SPIN_PER_MS = n / max(a.elapsed_time(b), 1e-3)
+        torch.cuda._sleep(int(min(ms, 200.0) * _SPIN_PER_MS))
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated on a plain
     copy) from the committed rocprofv3 summary of this workload -- only if the
@@ -749,7 +774,8 @@ def calib_lib():
 def calibrate():
     """The device's own rates: a 1 GiB copy and a 1 GiB read (best of 5), and
     back-to-back matrix instructions from every SIMD (bf16 16x16x32, fp8 and
-    fp4 16x16x128, bf16 32x32x16, fp8 32x32x64; best of 3).  The measured bf16
+    fp4 16x16x128, bf16 32x32x16, fp8 32x32x64; 2048 workgroups of 4 waves,
+    8 independent accumulators per wave; best of 3).  The measured bf16
     peak a kernel is priced against is the faster bf16 shape."""
     import torch
     L = calib_lib()
@@ -760,7 +786,7 @@ def calibrate():
     copy = L.dsv4calib_copy_gbs(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, 5)
     read = L.dsv4calib_read_gbs(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()), 5)
     del src, dst
-    blocks = 1024
+    blocks = 2048                                  # 8 waves per SIMD: enough to keep the matrix pipes full
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     tf = [L.dsv4calib_mfma_tflops(kd, blocks, 256, ctypes.c_void_p(out.data_ptr()), 3) for kd in (0, 1, 2, 3, 4)]
     torch.cuda.synchronize()
