@@ -124,30 +124,36 @@ __device__ __forceinline__ QueryInfo query_info(const AttnArgs &A, int qi) {
     return Q;
 }
 
-// Record locator of list element p (entries first, then window tokens):
+// Record locator of list element p.  The list is the window tokens first
+// (oldest first), then the entries (CSA: in top-k order; HCA: in index
+// order), so the records a query's first chunks need are known from its
+// position alone, before any top-k or block-table read.
 //   >= 0        classic-cache record index (block id * entries_per_block + slot)
 //   -1 - w      window record w (decode: ring slot; prefill: window-buffer index)
 //   kMasked     masked (invalid index or unmapped block)
 constexpr int32_t kMasked = INT32_MIN;
 
+template <bool PREFILL>
+__device__ __forceinline__ int32_t window_loc(const AttnArgs &A, const QueryInfo &Q, int64_t p) {
+    const int64_t s = Q.t - Q.n_win + 1 + p;             // the token of window position p < n_win
+    if constexpr (PREFILL) return (int32_t)(-1 - (Q.win_base + (s - (Q.pos0 - A.L.W))));
+    return (int32_t)(-1 - (s % A.L.W));
+}
+
 template <bool CSA, bool PREFILL>
 __device__ __forceinline__ int32_t record_loc(const AttnArgs &A, const QueryInfo &Q, int64_t p) {
     const Lay &L = A.L;
-    if (p < Q.n_ent) {
-        int64_t j = p;
-        if constexpr (CSA) {
-            j = A.topk[(int64_t)Q.qrow * L.topk + p];
-            if (j < 0 || j >= Q.n_vis) return kMasked;
-        }
-        int64_t bid = block_id(A.C.block_table, A.C.max_blocks, A.C.n_blocks, Q.r, (j * L.m) / kBlockTokens);
-        if (bid < 0) return kMasked;
-        return (int32_t)(bid * L.epb + (j % L.epb));
+    if (p < Q.n_win) return window_loc<PREFILL>(A, Q, p);
+    const int64_t e = p - Q.n_win;
+    if (e >= Q.n_ent) return kMasked;
+    int64_t j = e;
+    if constexpr (CSA) {
+        j = A.topk[(int64_t)Q.qrow * L.topk + e];
+        if (j < 0 || j >= Q.n_vis) return kMasked;
     }
-    int64_t u = p - Q.n_ent;
-    if (u >= Q.n_win) return kMasked;
-    int64_t s = Q.t - Q.n_win + 1 + u;
-    if constexpr (PREFILL) return (int32_t)(-1 - (Q.win_base + (s - (Q.pos0 - L.W))));
-    return (int32_t)(-1 - (s % L.W));
+    int64_t bid = block_id(A.C.block_table, A.C.max_blocks, A.C.n_blocks, Q.r, (j * L.m) / kBlockTokens);
+    if (bid < 0) return kMasked;
+    return (int32_t)(bid * L.epb + (j % L.epb));
 }
 
 template <bool PREFILL>
@@ -647,6 +653,7 @@ struct LoShape {
 };
 
 constexpr int kLoPrefetch = 2;
+constexpr int kLo8Group = 8;              // transposed reads per group in the eight-wave kernel
 
 __device__ __forceinline__ void wave_lds_fence() {
     // the wave's LDS accesses are performed in order; this keeps the compiler
@@ -674,16 +681,18 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     const int hg = u8 % A.nhg;
     if (qi >= A.nq) return;
     // (CSA) the top-k indices of this wave's first resolution batch depend on
-    // the query row alone: read them now, beside the request and position,
-    // instead of one round trip later (the row has topk entries; positions
-    // past it are clamped, and only positions inside the list are used)
+    // the query row alone once the window is full (list position p holds
+    // top-k position p - W): read them now, beside the request and position,
+    // instead of one round trip later (positions outside the row are
+    // clamped; only those inside the list are used, and a query whose window
+    // is not full reads its row again below)
     int32_t jpre[RES];
     if constexpr (CSA) {
 #pragma unroll
         for (int u = 0; u < RES; ++u) {
             const int e = 64 * u + lane;
-            const int p = (sw + kSubsets * (e >> 5)) * kChunk + (e & 31);
-            jpre[u] = A.topk[(int64_t)qi * L.topk + (p < L.topk ? p : L.topk - 1)];
+            const int p = (sw + kSubsets * (e >> 5)) * kChunk + (e & 31) - L.W;
+            jpre[u] = A.topk[(int64_t)qi * L.topk + (p < 0 ? 0 : p < L.topk ? p : L.topk - 1)];
         }
     }
     const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
@@ -724,13 +733,13 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     // once (indices are clamped instead of branched around).  A masked record
     // is replaced by a stand-in that is always valid and finite -- the
     // query's own window record -- and keeps weight 0 through the valid mask.
-    const int64_t n_ent = Q.n_ent;
-    const int32_t own = Q.n_win > 0 ? record_loc<CSA, PREFILL>(A, Q, Q.n_list - 1) : kMasked;
+    const int64_t n_ent = Q.n_ent, n_win = Q.n_win;
+    const int32_t own = n_win > 0 ? window_loc<PREFILL>(A, Q, n_win - 1) : kMasked;
     int32_t first_ok = -1;                               // (no window: the wave's first valid record stands in)
     auto resolve = [&](int t_lo, int t_hi) {             // chunk ordinals [t_lo, t_hi) of this wave
         for (int e0 = t_lo * kChunk; e0 < t_hi * kChunk; e0 += 64 * RES) {
             // entries in this batch at all?  (wave-uniform: the window needs no reads)
-            const bool any_ent = (int64_t)(sw + kSubsets * (e0 >> 5)) * kChunk < n_ent;
+            const bool any_ent = n_ent > 0 && (int64_t)(sw + kSubsets * ((e0 + 64 * RES - 1) >> 5)) * kChunk + 31 >= n_win;
             int64_t p[RES], j[RES];
             int32_t bid[RES];
 #pragma unroll
@@ -743,15 +752,24 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
             }
             if (any_ent) {
                 if constexpr (CSA) {
+                    if (e0 == 0 && n_win == L.W) {       // the pre-read row (uniform)
 #pragma unroll
-                    for (int u = 0; u < RES; ++u) {
-                        const int64_t pc = p[u] < n_ent ? p[u] : (n_ent > 0 ? n_ent - 1 : 0);
-                        j[u] = e0 == 0 ? jpre[u] : A.topk[(int64_t)Q.qrow * L.topk + pc];
+                        for (int u = 0; u < RES; ++u) j[u] = jpre[u];
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < RES; ++u) {
+                            const int64_t e = p[u] - n_win;
+                            const int64_t pc = e < 0 ? 0 : e < n_ent ? e : n_ent - 1;
+                            j[u] = A.topk[(int64_t)Q.qrow * L.topk + pc];
+                        }
                     }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < RES; ++u) j[u] = p[u] - n_win;
                 }
 #pragma unroll
                 for (int u = 0; u < RES; ++u) {
-                    const bool ent = p[u] < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+                    const bool ent = p[u] >= n_win && p[u] - n_win < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
                     const int64_t blk = ent ? (j[u] * L.m) / kBlockTokens : 0;
                     bid[u] = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
                 }
@@ -759,17 +777,10 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
             int32_t lc[RES];
 #pragma unroll
             for (int u = 0; u < RES; ++u) {
-                const bool ent = p[u] < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+                const bool ent = p[u] >= n_win && p[u] - n_win < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
                 const int32_t l_ent =
                     (ent && bid[u] >= 0 && bid[u] < A.C.n_blocks) ? (int32_t)(bid[u] * L.epb + j[u] % L.epb) : kMasked;
-                const int64_t w = p[u] - n_ent;
-                int32_t l_win = kMasked;
-                if (w >= 0 && w < Q.n_win) {
-                    const int64_t ts = Q.t - Q.n_win + 1 + w;
-                    if constexpr (PREFILL) l_win = (int32_t)(-1 - (Q.win_base + (ts - (Q.pos0 - L.W))));
-                    else l_win = (int32_t)(-1 - (ts % L.W));
-                }
-                lc[u] = p[u] < n_ent ? l_ent : l_win;
+                lc[u] = p[u] < n_win ? window_loc<PREFILL>(A, Q, p[u]) : l_ent;
             }
 #pragma unroll
             for (int u = 0; u < RES; ++u) {
@@ -1108,6 +1119,513 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- the LO kernel, eight waves (d = 512)
+// The same decomposition and operations once more, on eight waves per (query,
+// 16-head group): wave (s, q) reduces subset s over dim part q.  A part's code
+// pairs of the logits and its dim blocks of the output cover the same 16-byte
+// pieces of a record (part 0: the code pieces [0, 4*QPP); part 1: the other
+// code pieces, the RoPE pieces and the scale), so a wave loads only its own
+// pieces -- into registers in the logits' operand layout, the key operands of
+// S^T = K Q^T taken straight from them, and then into its own LDS buffer for
+// the transposed reads of O^T += V^T P^T.  The two parts of a subset exchange
+// their partial logits (part 1 also the RoPE logits and the record scales)
+// through LDS, and both run the same online softmax on the same logits.  With
+// 64 accumulator registers a wave (its 16 dim blocks), two waves share each
+// SIMD.  Subsets 0-1 and 2-3 run half a chunk step apart (one workgroup
+// barrier between the halves), so while one wave of a SIMD runs its softmax
+// and O^T += V^T P^T the other runs its logits.  Every load a wave makes is
+// issued unconditionally (a step past the subset's end reads a harmless
+// stand-in address and is not consumed), which keeps the compiler's
+// memory-counter waits exact: a step waits for its own chunk only, with the
+// next one still in flight.  Every logit, weight and accumulator takes the
+// operations of k_attend's dim parts in the same order, so the kernels agree
+// bit for bit.
+template <int D, int DR>
+struct Lo8Shape {
+    using Sh = AttnShape<D, DR>;
+    static constexpr int KPR = Sh::PPR / 4;                  // piece groups per record (group k: pieces 4k..4k+3)
+    static constexpr int G1 = Sh::QPP;                      // part 0: groups [0, G1); part 1: [G1, KPR)
+    static constexpr int NG0 = G1, NG1 = KPR - G1;          // piece groups of each part per record block
+    static constexpr int NST0 = G1, NST1 = Sh::KP + Sh::KR - G1;   // groups each part stages for its dim blocks
+    static constexpr int RS0 = 4 * NST0 + 1, RS1 = 4 * NST1 + 1;  // LDS row strides in pieces (odd)
+    static constexpr int SWZ = Sh::SWZ;
+    static constexpr int BUF0 = (kChunk * RS0 + SWZ) * 16, BUF1 = (kChunk * RS1 + SWZ) * 16;
+    static constexpr int XWF = 8 * 64;                     // floats of one partial-logit array
+    static constexpr int XSLOT = 3 * XWF + kChunk;         // a0, a1, RoPE logits, the chunk's 32 scales
+    static constexpr int MAXC = 16;                         // chunks per subset (one locator batch)
+    static constexpr int LOC = MAXC * kChunk * 4 + MAXC * 4;   // a subset's locators and valid masks
+    static constexpr int RT = DR / 2 * 8;                   // the RoPE table (part 1 of each subset)
+    static constexpr int XOFF = kSubsets * (BUF0 + BUF1);
+    static constexpr int LOFF = XOFF + kSubsets * XSLOT * 4;
+    static constexpr int STREAM = LOFF + kSubsets * (LOC + RT);
+    static constexpr int FOLD = kSubsets * 64 * 8 + kSubsets * Sh::NDB * 64 * 16;
+    static constexpr int LDS = STREAM > FOLD ? STREAM : FOLD;
+    static constexpr int MAX_LIST = kSubsets * MAXC * kChunk;   // longest record list it takes
+    static_assert(Sh::NCH % 4 == 0 && Sh::RCH % 4 == 0 && Sh::PPR % 4 == 0, "pieces in whole groups of four");
+    static_assert(Sh::DBQ == 4 * Sh::QPP, "a part's dim blocks are the pieces of its code pairs");
+    static_assert(Sh::KP + Sh::KR < KPR, "the scale piece follows the RoPE pieces");
+    static_assert(BUF0 % 16 == 0 && BUF1 % 16 == 0 && (XSLOT * 4) % 16 == 0 && (LOC + RT) % 16 == 0, "alignment");
+    static_assert(kSubsets == 4, "two groups of two subsets");
+};
+
+template <int D, int DR, bool CSA, bool PREFILL>
+__global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs A) {
+    using Sh = AttnShape<D, DR>;
+    using S8 = Lo8Shape<D, DR>;
+    constexpr int NCH = Sh::NCH, RCH = Sh::RCH, KP = Sh::KP, KR = Sh::KR, QPP = Sh::QPP, NDB = Sh::NDB;
+    constexpr int DBQ = Sh::DBQ, DN = Sh::DN, G1 = S8::G1, XWF = S8::XWF, SWZ = S8::SWZ, MAXC = S8::MAXC;
+    constexpr int RESH = MAXC * kChunk / 64 / kParts;    // locators per lane each part resolves
+    static_assert(RESH * 64 * kParts == MAXC * kChunk, "the parts split the locator batch");
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const Lay &L = A.L;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;                           // 0: subsets 0-1; 1: subsets 2-3, half a step later
+    const int sw = 2 * grp + ((wave >> 1) & 1);          // subset (the dim part is wave & 1)
+
+    const int lin = blockIdx.x, x8 = lin & 7, u8 = lin >> 3;
+    const int qi = (u8 / A.nhg) * 8 + x8;
+    const int hg = u8 % A.nhg;
+    if (qi >= A.nq) return;
+    const int head = hg * 16 + c16;
+    const bool head_ok = head < L.H;
+
+    static_assert(kParts == 2, "the part dispatch below covers two parts");
+    auto part_body = [&](auto dqc) {
+        constexpr int DQ = decltype(dqc)::value;
+        constexpr int NG = DQ == 0 ? S8::NG0 : S8::NG1;  // piece groups per record block
+        constexpr int NGL = DQ == 0 ? NG : NG - 1;       // 16-byte loads per record block (part 1: + the scale)
+        constexpr int GB = DQ == 0 ? 0 : G1;             // first piece group
+        constexpr int NST = DQ == 0 ? S8::NST0 : S8::NST1;
+        constexpr int RS = DQ == 0 ? S8::RS0 : S8::RS1;
+        constexpr int NPAIR = DQ == 0 ? QPP : KP - QPP;  // code pairs of this part's logits
+        constexpr int NQ = 2 * NPAIR + (DQ == 1 ? KR : 0);   // query pieces of 8 dims
+        uint8_t *buf = smem + sw * (S8::BUF0 + S8::BUF1) + (DQ == 0 ? 0 : S8::BUF0);
+        float *xs = (float *)(smem + S8::XOFF) + sw * S8::XSLOT;             // the subset's exchange slot
+        uint8_t *sl = smem + S8::LOFF + sw * (S8::LOC + S8::RT);
+        int32_t *locs = (int32_t *)sl;                                      // [t][32]: chunk sw + 4t
+        uint32_t *vmask = (uint32_t *)(sl + MAXC * kChunk * 4);
+        float2 *rtab = (float2 *)(sl + S8::LOC);
+
+        const bool f32act = L.act != DSV4_DT_BF16;
+        const int ab = f32act ? 4 : 2;
+        const uint8_t *qrow = (const uint8_t *)A.q + ((int64_t)qi * L.H + (head_ok ? head : L.H - 1)) * D * ab;
+        // (CSA) the top-k indices of this part's half of the subset's records,
+        // read beside the request and position: once the window is full, list
+        // position p holds top-k position p - W (positions outside the row are
+        // clamped and not used; a query whose window is not full reads its row
+        // again below)
+        int32_t jpre[RESH];
+        if constexpr (CSA) {
+#pragma unroll
+            for (int u = 0; u < RESH; ++u) {
+                const int e = 64 * (RESH * DQ + u) + lane;
+                const int p = (sw + kSubsets * (e >> 5)) * kChunk + (e & 31) - L.W;
+                jpre[u] = A.topk[(int64_t)qi * L.topk + (p < 0 ? 0 : p < L.topk ? p : L.topk - 1)];
+            }
+        }
+        const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
+        if (!Q.ok) return;                               // (the whole workgroup)
+        const int n_list = (int)Q.n_list;
+        const int n_win = Q.n_win;
+        const int nchunks = (n_list + kChunk - 1) / kChunk;
+        const int cpw = (nchunks + kSubsets - 1) / kSubsets;                 // chunks of subset 0 (the most)
+        int mine = sw < nchunks ? (nchunks - 1 - sw) / kSubsets + 1 : 0;     // chunks sw, sw+4, ...
+        // the stand-in for masked records (always valid and finite): the
+        // query's own window record, else (no window) the subset's first valid
+        // record, found below
+        int32_t stand = n_win > 0 ? window_loc<PREFILL>(A, Q, n_win - 1) : kMasked;
+        // loads of a step past the subset's end read the query row instead
+        // (valid memory; such a step's results are never consumed)
+        const uint8_t *qsafe = qrow;
+        // ---- this part's loads of chunk t: lane (g, c16) fetches piece 4k+g of
+        // record 16rb+c16 for the part's groups k (part 1: the scale as one
+        // word, the rest of its group being padding)
+        auto locs_of = [&](int t, int32_t (&lc)[2]) {   // the lane's records of chunk t (rb = 0, 1)
+            const int tt = t < mine ? t : 0;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) lc[rb] = locs[tt * kChunk + 16 * rb + c16];
+        };
+        auto issue = [&](u32x4 (&pre)[2 * NGL], uint32_t (&scl)[2], int t, const int32_t (&lcs)[2]) {
+            const bool in = t < mine;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int32_t lc = lcs[rb] == kMasked ? stand : lcs[rb];
+                const uint8_t *rec = in ? loc_addr<PREFILL>(A, Q, lc) : qsafe;
+                const uint8_t *pc = rec + 16 * g;
+#pragma unroll
+                for (int k = 0; k < NGL; ++k) pre[rb * NGL + k] = *(const u32x4 *)(pc + 64 * (GB + k));
+                if constexpr (DQ == 1) scl[rb] = *(const uint32_t *)(rec + 16 * (Sh::CREC - 1));
+            }
+        };
+        u32x4 R0[2 * NGL], R1[2 * NGL];
+        uint32_t C0[2], C1[2];
+        const bool early = n_win >= kChunk * (sw + 1);   // the subset's first chunk lies in the window
+
+        u32x4 qa[NQ], qb[NQ];                            // the query pieces (read below)
+        // ---- locators of the subset's records: this part resolves chunk
+        // ordinals [8 DQ, 8 DQ + 8) -- its top-k reads, then its block-table
+        // reads, all in flight at once -- into the subset's shared array
+        {
+            const int64_t n_ent = Q.n_ent;
+            int32_t p[RESH], j[RESH], bid[RESH];
+#pragma unroll
+            for (int u = 0; u < RESH; ++u) {
+                const int e = 64 * (RESH * DQ + u) + lane;
+                p[u] = (sw + kSubsets * (e >> 5)) * kChunk + (e & 31);
+                if (e >= mine * kChunk) p[u] = n_list;                       // past the subset: masked
+            }
+            if constexpr (CSA) {
+                if (n_win != L.W) {                      // (window not full: the row again, at p - n_win)
+#pragma unroll
+                    for (int u = 0; u < RESH; ++u) {
+                        const int64_t en = (int64_t)p[u] - n_win;
+                        jpre[u] = A.topk[(int64_t)qi * L.topk + (en < 0 ? 0 : en < n_ent ? en : n_ent - 1)];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < RESH; ++u) {
+                const int64_t en = (int64_t)p[u] - n_win;                    // entry position
+                j[u] = (int32_t)en;
+                if constexpr (CSA) j[u] = jpre[u];
+                const bool ent = en >= 0 && en < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+                const int64_t blk = ent ? ((int64_t)j[u] * L.m) / kBlockTokens : 0;
+                bid[u] = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
+            }
+            // ---- the query pieces of this part, issued behind the block-table
+            // reads (they are needed only with the first records): code pair kp,
+            // half h reads dims 16(4kp+g) + 8h .. +8; RoPE step ks reads dims
+            // DN + 8(4ks+g) .. +8.  bf16 rows take one 16-byte load a piece, fp32
+            // rows two (the second load of a bf16 piece repeats the first, so no
+            // load depends on the activation type).
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                    const int dd = i < 2 * NPAIR ? 16 * (4 * (QPP * DQ + i / 2) + g) + 8 * (i & 1)
+                                             : DN + 8 * (4 * (i - 2 * NPAIR) + g);
+                const uint8_t *pa = qrow + dd * ab;
+                qa[i] = *(const u32x4 *)pa;
+                qb[i] = *(const u32x4 *)(f32act ? pa + 16 : pa);
+            }
+            // the subset's first chunk: when it lies in the window (a full
+            // window covers the first chunk of every subset) its records are
+            // known from the position alone, and its loads go out now, behind
+            // the block-table reads (loads complete in order: waiting for the
+            // block table does not wait for them)
+            if (early) {
+                int32_t l0[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) l0[rb] = window_loc<PREFILL>(A, Q, sw * kChunk + 16 * rb + c16);
+                issue(R0, C0, 0, l0);
+            }
+#pragma unroll
+            for (int u = 0; u < RESH; ++u) {
+                const int e = 64 * (RESH * DQ + u) + lane;
+                const int64_t en = (int64_t)p[u] - n_win;
+                const bool ent = en >= 0 && en < n_ent && j[u] >= 0 && j[u] < Q.n_vis;
+                const int32_t l_ent =
+                    (ent && bid[u] >= 0 && bid[u] < A.C.n_blocks) ? (int32_t)(bid[u] * L.epb + j[u] % L.epb) : kMasked;
+                const int32_t lc = p[u] < n_win ? window_loc<PREFILL>(A, Q, p[u]) : l_ent;
+                const uint64_t vb = __builtin_amdgcn_ballot_w64(lc != kMasked);
+                if (e < mine * kChunk) locs[e] = lc;
+                const int t0 = 2 * (RESH * DQ + u);       // the two chunk ordinals of this locator row
+                if (lane == 0) {
+                    if (t0 < mine) vmask[t0] = (uint32_t)vb;
+                    if (t0 + 1 < mine) vmask[t0 + 1] = (uint32_t)(vb >> 32);
+                }
+            }
+        }
+        if constexpr (DQ == 1) {
+            if (lane < DR / 2) {
+                float c, sn;
+                rope_cs(L, Q.t, lane, c, sn);
+                rtab[lane] = make_float2(c, sn);
+            }
+        }
+        __syncthreads();                                 // locators, masks and RoPE tables visible
+
+        if (stand == kMasked) {                          // no window: the subset's first valid record
+            int c = 0;
+            while (c < mine && vmask[c] == 0) ++c;
+            if (c < mine) stand = locs[c * kChunk + __builtin_ctz(vmask[c])];
+            else mine = 0;                               // nothing valid: the subset contributes nothing
+        }
+
+        {
+            int32_t l0[2], l1[2];
+            locs_of(0, l0);
+            locs_of(1, l1);
+            if (!early) issue(R0, C0, 0, l0);
+            issue(R1, C1, 1, l1);
+        }
+
+        // ---- query fragments (B operand of S^T = K Q^T); RoPE ones rotated at t
+        auto piece8 = [&](int i, float (&v)[8]) {
+            if (!f32act) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = __uint_as_float(qa[i][j] << 16);
+                    v[2 * j + 1] = __uint_as_float(qa[i][j] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = __uint_as_float(qa[i][j]);
+                    v[4 + j] = __uint_as_float(qb[i][j]);
+                }
+            }
+        };
+        bf16x8 Qn[NPAIR][2];
+#pragma unroll
+        for (int e = 0; e < NPAIR; ++e)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float v[8];
+                piece8(2 * e + h, v);
+                bf16x8 f;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) f[jj] = f2bf(v[jj]);
+                Qn[e][h] = f;
+            }
+        bf16x8 Qr[DQ == 1 ? KR : 1];
+        if constexpr (DQ == 1) {
+#pragma unroll
+            for (int ks = 0; ks < KR; ++ks) {
+                const int ch = 4 * ks + g;
+                float v[8];
+                piece8(2 * NPAIR + ks, v);
+                bf16x8 f;
+#pragma unroll
+                for (int jj = 0; jj < 8; jj += 2) {
+                    float a = 0.0f, b = 0.0f;
+                    if (ch < RCH) {
+                        const float2 cs = rtab[(8 * ch + jj) / 2];
+                        a = v[jj] * cs.x - v[jj + 1] * cs.y;
+                        b = v[jj] * cs.y + v[jj + 1] * cs.x;
+                    }
+                    f[jj] = f2bf(a);
+                    f[jj + 1] = f2bf(b);
+                }
+                Qr[ks] = f;
+            }
+        }
+        const float tau2 = L.tau * 1.4426950408889634f;   // logits in base 2
+        auto slot = [&](int c, int r) { return buf + (r * RS + c + (r >> 4) * SWZ) * 16; };   // c: the part's piece
+
+        // ---- first half of a chunk step: this part's partial logits from the
+        // registers, into the exchange slot; the pieces staged for O^T += V^T P^T;
+        // the loads of chunk t+2 into the freed registers
+        auto produce_logits = [&](const u32x4 (&pre)[2 * NGL], const uint32_t (&scl)[2]) {
+            // the two record blocks' chains interleaved; each keeps its pairs in order
+            f32x4 a[2], b[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) a[rb] = b[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int e = 0; e < NPAIR; ++e)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        const u32x4 u = pre[rb * NGL + e];
+                        a[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8(u[2 * h], u[2 * h + 1]), Qn[e][h], a[rb], 0,
+                                                                        0, 0);
+                    }
+            if constexpr (DQ == 1) {
+#pragma unroll
+                for (int ks = 0; ks < KR; ++ks)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        union { u32x4 v; bf16x8 b; } cv;
+                        cv.v = pre[rb * NGL + (KP - G1) + ks];
+                        b[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Qr[ks], b[rb], 0, 0, 0);
+                    }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int k = (rb * 64 + lane) * 4;      // [rb][lane][i]: one 16-byte piece a lane
+                if constexpr (DQ == 0) {
+                    *(f32x4 *)(xs + k) = a[rb];
+                } else {
+                    *(f32x4 *)(xs + XWF + k) = a[rb];
+                    *(f32x4 *)(xs + 2 * XWF + k) = b[rb];
+                    if (g == 0) xs[3 * XWF + 16 * rb + c16] = __uint_as_float(scl[rb]);   // the record scales
+                }
+            }
+            wave_lds_fence();                            // the previous chunk's transposed reads come first
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int k = 0; k < NST; ++k) *(u32x4 *)slot(4 * k + g, 16 * rb + c16) = pre[rb * NGL + k];
+        };
+        auto produce = [&](u32x4 (&pre)[2 * NGL], uint32_t (&scl)[2], int t) {
+            int32_t lnext[2];
+            locs_of(t + 2, lnext);                       // (LDS latency hidden behind the logits)
+            if (t < mine) produce_logits(pre, scl);
+            issue(pre, scl, t + 2, lnext);               // (every step: the loads stay in order)
+        };
+
+        // ---- second half: logits from both parts' partials, online softmax,
+        // O^T += V^T P^T on this part's dim blocks
+        AttnState<DBQ> S;
+        state_clear(S);
+        auto softmax = [&](int t, bf16x8 &Pn, bf16x8 &Pr) {
+            float lg[2][4], sc[2][4];
+            const uint32_t vmg = vmask[t] >> (4 * g);     // bit 16rb+i: record 16rb+4g+i usable
+            f32x4 x0[2], x1[2], xr[2], xc[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int k = (rb * 64 + lane) * 4;
+                x0[rb] = *(const f32x4 *)(xs + k);
+                x1[rb] = *(const f32x4 *)(xs + XWF + k);
+                xr[rb] = *(const f32x4 *)(xs + 2 * XWF + k);
+                xc[rb] = *(const f32x4 *)(xs + 3 * XWF + 16 * rb + 4 * g);   // scales of records 16rb+4g+i
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = (vmg >> (16 * rb + i)) & 1u;
+                    sc[rb][i] = xc[rb][i];
+                    const float a = x0[rb][i] + x1[rb][i];
+                    const float v = tau2 * (sc[rb][i] * a + xr[rb][i]);
+                    lg[rb][i] = ok ? v : -INFINITY;
+                }
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, lg[rb][i]);
+            cmax = head_max(cmax);
+            const float m_new = lazy_max(S.m, cmax);
+            float p[2][4];
+            float alpha = 1.0f;
+            if (m_new == -INFINITY) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[rb][i] = 0.0f;
+            } else {
+                alpha = __builtin_amdgcn_exp2f(S.m - m_new);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[rb][i] = __builtin_amdgcn_exp2f(lg[rb][i] - m_new);
+            }
+            float ps = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ps = ps + p[rb][i];
+            ps = head_sum(ps);
+            S.l = S.l * alpha + ps;
+            S.m = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int i = 0; i < DBQ; ++i) S.O[i] = S.O[i] * alpha;
+            }
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int rb = jj >> 2, i = jj & 3;
+                Pn[jj] = f2bf(p[rb][i] * sc[rb][i]);
+                Pr[jj] = f2bf(p[rb][i]);
+            }
+        };
+        auto pv = [&](const bf16x8 &Pn, const bf16x8 &Pr) {
+            const int trow = c16 >> 1, thalf = c16 & 1;
+            const int trec = (trow < 4 ? 0 : 16) + 4 * g + (trow & 3);
+            const int r16 = c16 >> 2, q16 = c16 & 3;
+#pragma unroll
+            for (int ii = 0; ii < DBQ; ++ii) {
+                if (ii % kLo8Group == 0) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+                const int db = DBQ * DQ + ii;
+                if (db < NCH) {
+                    const i32x2 v =
+                        __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_p)(slot(db - 4 * GB, trec) + 8 * thalf));
+                    S.O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8((uint32_t)v[0], (uint32_t)v[1]), Pn, S.O[ii], 0,
+                                                                      0, 0);
+                } else if (db < NDB) {
+                    const int ch = NCH + 2 * (db - NCH) + (q16 >> 1) - 4 * GB;
+                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(slot(ch, 4 * g + r16) + 8 * (q16 & 1)));
+                    i16x4 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(slot(ch, 16 + 4 * g + r16) + 8 * (q16 & 1)));
+                    union { i16x4 s[2]; bf16x8 b; } cv;
+                    cv.s[0] = lo;
+                    cv.s[1] = hi;
+                    S.O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Pr, S.O[ii], 0, 0, 0);
+                }
+            }
+        };
+
+        // every wave takes part in every barrier: the second group enters the
+        // step sequence one barrier later, and the first leaves one later
+        auto step = [&](u32x4 (&pre)[2 * NGL], uint32_t (&scl)[2], int t) {
+            produce(pre, scl, t);
+            __syncthreads();                             // both parts' partials of chunk t visible
+            if (t < mine) {
+                bf16x8 Pn, Pr;
+                softmax(t, Pn, Pr);
+                pv(Pn, Pr);
+            }
+            __syncthreads();                             // the exchange slot is free again
+        };
+        // (steps run in pairs; an odd count ends with a step no subset consumes)
+        if (grp == 1) __syncthreads();
+#pragma unroll 1
+        for (int t = 0; t < cpw; t += 2) {
+            step(R0, C0, t);
+            step(R1, C1, t + 1);
+        }
+        if (grp == 0) __syncthreads();
+
+        // ---- fold the four subset states left to right through LDS (the
+        // operations of k_attend's sequential fold); wave (s, q) emits dim
+        // blocks DBQ*q + s, +4, ... of its part
+        __syncthreads();
+        float2 *ml = (float2 *)smem;                             // [subset][64]
+        f32x4 *ob = (f32x4 *)(smem + kSubsets * 64 * 8);         // [subset][NDB][64]
+        if constexpr (DQ == 0) ml[sw * 64 + lane] = make_float2(S.m, S.l);
+#pragma unroll
+        for (int i = 0; i < DBQ; ++i) ob[(sw * NDB + DBQ * DQ + i) * 64 + lane] = S.O[i];
+        __syncthreads();
+        float m = ml[lane].x, l = ml[lane].y;
+        float fw[kSubsets][2];
+#pragma unroll
+        for (int s = 1; s < kSubsets; ++s) {
+            const float2 b = ml[s * 64 + lane];
+            float mm, ll, fa, fb;
+            fold_scales(m, l, b.x, b.y, mm, ll, fa, fb);
+            fw[s][0] = fa;
+            fw[s][1] = fb;
+            m = mm;
+            l = ll;
+        }
+        if (!head_ok) return;
+        const float z = A.sinks[head] * 1.4426950408889634f;
+        const float M = fmaxf(m, z);
+        const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        const float den = l * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
+        const float cf = den > 0.0f ? f / den : 0.0f;
+        const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
+#pragma unroll
+        for (int b = DBQ * DQ + sw; b < DBQ * DQ + DBQ; b += kSubsets) {
+            f32x4 o = ob[b * 64 + lane];
+#pragma unroll
+            for (int s = 1; s < kSubsets; ++s) o = fold_o(o, fw[s][0], ob[(s * NDB + b) * 64 + lane], fw[s][1]);
+            const int dd = b * 16 + 4 * g;
+            if (L.act == DSV4_DT_BF16) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 v = {f2bf(o[0] * cf), f2bf(o[1] * cf), f2bf(o[2] * cf), f2bf(o[3] * cf)};
+                *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
+            } else {
+                *(float4 *)((float *)A.out + obase + dd) = make_float4(o[0] * cf, o[1] * cf, o[2] * cf, o[3] * cf);
+            }
+        }
+    };
+    if ((wave & 1) == 0) part_body(std::integral_constant<int, 0>());
+    else part_body(std::integral_constant<int, 1>());
+}
+
 // ---------------------------------------------------------------- fp32 records
 // Records stored as d fp32 values (the reference-precision storage mode): one
 // wave per (query, head), lane l holding dims [l*VPL, l*VPL + VPL).  The
@@ -1274,8 +1792,25 @@ static hipError_t launch_lo(const AttnArgs &A, hipStream_t s) {
 }
 
 template <int D, int DR, bool CSA, bool PREFILL>
+static hipError_t launch_lo8(const AttnArgs &A, hipStream_t s) {
+    static int64_t lim = 0;
+    constexpr int64_t lds = Lo8Shape<D, DR>::LDS;
+    hipError_t e = raise_lds_limit((const void *)k_attend_lo8<D, DR, CSA, PREFILL>, lds, lim);
+    if (e != hipSuccess) return e;
+    const int groups = (A.nq + 7) / 8;
+    hipLaunchKernelGGL((k_attend_lo8<D, DR, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kSubsets * kParts),
+                       (size_t)lds, s, A);
+    return hipGetLastError();
+}
+
+// LO: the eight-wave kernel where the record list fits its locator batch (the
+// V4 shape), else the four-wave one.
+template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_t(const AttnArgs &A, bool hi, hipStream_t s) {
-    return hi ? launch_gr<D, DR, 1, CSA, PREFILL>(A, s) : launch_lo<D, DR, CSA, PREFILL>(A, s);
+    if (hi) return launch_gr<D, DR, 1, CSA, PREFILL>(A, s);
+    if constexpr (D == 512)
+        if (attend_list_max(A.L, A.C, CSA) <= Lo8Shape<D, DR>::MAX_LIST) return launch_lo8<D, DR, CSA, PREFILL>(A, s);
+    return launch_lo<D, DR, CSA, PREFILL>(A, s);
 }
 
 hipError_t launch_attend(const AttnArgs &A, bool csa, bool prefill, bool hi, hipStream_t s) {
