@@ -1225,10 +1225,27 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                 jpre[u] = A.topk[(int64_t)qi * L.topk + (p < 0 ? 0 : p < L.topk ? p : L.topk - 1)];
             }
         }
+        // (CSA) and the top-k indices of the lane's two records of the
+        // subset's second chunk (list chunk sw + 4), which the fast start
+        // below resolves per lane
+        int32_t t1[2] = {0, 0};
+        if constexpr (CSA) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int p = (sw + kSubsets) * kChunk + 16 * rb + c16 - L.W;
+                t1[rb] = A.topk[(int64_t)qi * L.topk + (p < 0 ? 0 : p < L.topk ? p : L.topk - 1)];
+            }
+        }
         const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
         if (!Q.ok) return;                               // (the whole workgroup)
         const int n_list = (int)Q.n_list;
         const int n_win = Q.n_win;
+        // Fast start (a full window of four chunks): a subset's first chunk is
+        // window records, known from the position alone, and each lane resolves
+        // its two records of the second chunk itself, so both chunks' loads go
+        // out before the loop without waiting for the shared locators; those
+        // become visible at the first step's barrier.  (Uniform per workgroup.)
+        const bool fast = n_win == L.W && L.W == kSubsets * kChunk;
         const int nchunks = (n_list + kChunk - 1) / kChunk;
         const int cpw = (nchunks + kSubsets - 1) / kSubsets;                 // chunks of subset 0 (the most)
         int mine = sw < nchunks ? (nchunks - 1 - sw) / kSubsets + 1 : 0;     // chunks sw, sw+4, ...
@@ -1261,7 +1278,6 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
         };
         u32x4 R0[2 * NGL], R1[2 * NGL];
         uint32_t C0[2], C1[2];
-        const bool early = n_win >= kChunk * (sw + 1);   // the subset's first chunk lies in the window
 
         u32x4 qa[NQ], qb[NQ];                            // the query pieces (read below)
         // ---- locators of the subset's records: this part resolves chunk
@@ -1294,6 +1310,17 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                 const int64_t blk = ent ? ((int64_t)j[u] * L.m) / kBlockTokens : 0;
                 bid[u] = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
             }
+            // the lane's second-chunk records (fast start): their block-table reads
+            int32_t j1[2], bt1[2];
+            bool ok1[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int64_t en = (int64_t)(sw + kSubsets) * kChunk + 16 * rb + c16 - n_win;
+                j1[rb] = CSA ? t1[rb] : (int32_t)en;
+                ok1[rb] = en >= 0 && en < n_ent && j1[rb] >= 0 && j1[rb] < Q.n_vis;
+                const int64_t blk = ok1[rb] ? ((int64_t)j1[rb] * L.m) / kBlockTokens : 0;
+                bt1[rb] = A.C.block_table[(int64_t)Q.r * A.C.max_blocks + blk];
+            }
             // ---- the query pieces of this part, issued behind the block-table
             // reads (they are needed only with the first records): code pair kp,
             // half h reads dims 16(4kp+g) + 8h .. +8; RoPE step ks reads dims
@@ -1308,16 +1335,20 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                 qa[i] = *(const u32x4 *)pa;
                 qb[i] = *(const u32x4 *)(f32act ? pa + 16 : pa);
             }
-            // the subset's first chunk: when it lies in the window (a full
-            // window covers the first chunk of every subset) its records are
-            // known from the position alone, and its loads go out now, behind
-            // the block-table reads (loads complete in order: waiting for the
-            // block table does not wait for them)
-            if (early) {
-                int32_t l0[2];
+            // fast start: the first chunk's loads go out now, behind the
+            // block-table reads (loads complete in order: waiting for the block
+            // table does not wait for them), then the second chunk's, once its
+            // block ids are in
+            if (fast) {
+                int32_t l0[2], l1[2];
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) l0[rb] = window_loc<PREFILL>(A, Q, sw * kChunk + 16 * rb + c16);
                 issue(R0, C0, 0, l0);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    l1[rb] = (ok1[rb] && bt1[rb] >= 0 && bt1[rb] < A.C.n_blocks) ? (int32_t)(bt1[rb] * L.epb + j1[rb] % L.epb)
+                                                                                 : kMasked;
+                issue(R1, C1, 1, l1);
             }
 #pragma unroll
             for (int u = 0; u < RESH; ++u) {
@@ -1343,20 +1374,19 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                 rtab[lane] = make_float2(c, sn);
             }
         }
-        __syncthreads();                                 // locators, masks and RoPE tables visible
-
-        if (stand == kMasked) {                          // no window: the subset's first valid record
-            int c = 0;
-            while (c < mine && vmask[c] == 0) ++c;
-            if (c < mine) stand = locs[c * kChunk + __builtin_ctz(vmask[c])];
-            else mine = 0;                               // nothing valid: the subset contributes nothing
-        }
-
-        {
+        wave_lds_fence();                                // (the RoPE table: this wave's own)
+        if (!fast) {                                     // (uniform: every wave of the workgroup)
+            __syncthreads();                             // locators and masks visible
+            if (stand == kMasked) {                      // no window: the subset's first valid record
+                int c = 0;
+                while (c < mine && vmask[c] == 0) ++c;
+                if (c < mine) stand = locs[c * kChunk + __builtin_ctz(vmask[c])];
+                else mine = 0;                           // nothing valid: the subset contributes nothing
+            }
             int32_t l0[2], l1[2];
             locs_of(0, l0);
             locs_of(1, l1);
-            if (!early) issue(R0, C0, 0, l0);
+            issue(R0, C0, 0, l0);
             issue(R1, C1, 1, l1);
         }
 
@@ -1569,12 +1599,27 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
             }
             __syncthreads();                             // the exchange slot is free again
         };
-        // (steps run in pairs; an odd count ends with a step no subset consumes)
+        // The first step refills after its exchange barrier (the shared
+        // locators of chunk 2 are visible from there on); the others run in
+        // pairs, an odd count ending with a step no subset consumes.
         if (grp == 1) __syncthreads();
+        {
+            if (0 < mine) produce_logits(R0, C0);
+            __syncthreads();                             // partials (and the locators) visible
+            if (0 < mine) {
+                bf16x8 Pn, Pr;
+                softmax(0, Pn, Pr);
+                pv(Pn, Pr);
+            }
+            int32_t l2[2];
+            locs_of(2, l2);
+            issue(R0, C0, 2, l2);
+            __syncthreads();                             // the exchange slot is free again
+        }
 #pragma unroll 1
-        for (int t = 0; t < cpw; t += 2) {
-            step(R0, C0, t);
-            step(R1, C1, t + 1);
+        for (int t = 1; t < cpw; t += 2) {
+            step(R1, C1, t);
+            step(R0, C0, t + 1);
         }
         if (grp == 0) __syncthreads();
 
