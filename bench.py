@@ -285,7 +285,8 @@ def main():
             dom = "index_score"
         pl = per_launch[dom]
         achieved = pl["work"] / (kn[dom]["avg_us"] * 1e-6) / (1e9 if pl["unit"] == "GB/s" else 1e12)
-        kname = {"index_score": "k_index_score_decode", "attend": "k_attend_lo"}[dom]
+        kname = {"index_score": "k_index_score_decode",
+                 "attend": lo_kernel(d, max(k + 128, need_blocks + 128))}[dom]
         out = {"kernel": kname, "bound": pl["bound"], "achieved": round(achieved, 2), "peak": pl["peak"],
                "unit": pl["unit"], "frac": round(achieved / pl["peak"], 4),
                "traffic": measured_traffic(dom) if (Bsz, ctx, R, mx) == (32, 131072, 4, False) else None}
@@ -677,7 +678,9 @@ def decode_mix_main(a):
     att_gbs = att_bytes / att_s / 1e9
     dom = "attend" if (not pair or kern["attend"]["total_ms"] >= kern["index_score"]["total_ms"]) else "index_score"
     if dom == "attend":
-        roof = {"kernel": "k_attend_lo", "bound": "mfma", "achieved": round(att_tf, 2), "peak": BF16_PEAK_TFLOPS,
+        kn_h = lo_kernel(d, mb + 128)
+        kn = (lo_kernel(d, k + 128) + " (CSA), " + kn_h + " (HCA)") if pair else kn_h
+        roof = {"kernel": kn, "bound": "mfma", "achieved": round(att_tf, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4), "traffic": None}
     else:
         sc_gbs = score_bytes / (kern["index_score"]["total_ms"] / steps * 1e-3) / 1e9
@@ -711,6 +714,14 @@ TRAFFIC = {
     "index_score": (os.path.join(HERE, "profiles", "k_index_score_decode_128k_b32_hbm_traffic.txt"),
                     os.path.join(CSRC, "k_index.hip"), "k_index_src_sha256"),
 }
+
+
+LO8_MAX_LIST = 2048   # records: the eight-wave LO attention kernel takes lists up to this length (d = 512)
+
+
+def lo_kernel(d, list_max):
+    """Name of the LO attention kernel the library launches for this shape."""
+    return "k_attend_lo8" if d == 512 and list_max <= LO8_MAX_LIST else "k_attend_lo"
 
 
 _SPIN_PER_MS = None

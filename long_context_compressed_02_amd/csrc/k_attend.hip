@@ -1148,7 +1148,10 @@ struct Lo8Shape {
     static constexpr int NG0 = G1, NG1 = KPR - G1;          // piece groups of each part per record block
     static constexpr int NST0 = G1, NST1 = Sh::KP + Sh::KR - G1;   // groups each part stages for its dim blocks
     static constexpr int RS0 = 4 * NST0 + 1, RS1 = 4 * NST1 + 1;  // LDS row strides in pieces (odd)
-    static constexpr int SWZ = Sh::SWZ;
+    // records 16..31 shifted by 8 pieces (32 banks): the transposed reads of a
+    // half-wave (records 4g..4g+3 and 16+4g.. of two lane groups) then fall on
+    // distinct banks (a shift of 4 made them collide pairwise)
+    static constexpr int SWZ = 8;
     static constexpr int BUF0 = (kChunk * RS0 + SWZ) * 16, BUF1 = (kChunk * RS1 + SWZ) * 16;
     static constexpr int XWF = 8 * 64;                     // floats of one partial-logit array
     static constexpr int XSLOT = 3 * XWF + kChunk;         // a0, a1, RoPE logits, the chunk's 32 scales
