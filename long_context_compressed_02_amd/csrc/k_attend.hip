@@ -1449,13 +1449,39 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
         // ---- first half of a chunk step: this part's partial logits from the
         // registers, into the exchange slot; the pieces staged for O^T += V^T P^T;
         // the loads of chunk t+2 into the freed registers
-        auto produce_logits = [&](const u32x4 (&pre)[2 * NGL], const uint32_t (&scl)[2]) {
+        // First half of a chunk step: this part's partial logits from the
+        // registers, into the exchange slot; each piece group, once its MFMAs
+        // have it, staged for O^T += V^T P^T and its registers refilled with
+        // chunk t+2's group at once -- the refill loads trickle out between
+        // the MFMAs instead of queueing in one burst.  Every step runs it (a
+        // step past the subset's end computes on the stand-in rows and is
+        // not consumed): the loads stay unconditional and in order.
+        // (REFILL false: the first step, whose refill goes out after its barrier)
+        auto produce = [&](auto refill_c, u32x4 (&pre)[2 * NGL], uint32_t (&scl)[2], int t) {
+            constexpr bool REFILL = decltype(refill_c)::value;
+            int32_t lnext[2];
+            locs_of(t + 2, lnext);
+            const bool in2 = t + 2 < mine;
+            const uint8_t *rc[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int32_t lc = lnext[rb] == kMasked ? stand : lnext[rb];
+                rc[rb] = in2 ? loc_addr<PREFILL>(A, Q, lc) : qsafe;
+            }
+            wave_lds_fence();                            // the previous chunk's transposed reads come first
+            auto refill = [&](int k) {                   // stage group k of both record blocks, load its successor
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    if (k < NST) *(u32x4 *)slot(4 * k + g, 16 * rb + c16) = pre[rb * NGL + k];
+                    if constexpr (REFILL) pre[rb * NGL + k] = *(const u32x4 *)(rc[rb] + 16 * g + 64 * (GB + k));
+                }
+            };
             // the two record blocks' chains interleaved; each keeps its pairs in order
             f32x4 a[2], b[2];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) a[rb] = b[rb] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int e = 0; e < NPAIR; ++e)
+            for (int e = 0; e < NPAIR; ++e) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -1464,15 +1490,19 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                         a[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cvt8(u[2 * h], u[2 * h + 1]), Qn[e][h], a[rb], 0,
                                                                         0, 0);
                     }
+                refill(e);
+            }
             if constexpr (DQ == 1) {
 #pragma unroll
-                for (int ks = 0; ks < KR; ++ks)
+                for (int ks = 0; ks < KR; ++ks) {
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
                         union { u32x4 v; bf16x8 b; } cv;
                         cv.v = pre[rb * NGL + (KP - G1) + ks];
                         b[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Qr[ks], b[rb], 0, 0, 0);
                     }
+                    refill((KP - G1) + ks);
+                }
             }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -1485,17 +1515,10 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                     if (g == 0) xs[3 * XWF + 16 * rb + c16] = __uint_as_float(scl[rb]);   // the record scales
                 }
             }
-            wave_lds_fence();                            // the previous chunk's transposed reads come first
+            if constexpr (DQ == 1 && REFILL) {           // the next scales, once these are written out
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int k = 0; k < NST; ++k) *(u32x4 *)slot(4 * k + g, 16 * rb + c16) = pre[rb * NGL + k];
-        };
-        auto produce = [&](u32x4 (&pre)[2 * NGL], uint32_t (&scl)[2], int t) {
-            int32_t lnext[2];
-            locs_of(t + 2, lnext);                       // (LDS latency hidden behind the logits)
-            if (t < mine) produce_logits(pre, scl);
-            issue(pre, scl, t + 2, lnext);               // (every step: the loads stay in order)
+                for (int rb = 0; rb < 2; ++rb) scl[rb] = *(const uint32_t *)(rc[rb] + 16 * (Sh::CREC - 1));
+            }
         };
 
         // ---- second half: logits from both parts' partials, online softmax,
@@ -1593,7 +1616,7 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
         // every wave takes part in every barrier: the second group enters the
         // step sequence one barrier later, and the first leaves one later
         auto step = [&](u32x4 (&pre)[2 * NGL], uint32_t (&scl)[2], int t) {
-            produce(pre, scl, t);
+            produce(std::true_type(), pre, scl, t);
             __syncthreads();                             // both parts' partials of chunk t visible
             if (t < mine) {
                 bf16x8 Pn, Pr;
@@ -1607,7 +1630,7 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
         // pairs, an odd count ending with a step no subset consumes.
         if (grp == 1) __syncthreads();
         {
-            if (0 < mine) produce_logits(R0, C0);
+            produce(std::false_type(), R0, C0, 0);
             __syncthreads();                             // partials (and the locators) visible
             if (0 < mine) {
                 bf16x8 Pn, Pr;
