@@ -38,8 +38,12 @@ FLAGS = [
 # every chunk).  Indexer: the scores leave the MFMA straight into the VALU
 # epilogue (ReLU, head weights), which would otherwise copy every result out
 # of an AGPR first.
+# Calibration: the loops of independent MFMAs keep their accumulators in
+# VGPRs too -- with AGPR accumulators the compiler shuffled them with ~50
+# register moves per 8 matrix instructions and the 16x16 rates read half.
 FILE_FLAGS = {"k_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-              "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+              "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "calib.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:
