@@ -1177,7 +1177,7 @@ struct Lo8Shape {
     static_assert(kSubsets == 4, "two groups of two subsets");
 };
 
-template <int D, int DR, bool CSA, bool PREFILL>
+template <int D, int DR, bool CSA, bool PREFILL, bool F32A>
 __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs A) {
     using Sh = AttnShape<D, DR>;
     using S8 = Lo8Shape<D, DR>;
@@ -1217,16 +1217,15 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
         uint32_t *vmask = (uint32_t *)(sl + MAXC * kChunk * 4);
         float2 *rtab = (float2 *)(sl + S8::LOC);
 
-        const bool f32act = L.act != DSV4_DT_BF16;
-        const int ab = f32act ? 4 : 2;
+        constexpr bool f32act = F32A;                    // fp32 activations (else bf16)
+        constexpr int ab = f32act ? 4 : 2;
         const uint8_t *qrow = (const uint8_t *)A.q + ((int64_t)qi * L.H + (head_ok ? head : L.H - 1)) * D * ab;
         // ---- the query pieces of this part, first of all (their addresses
         // need only the workgroup's query and head group): code pair kp, half h
         // reads dims 16(4kp+g) + 8h .. +8; RoPE step ks reads dims DN +
         // 8(4ks+g) .. +8.  bf16 rows take one 16-byte load a piece, fp32 rows
-        // two (the second load of a bf16 piece repeats the first, so no load
-        // depends on the activation type).  Measured 0.5 us faster per launch
-        // than issuing them behind the block-table reads.
+        // two.  Measured 0.5 us faster per launch than issuing them behind the
+        // block-table reads.
         u32x4 qa[NQ], qb[NQ];
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -1234,7 +1233,7 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
                                          : DN + 8 * (4 * (i - 2 * NPAIR) + g);
             const uint8_t *pa = qrow + dd * ab;
             qa[i] = *(const u32x4 *)pa;
-            qb[i] = *(const u32x4 *)(f32act ? pa + 16 : pa);
+            if constexpr (f32act) qb[i] = *(const u32x4 *)(pa + 16);
         }
         // (CSA) the top-k indices of this part's half of the subset's records,
         // read beside the request and position: once the window is full, list
@@ -1691,7 +1690,7 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
 #pragma unroll
             for (int s = 1; s < kSubsets; ++s) o = fold_o(o, fw[s][0], ob[(s * NDB + b) * 64 + lane], fw[s][1]);
             const int dd = b * 16 + 4 * g;
-            if (L.act == DSV4_DT_BF16) {
+            if constexpr (!F32A) {
                 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                 const bf16x4 v = {f2bf(o[0] * cf), f2bf(o[1] * cf), f2bf(o[2] * cf), f2bf(o[3] * cf)};
                 *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
@@ -1869,15 +1868,15 @@ static hipError_t launch_lo(const AttnArgs &A, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D, int DR, bool CSA, bool PREFILL>
+template <int D, int DR, bool CSA, bool PREFILL, bool F32A>
 static hipError_t launch_lo8(const AttnArgs &A, hipStream_t s) {
     static int64_t lim = 0;
     constexpr int64_t lds = Lo8Shape<D, DR>::LDS;
-    hipError_t e = raise_lds_limit((const void *)k_attend_lo8<D, DR, CSA, PREFILL>, lds, lim);
+    hipError_t e = raise_lds_limit((const void *)k_attend_lo8<D, DR, CSA, PREFILL, F32A>, lds, lim);
     if (e != hipSuccess) return e;
     const int groups = (A.nq + 7) / 8;
-    hipLaunchKernelGGL((k_attend_lo8<D, DR, CSA, PREFILL>), dim3(groups * 8 * A.nhg), dim3(64 * kSubsets * kParts),
-                       (size_t)lds, s, A);
+    hipLaunchKernelGGL((k_attend_lo8<D, DR, CSA, PREFILL, F32A>), dim3(groups * 8 * A.nhg),
+                       dim3(64 * kSubsets * kParts), (size_t)lds, s, A);
     return hipGetLastError();
 }
 
@@ -1887,7 +1886,9 @@ template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_t(const AttnArgs &A, bool hi, hipStream_t s) {
     if (hi) return launch_gr<D, DR, 1, CSA, PREFILL>(A, s);
     if constexpr (D == 512)
-        if (attend_list_max(A.L, A.C, CSA) <= Lo8Shape<D, DR>::MAX_LIST) return launch_lo8<D, DR, CSA, PREFILL>(A, s);
+        if (attend_list_max(A.L, A.C, CSA) <= Lo8Shape<D, DR>::MAX_LIST)
+            return A.L.act == DSV4_DT_BF16 ? launch_lo8<D, DR, CSA, PREFILL, false>(A, s)
+                                           : launch_lo8<D, DR, CSA, PREFILL, true>(A, s);
     return launch_lo<D, DR, CSA, PREFILL>(A, s);
 }
 

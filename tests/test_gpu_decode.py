@@ -284,15 +284,20 @@ def _sinks(profile):
     return z
 
 
+@pytest.mark.parametrize("act", [B.DSV4_DT_BF16, B.DSV4_DT_F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("sink_profile", ["normal", "limits"])
 @pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
-def test_attend_decode_parity_and_invariance(kind, sink_profile):
+def test_attend_decode_parity_and_invariance(kind, sink_profile, act):
+    """FP8 records at the production head shape, bf16 or fp32 activations:
+    HI and LO give the same bytes, batch order and size do not change a
+    query's result, and every head is close to the oracle."""
     ctx = [5, 130, 1000, 5000, 128, 4097]
-    cfg, oc, cache, ents, wins = _fill_attention_case(kind, ctx, seed=4)
+    cfg, oc, cache, ents, wins = _fill_attention_case(kind, ctx, seed=4, act=act)
     nq = len(ctx)
     pos = [c - 1 for c in ctx]
     q, _, _ = synth.decode_queries(synth.CSA_DECODE_128K, nq, sub=4)
-    qt, qx = Hh.act_tensor(q, B.DSV4_DT_BF16)
+    qt, qx = Hh.act_tensor(q, act)
+    odt, bits = (torch.bfloat16, torch.int16) if act == B.DSV4_DT_BF16 else (torch.float32, torch.int32)
     sinks = _sinks(sink_profile)
     st = torch.from_numpy(sinks).to(Hh.DEV)
     csa = kind == B.DSV4_CSA
@@ -300,7 +305,7 @@ def test_attend_decode_parity_and_invariance(kind, sink_profile):
     tk = Hh.i32(topk)
 
     def run(rows, policy):
-        o = torch.empty((len(rows), oc.n_heads, oc.d), dtype=torch.bfloat16, device=Hh.DEV)
+        o = torch.empty((len(rows), oc.n_heads, oc.d), dtype=odt, device=Hh.DEV)
         if csa:
             B.dsv4_csa_attend_decode(cfg, cache, qt[rows].contiguous(), Hh.i32(rows), Hh.i32([pos[r] for r in rows]),
                                      tk[rows].contiguous(), st, o, policy)
@@ -313,15 +318,15 @@ def test_attend_decode_parity_and_invariance(kind, sink_profile):
     lo = run(rows, B.DSV4_POLICY_LO)
     hi = run(rows, B.DSV4_POLICY_HI)
     torch.cuda.synchronize()
-    assert torch.equal(lo.view(torch.int16), hi.view(torch.int16)), "HI and LO kernels differ"
+    assert torch.equal(lo.view(bits), hi.view(bits)), "HI and LO kernels differ"
     # batch invariance: alone, and in a permuted batch
     perm = [3, 0, 5, 2, 4, 1]
     pm = run(perm, B.DSV4_POLICY_LO)
     for i, r in enumerate(perm):
-        assert torch.equal(pm[i].view(torch.int16), lo[r].view(torch.int16))
+        assert torch.equal(pm[i].view(bits), lo[r].view(bits))
     for r in (0, 3):
         alone = run([r], B.DSV4_POLICY_HI)
-        assert torch.equal(alone[0].view(torch.int16), lo[r].view(torch.int16))
+        assert torch.equal(alone[0].view(bits), lo[r].view(bits))
     # oracle
     got = lo.to(torch.float64).cpu().numpy()
     for r, t in enumerate(pos):
