@@ -249,7 +249,8 @@ dsv4_status dsv4_compress_kv_prefill(const dsv4_cfg *cfg, const dsv4_cache *cach
  * to topk_dev[b][0..k), padded with -1.  Sources: vastsailsolution.com CSA
  * section (indexer: query projected into ReLU index heads scored against the
  * compressed index keys; top-k); xiaoyuzhoufm.com 1.1 (CSA applies DSA).
- *   qI [B][idx_heads][idx_dim] act dtype;  w_dev [B][idx_heads] fp32 (NULL = all ones)
+ *   qI [B][idx_heads][idx_dim] act dtype, 16-byte aligned (else
+ *   DSV4_ERR_INVALID_ARG);  w_dev [B][idx_heads] fp32 (NULL = all ones)
  *   ws_dev / ws_bytes: workspace of at least
  *   dsv4_workspace_bytes(cfg, B, max_blocks*128/m).
  */
@@ -276,7 +277,8 @@ dsv4_status dsv4_index_topk_decode_noalloc(const dsv4_cfg *cfg, const dsv4_cache
                                            int32_t B, int32_t *topk_dev, void *stream);
 
 /* Same for the packed queries of a prefill chunk (positions pos0 + offset);
- * topk_dev is [total_tokens][k]. */
+ * qI is [total_tokens][idx_heads][idx_dim] (16-byte aligned), topk_dev is
+ * [total_tokens][k]. */
 dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache,
                                     const void *qI, const float *w_dev,
                                     const int32_t *cu_seqlens_dev, const int32_t *req_dev,

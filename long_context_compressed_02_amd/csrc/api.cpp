@@ -248,11 +248,13 @@ static dsv4_status index_topk_common(const Lay &L, const dsv4_cache *cache, cons
         e = launch_score_f32(L, *cache, qI, w, req_q, pos_q, nq, W, s);
     } else {
         if (L.epb < 16) return DSV4_ERR_UNSUPPORTED;   // scoring reads 16-key runs inside one block
-        e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
-        if (e != hipSuccess) return DSV4_ERR_LAUNCH;
+        if (prefill) {                             // (decode quantises the queries inside the scorer)
+            e = launch_quant_q(L, qI, w, nq * L.HI, W, s);
+            if (e != hipSuccess) return DSV4_ERR_LAUNCH;
+        }
         Timed tm(timed ? DSV4_K_INDEX_SCORE : -1, s);
         e = prefill ? launch_score_prefill(L, *cache, req_q, pos_q, nq, W, s)
-                    : launch_score_decode(L, *cache, req_q, pos_q, nq, W, s);
+                    : launch_score_decode(L, *cache, qI, w, req_q, pos_q, nq, W, s);
     }
     if (e != hipSuccess) return DSV4_ERR_LAUNCH;
     Timed tm(timed ? DSV4_K_TOPK : -1, s);
@@ -270,7 +272,7 @@ dsv4_status dsv4_index_topk_decode(const dsv4_cfg *cfg, const dsv4_cache *cache,
     if (B < 0) return DSV4_ERR_INVALID_ARG;
     if (B == 0) return DSV4_OK;
     if (B > kMaxGridRows) return DSV4_ERR_UNSUPPORTED;
-    if (!qI || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
+    if (!qI || !aligned16(qI) || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
     if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
     return index_topk_common(L, cache, qI, w_dev, req_dev, pos_dev, B, topk_dev, (uint8_t *)ws_dev, ws_bytes,
                              S(stream), false);
@@ -318,7 +320,7 @@ dsv4_status dsv4_index_topk_decode_noalloc(const dsv4_cfg *cfg, const dsv4_cache
     if (B < 0) return DSV4_ERR_INVALID_ARG;
     if (B == 0) return DSV4_OK;
     if (B > kMaxGridRows) return DSV4_ERR_UNSUPPORTED;
-    if (!qI || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
+    if (!qI || !aligned16(qI) || !req_dev || !pos_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
     const int64_t need = index_ws_bytes(L, B, (int64_t)cache->max_blocks * L.epb, nullptr, nullptr);
     if (need > kNoAllocScratch) return DSV4_ERR_WORKSPACE;
     uint8_t *ws = nullptr;
@@ -337,7 +339,7 @@ dsv4_status dsv4_index_topk_prefill(const dsv4_cfg *cfg, const dsv4_cache *cache
     if ((st = check_cache(L, cache, DSV4_CSA)) != DSV4_OK) return st;
     if (n_seq < 0 || total_tokens < 0) return DSV4_ERR_INVALID_ARG;
     if (n_seq == 0 || total_tokens == 0) return DSV4_OK;
-    if (!qI || !cu_seqlens_dev || !req_dev || !pos0_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
+    if (!qI || !aligned16(qI) || !cu_seqlens_dev || !req_dev || !pos0_dev || !topk_dev) return DSV4_ERR_INVALID_ARG;
     if (!ws_dev || ws_bytes <= 0 || ((uintptr_t)ws_dev & 255)) return DSV4_ERR_WORKSPACE;
     // per-query (request, position) rows first, then groups of queries that fit
     const int64_t rows_bytes = al((int64_t)total_tokens * 8, 256);

@@ -27,40 +27,65 @@ namespace dsv4 {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- query quantisation
-// One wave per (query, head) row, into a 128-byte slot: E4M3 codes (zero-
-// padded to 128 bytes) and wq = w * scale, or (MXFP4) 64 bytes of E2M1 codes
-// (zero past dI), the word of E8M0 block scales at byte 64, and wq = w.  Same
-// decision rule as the stored index keys.
-__global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, const float *w,
-                                                       int rows, uint8_t *q8, float *wq) {
+// One (query, head) row held by a wave, lane l holding values 2l and 2l+1
+// (zero past dI), into a 128-byte slot: E4M3 codes (zero-padded to 128 bytes)
+// and wq = w * scale, or (MXFP4) 64 bytes of E2M1 codes (zero past dI), the
+// word of E8M0 block scales at byte 64, and wq = w.  Same decision rule as the
+// stored index keys.  Returns wq (every lane); the slot may be global or LDS.
+// MX: the rows are MXFP4 (else E4M3).
+template <bool MX>
+__device__ __forceinline__ float quant_q_row(const Lay &L, float x0, float x1, float wrow, uint8_t *slot) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
     const int dI = L.dI;
-    float x0 = 2 * lane < dI ? load_act(qI, row * dI + 2 * lane, L.act) : 0.0f;
-    float x1 = 2 * lane + 1 < dI ? load_act(qI, row * dI + 2 * lane + 1, L.act) : 0.0f;
-    if (L.idx_store == DSV4_STORE_MXFP4) {
+    if constexpr (MX) {
         uint32_t scales;
         const uint32_t byte = mx4_row(x0, x1, 2 * lane < dI, 2 * lane + 1 < dI, &scales);
-        q8[row * 128 + lane] = (uint8_t)byte;
-        if (lane == 0) {
-            *(uint32_t *)(q8 + row * 128 + 64) = scales;
-            wq[row] = w ? w[row] : 1.0f;
-        }
-        return;
+        slot[lane] = (uint8_t)byte;
+        if (lane == 0) *(uint32_t *)(slot + 64) = scales;
+        return wrow;
     }
-    float am = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    float scale = 1.0f, inv = 1.0f;
-    if (am >= 1e-30f) {
-        scale = am / 448.0f;
-        inv = 448.0f / am;
-    }
+    const float am = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const bool nz = am >= 1e-30f;                  // (a row of zeros keeps scale 1)
+    const float scale = nz ? am / 448.0f : 1.0f;
+    const float inv = nz ? 448.0f / am : 1.0f;
     uint32_t c0 = 2 * lane < dI ? fp8_code(x0 * inv) : 0u;
     uint32_t c1 = 2 * lane + 1 < dI ? fp8_code(x1 * inv) : 0u;
-    *(uint16_t *)(q8 + row * 128 + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
-    if (lane == 0) wq[row] = (w ? w[row] : 1.0f) * scale;
+    *(uint16_t *)(slot + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+    return wrow * scale;
+}
+
+// The lane's two values of row `row` of qI (zero past dI).  Two 4-byte loads
+// whatever the activation type (a bf16 pair is one word, read twice; an fp32
+// pair two), at addresses clamped into the row for lanes past its end: no
+// load sits under a branch, so the compiler's memory-counter waits stay exact.
+__device__ __forceinline__ void load_q_pair(const Lay &L, const void *qI, int64_t row, float &x0, float &x1) {
+    const int lane = threadIdx.x & 63;
+    const int dI = L.dI;
+    const bool f32 = L.act != DSV4_DT_BF16;
+    const int64_t i = row * dI + (2 * lane < dI ? 2 * lane : 0);
+    const uint32_t *p = (const uint32_t *)((const uint8_t *)qI + i * (f32 ? 4 : 2));
+    const uint32_t u0 = p[0], u1 = p[f32 ? 1 : 0];
+    x0 = __uint_as_float(f32 ? u0 : u0 << 16);
+    x1 = __uint_as_float(f32 ? u1 : u0 & 0xffff0000u);
+    x0 = 2 * lane < dI ? x0 : 0.0f;
+    x1 = 2 * lane + 1 < dI ? x1 : 0.0f;
+}
+
+// One wave per (query, head) row (prefill batches; decode quantises inside
+// the scoring kernel).
+__global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, const float *w,
+                                                       int rows, uint8_t *q8, float *wq) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    float x0, x1;
+    load_q_pair(L, qI, row, x0, x1);
+    const float wr = w ? w[row] : 1.0f;
+    const float v = L.idx_store == DSV4_STORE_MXFP4 ? quant_q_row<true>(L, x0, x1, wr, q8 + row * 128)
+                                                    : quant_q_row<false>(L, x0, x1, wr, q8 + row * 128);
+    if ((threadIdx.x & 63) == 0) wq[row] = v;
 }
 
 // p(l) + p(l^16) + p(l^32) + p(l^48) as (p(l) + p(l^16)) + (p(l^32) + p(l^48)):
@@ -108,18 +133,44 @@ static_assert(kKeysPerWave % 64 == 0, "scoring ranges are whole pipeline groups"
 // the MFMA returns sum_b 2^(xq_b + xk_b) * (codes of block b . codes of block
 // b) (exact products, fp32 sums): the dot product of the stored values.  The
 // head weights then apply as they are (wq = w).
+// The query rows are quantised inside the kernel: wave w < HB quantises heads
+// [16w, 16w+16) of the workgroup's query (the same operations as
+// k_quant_index_q, so the same codes and weights) into LDS, while the first
+// keys are already on their way.
 template <int HB, bool FULL, bool F4>
-__global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C, const uint8_t *q8,
-                                                            const float *wq, const int32_t *req,
+__global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C, const void *qI,
+                                                            const float *w, const int32_t *req,
                                                             const int32_t *pos, float *scores,
                                                             int64_t ld, uint2 *wr, int nwr) {
     const int q = blockIdx.y;
     const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);    // wave-uniform (scalar)
+    // this wave's query rows first (their addresses need nothing else)
+    // (MXFP4) wave w < HB holds heads [16w, 16w+16), two values a lane, the
+    // layout of the separate quantiser; (E4M3) thread 4h + c holds dims
+    // [32c, 32c+32) of head h: eight 16-byte loads (a bf16 quarter row takes
+    // four, read twice), every address clamped into the query's rows
+    constexpr int NQL = F4 ? 16 : 8;
+    float qx0[F4 ? 16 : 1], qx1[F4 ? 16 : 1];
+    u32x4 qv[F4 ? 1 : 8];
+    if constexpr (F4) {
+#pragma unroll
+        for (int i = 0; i < NQL; ++i) {
+            const int h = (wave < HB ? wave * 16 : 0) + i;
+            load_q_pair(L, qI, (int64_t)q * L.HI + (h < L.HI ? h : 0), qx0[i], qx1[i]);
+        }
+    } else {
+        const int h = threadIdx.x >> 2, c = threadIdx.x & 3;
+        const bool f32 = L.act != DSV4_DT_BF16;
+        const int64_t e0 = ((int64_t)q * L.HI + (h < L.HI ? h : 0)) * L.dI + (32 * c < L.dI ? 32 * c : 0);
+        const uint8_t *p = (const uint8_t *)qI + e0 * (f32 ? 4 : 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qv[k] = *(const u32x4 *)(p + 16 * (f32 ? k : (k & 3)));
+    }
     const int r = req[q];
     const int t = pos[q];
     if (r < 0 || r >= C.n_req || t < 0 || (int64_t)t >= (int64_t)C.max_blocks * kBlockTokens) return;
-    const int N = (t + 1) / L.m;
+    const int N = (t + 1) >> __builtin_ctz((uint32_t)L.m);   // (m is a power of two)
     const int k0 = (blockIdx.x * 4 + wave) * kKeysPerWave;
     const int dI = L.dI;
     // k-order of the 16x16x128 operands: lane group g holds bytes [16g, 16g+16)
@@ -128,35 +179,12 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     const int o0 = 16 * g, o1 = 64 + 16 * g;
     const bool v0 = FULL || o0 < dI, v1 = FULL || o1 < dI;   // chunks holding real bytes
     const i32x4 z4 = {0, 0, 0, 0};
-    // A operand: query codes (zero-padded to 128 bytes per row), rows = index heads
-    i32x8 A[HB];
-    uint32_t sa[HB];                               // (MXFP4) the lane's block scale per head block
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        const int row = hb * 16 + c16;
-        const bool ok = row < L.HI;
-        const uint8_t *p = q8 + ((int64_t)q * L.HI + (ok ? row : 0)) * 128;
-        i32x8 a;
-        if constexpr (F4) {
-            a.lo = *(const i32x4 *)(p + 16 * g);
-            a.hi = z4;
-            sa[hb] = ok ? (*(const uint32_t *)(p + 64) >> (8 * g)) & 0xffu : 0u;
-        } else {
-            a.lo = *(const i32x4 *)(p + o0);
-            a.hi = *(const i32x4 *)(p + o1);
-            sa[hb] = 127u;
-        }
-        A[hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    // head weights in LDS (registers are kept for the operands: at 96 VGPRs or
-    // fewer five waves share a SIMD, and a whole decode batch is resident at once)
+    // the quantised query rows (filled below): codes in LDS, the head weights
+    // times the row scales in LDS, and the A operands read back from there
+    __shared__ __attribute__((aligned(16))) uint8_t qsl[HB * 16 * 128];
     __shared__ f32x4 wls[HB * 4];                  // [hb][g]: heads hb*16 + 4g + i
-    if (threadIdx.x < HB * 16) {
-        const int h = threadIdx.x;
-        ((float *)wls)[h] = h < L.HI ? wq[(int64_t)q * L.HI + h] : 0.0f;
-    }
-    __syncthreads();
-    if (k0 >= N) return;                           // (after the barrier: every wave takes part in it)
+    i32x8 A[HB];                                   // rows = index heads (zero past idx_heads)
+    uint32_t sa[HB];                               // (MXFP4) the lane's block scale per head block
     const int32_t *btr = C.block_table + (int64_t)r * C.max_blocks;
     const int lane_off = c16 * L.key_bytes;
     const uint8_t *pool = (const uint8_t *)C.index_keys;
@@ -246,6 +274,81 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
     uint32_t e0[GS], e1[GS];
 #pragma unroll
     for (int i = 0; i < GS; ++i) load_sb(k0 + 16 * i, B0[i], s0[i], e0[i]);
+    // ---- the query rows: codes and weighted scales into LDS (rows past
+    // idx_heads get weight 0 and are never read)
+    if constexpr (F4) {
+        if (wave < HB) {                           // (uniform)
+#pragma unroll
+            for (int i = 0; i < NQL; ++i) {
+                const int h = wave * 16 + i;
+                float v = 0.0f;
+                if (h < L.HI) {                    // (uniform)
+                    const int64_t row = (int64_t)q * L.HI + h;
+                    v = quant_q_row<true>(L, qx0[i], qx1[i], w ? w[row] : 1.0f, qsl + h * 128);
+                }
+                if (lane == 0) ((float *)wls)[h] = v;
+            }
+        }
+    } else {
+        // E4M3, the decision rule of quant_q_row: the row's largest magnitude
+        // (max over its four threads: exact in any order), scale = amax / 448,
+        // codes of x * (448 / amax), wq = w * scale
+        const int h = threadIdx.x >> 2, c = threadIdx.x & 3;
+        const bool f32 = L.act != DSV4_DT_BF16;
+        float x[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const uint32_t wf = qv[k >> 2][k & 3];                  // fp32: value k
+            const uint32_t wb = qv[k >> 3][(k >> 1) & 3];           // bf16: value k in half k & 1
+            const float v = __uint_as_float(f32 ? wf : ((k & 1) ? (wb & 0xffff0000u) : (wb << 16)));
+            x[k] = 32 * c + k < dI ? v : 0.0f;
+        }
+        float am = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) am = fmaxf(am, fabsf(x[k]));
+        am = fmaxf(am, __shfl_xor(am, 1));
+        am = fmaxf(am, __shfl_xor(am, 2));
+        const bool nz = am >= 1e-30f;
+        const float scale = nz ? am / 448.0f : 1.0f;
+        const float inv = nz ? 448.0f / am : 1.0f;
+        if (h < HB * 16) {
+            uint32_t wd[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                uint32_t u = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int d = 32 * c + 4 * k + b;
+                    u |= (d < dI ? fp8_code(x[4 * k + b] * inv) : 0u) << (8 * b);
+                }
+                wd[k] = u;
+            }
+            uint4 *dst = (uint4 *)(qsl + h * 128 + 32 * c);
+            dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+            if (c == 0) ((float *)wls)[h] = h < L.HI ? (w ? w[(int64_t)q * L.HI + h] : 1.0f) * scale : 0.0f;
+        }
+    }
+    __syncthreads();
+    // A operand: query codes (zero-padded to 128 bytes per row)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int row = hb * 16 + c16;
+        const bool ok = row < L.HI;
+        const uint8_t *p = qsl + (ok ? row : 0) * 128;
+        i32x8 a;
+        if constexpr (F4) {
+            a.lo = *(const i32x4 *)(p + 16 * g);
+            a.hi = z4;
+            sa[hb] = ok ? (*(const uint32_t *)(p + 64) >> (8 * g)) & 0xffu : 0u;
+        } else {
+            a.lo = *(const i32x4 *)(p + o0);
+            a.hi = *(const i32x4 *)(p + o1);
+            sa[hb] = 127u;
+        }
+        A[hb] = ok ? a : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if (k0 >= N) return;                           // (after the barrier: every wave takes part in it)
 #pragma unroll
     for (int grp = 0; grp < NG; grp += 2) {
         const int kg = k0 + grp * GS * 16;
@@ -1341,13 +1444,13 @@ hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows
     return hipGetLastError();
 }
 
-hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
-                               int n, const IndexWs &ws, hipStream_t s) {
+hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const void *qI, const float *w,
+                               const int32_t *req, const int32_t *pos, int n, const IndexWs &ws, hipStream_t s) {
     dim3 g((unsigned)((ws.ld + kKeysPerWG - 1) / kKeysPerWG), n);
     const int hb = (L.HI + 15) / 16;
     const bool full = L.dI == 128;
 #define DSV4_SCORE(HBV, FV, F4V) \
-    hipLaunchKernelGGL((k_index_score_decode<HBV, FV, F4V>), g, dim3(256), 0, s, L, C, ws.q8, ws.wq, req, pos, ws.scores, \
+    hipLaunchKernelGGL((k_index_score_decode<HBV, FV, F4V>), g, dim3(256), 0, s, L, C, qI, w, req, pos, ws.scores, \
                        ws.ld, ws.wr, ws.nwr)
 #define DSV4_SCORE_HB(FV, F4V)                \
     do {                                      \

@@ -56,8 +56,8 @@ struct IndexWs {
 int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base);
 hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows, const IndexWs &ws,
                           hipStream_t s);
-hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
-                               int n, const IndexWs &ws, hipStream_t s);
+hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const void *qI, const float *w,
+                               const int32_t *req, const int32_t *pos, int n, const IndexWs &ws, hipStream_t s);
 // The same scores for the packed rows of a prefill chunk (rows of one request
 // in index order share their key loads).
 hipError_t launch_score_prefill(const Lay &L, const dsv4_cache &C, const int32_t *req, const int32_t *pos,
