@@ -80,11 +80,14 @@ typedef int32_t dsv4_status;
 
 /* decode kernel policy (the two kernels give bitwise identical results) */
 #define DSV4_POLICY_AUTO 0
-#define DSV4_POLICY_HI 1         /* for a saturated GPU: per (query, 16-head group) one workgroup of
-                                    2 waves (one per half of the dims) taking the record subsets in
-                                    turn, so that several workgroups share a compute unit */
+#define DSV4_POLICY_HI 1         /* for a saturated GPU: d = 512: per (query, four 16-head groups)
+                                    one workgroup of 8 waves (head group x half of the dims) taking
+                                    the record subsets in turn, each record loaded and converted to
+                                    bf16 once per workgroup; other d: per (query, 16-head group) 2
+                                    waves.  Prefill always runs this layout. */
 #define DSV4_POLICY_LO 2         /* for an unsaturated GPU: per (query, 16-head group) one workgroup
-                                    of 4 waves, one per record subset, over all dims */
+                                    of 8 waves (record subset x half of the dims; lists up to 2048
+                                    records at d = 512) or 4 waves (one per subset, over all dims) */
 
 /* cache-write / read-back targets */
 #define DSV4_TARGET_ENTRY 0

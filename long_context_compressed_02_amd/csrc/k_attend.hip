@@ -1703,6 +1703,418 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
     else part_body(std::integral_constant<int, 1>());
 }
 
+// ---------------------------------------------------------------- the HI kernel, shared records (d = 512)
+// For a saturated GPU (prefill chunks, large batches): one workgroup of eight
+// waves per (query, four 16-head groups), wave (h, q) reducing head group h
+// over dim part q with the subsets one after another, exactly as k_attend's
+// two waves do -- the same partial dot products in the same order, the same
+// exchange, online softmax and left-to-right fold -- so the kernels agree bit
+// for bit.  What changes is where the records come from: a chunk is loaded
+// once per workgroup by all its threads, its E4M3 codes converted to bf16 once
+// (exactly) and staged in LDS, and the four head groups' waves read it there:
+// the key operands of S^T = K Q^T as 16-byte reads, the transposed operands of
+// O^T += V^T P^T with ds_read_b64_tr_b16 for every dim.  Two chunk buffers:
+// while one chunk is computed on, the next is converted into the other buffer
+// and the one after that is loaded.  (Measured on the 8K prefill chunk: 4.03
+// ms against 4.42 ms for k_attend; with two head groups per workgroup, two
+// workgroups sharing a compute unit, 4.27 ms.)
+template <int D, int DR>
+struct HqShape {
+    using Sh = AttnShape<D, DR>;
+    static constexpr int NHQ = 4;                              // head groups per workgroup
+    static constexpr int NT = 64 * kParts * NHQ;               // threads
+    static constexpr int TPR = NT / kChunk;                    // staging threads per record
+    static constexpr int NLP = 32 / TPR + 1;                   // pieces each loads: 32 / TPR, then one of 32..CREC-1
+    static constexpr int BPR = 2 * Sh::NCH + Sh::RCH;          // bf16 pieces of a staged record
+    // A record's row holds its BPR pieces; piece c of record r sits at column
+    // c ^ swz(r), swz(r) = 2 (r mod 8) + (r / 8 mod 2).  With 64 LDS banks (16
+    // pieces) the 16 records a key-operand read serves per clock then cover
+    // all banks, and so do the 8 records x 2 pieces of a transposed read.
+    static constexpr int RSH = BPR;
+    static constexpr int BUFH = kChunk * RSH * 16;             // one chunk buffer
+    static constexpr int XOFF = 2 * BUFH + 2 * kChunk * 4;     // the buffers, then their record scales
+    static constexpr int LOFF = XOFF + NHQ * (kParts + 1) * Sh::XW * 4;
+    static __host__ __device__ int64_t lds_bytes(int64_t list_max) {
+        return LOFF + (list_max * 4 + 15) / 16 * 16 + ((list_max + kChunk - 1) / kChunk * 4 + 15) / 16 * 16;
+    }
+    static_assert(Sh::CREC > 32 && Sh::CREC - 32 <= TPR, "the last load of each thread covers pieces 32..CREC-1");
+    static_assert(BPR % 16 == 0, "the column swizzle stays inside the row");
+    static_assert(BUFH % 16 == 0 && XOFF % 16 == 0 && LOFF % 16 == 0, "alignment");
+};
+
+template <int D, int DR, bool CSA, bool PREFILL, bool F32A>
+__global__ __launch_bounds__((HqShape<D, DR>::NT)) __attribute__((amdgpu_waves_per_eu(2))) void k_attend_hq(AttnArgs A) {
+    using Sh = AttnShape<D, DR>;
+    using HS = HqShape<D, DR>;
+    constexpr int NCH = Sh::NCH, RCH = Sh::RCH, CREC = Sh::CREC, KP = Sh::KP, KR = Sh::KR, QPP = Sh::QPP;
+    constexpr int NDB = Sh::NDB, DBQ = Sh::DBQ, XW = Sh::XW, DN = Sh::DN, NHQ = HS::NHQ;
+    constexpr int RSH = HS::RSH, BUFH = HS::BUFH, TPR = HS::TPR, NLP = HS::NLP;
+    constexpr int NT = HS::NT;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ float2 rope_tab[DR / 2];
+    __shared__ int32_t safe_sh;
+
+    const Lay &L = A.L;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar registers)
+    const int dq = wave & 1, hq = wave >> 1;                      // dim part, head group in the workgroup
+
+    // ---- which query and head groups (a query's workgroups are dealt onto
+    // one XCD: workgroup ids go round-robin over the 8 XCDs)
+    const int nhq = (A.nhg + NHQ - 1) / NHQ;
+    const int lin = blockIdx.x, x8 = lin & 7, u8 = lin >> 3;
+    const int qi = (u8 / nhq) * 8 + x8;
+    const int hg = (u8 % nhq) * NHQ + hq;
+    if (qi >= A.nq) return;
+    const QueryInfo Q = query_info<CSA, PREFILL>(A, qi);
+    if (!Q.ok) return;
+    const int head = hg * 16 + c16;
+    const bool head_ok = hg < A.nhg && head < L.H;
+
+    // LDS: two chunk buffers (bf16 records), their scales, one partial-logit
+    // exchange per head group, the record locators and valid masks
+    float *scl = (float *)(smem + 2 * BUFH);                     // [buffer][record]
+    float *xch = (float *)(smem + HS::XOFF) + hq * (kParts + 1) * XW;
+    int32_t *locs = (int32_t *)(smem + HS::LOFF);
+    const int loc_bytes = ((int)Q.n_list * 4 + 15) / 16 * 16;
+    uint32_t *vmask = (uint32_t *)(smem + HS::LOFF + loc_bytes);   // [chunk]: bit r = record r usable
+
+    // ---- resolve every record of the list once; any valid record stands in
+    // for masked ones (its bytes are loaded, its weight is 0)
+    if (tid == 0) safe_sh = -1;
+    __syncthreads();
+    int32_t last_ok = -1;
+    for (int64_t p0 = (int64_t)wave * 64; p0 < Q.n_list; p0 += NT) {   // wave-uniform: 64 consecutive records
+        const int64_t p = p0 + lane;
+        const int32_t lc = p < Q.n_list ? record_loc<CSA, PREFILL>(A, Q, p) : kMasked;
+        if (p < Q.n_list) locs[p] = lc;
+        if (lc != kMasked) last_ok = (int32_t)p;
+        const uint64_t vb = __builtin_amdgcn_ballot_w64(lc != kMasked);
+        if (lane == 0) {
+            vmask[p0 / kChunk] = (uint32_t)vb;
+            if (p0 + kChunk < Q.n_list) vmask[p0 / kChunk + 1] = (uint32_t)(vb >> 32);
+        }
+    }
+    if (last_ok >= 0) atomicMax(&safe_sh, last_ok);
+    if (tid < DR / 2) {
+        float c, sn;
+        rope_cs(L, Q.t, tid, c, sn);
+        rope_tab[tid] = make_float2(c, sn);
+    }
+    __syncthreads();
+    const int32_t safe = safe_sh >= 0 ? locs[safe_sh] : kMasked;
+    const int n_list = (int)Q.n_list;                // (lists are far below 2^31 records)
+    const int nchunks = safe == kMasked ? 0 : (n_list + kChunk - 1) / kChunk;
+
+    // ---- chunk staging by all threads: thread t loads pieces j + TPR k
+    // (k < 32 / TPR) and 32 + min(j, CREC - 33) of record t / TPR (j = t mod
+    // TPR; the last load of threads j > CREC - 33 repeats the scale piece and
+    // is not stored), converts the code pieces to bf16 and writes them to the
+    // chunk buffer: bf16 piece 2c + h of a record holds dims 16c + 8h .. +8 of
+    // code piece c, bf16 piece 2 NCH + k its RoPE piece k
+    const int sr = tid / TPR, sj = tid % TPR;
+    auto piece_of = [&](int k) { return k < NLP - 1 ? sj + TPR * k : 32 + (sj < CREC - 33 ? sj : CREC - 33); };
+    auto hslot = [&](int b, int c, int r) {
+        return smem + b * BUFH + (r * RSH + (c ^ (2 * (r & 7) + ((r >> 3) & 1)))) * 16;
+    };
+    auto issue = [&](u32x4 (&pre)[NLP], int ck) {
+        const int p = ck * kChunk + sr;
+        int32_t lc = locs[p < n_list ? p : n_list - 1];   // (no branch around the LDS read)
+        if (p >= n_list || lc == kMasked) lc = safe;
+        const uint8_t *rec = loc_addr<PREFILL>(A, Q, lc);
+#pragma unroll
+        for (int k = 0; k < NLP; ++k) pre[k] = *(const u32x4 *)(rec + 16 * piece_of(k));
+    };
+    auto stage = [&](const u32x4 (&pre)[NLP], int b) {
+#pragma unroll
+        for (int k = 0; k < NLP; ++k) {
+            const int pc = piece_of(k);
+            const u32x4 u = pre[k];
+            if (pc < NCH) {
+                union { bf16x8 b; u32x4 v; } lo, hi;
+                lo.b = cvt8(u[0], u[1]);
+                hi.b = cvt8(u[2], u[3]);
+                // threads of odd record / upper half store their odd piece
+                // first: each store of 16 lanes then spreads over the banks
+                const bool sw8 = ((sj >= TPR / 2) ^ (sr & 1)) != 0;
+                *(u32x4 *)hslot(b, 2 * pc + (sw8 ? 1 : 0), sr) = sw8 ? hi.v : lo.v;
+                *(u32x4 *)hslot(b, 2 * pc + (sw8 ? 0 : 1), sr) = sw8 ? lo.v : hi.v;
+            } else if (pc < NCH + RCH) {
+                *(u32x4 *)hslot(b, NCH + pc, sr) = u;
+            } else if (k == NLP - 1 && sj == CREC - 33) {
+                scl[b * kChunk + sr] = __uint_as_float(u[0]);
+            }
+        }
+    };
+
+    static_assert(kParts == 2, "the part dispatch below covers two parts");
+    auto part_body = [&](auto dqc) {
+        constexpr int DQ = decltype(dqc)::value;
+        // ---- query fragments of this dim part (B operand of S^T = K Q^T), lane
+        // (head c16, group g): code pair kp reads piece 4kp+g, dims 16(4kp+g) +
+        // [0,8) and [8,16); RoPE step ks reads RoPE piece 4ks+g, rotated at t.
+        bf16x8 Qn[QPP][2], Qr[KR];
+        {
+            const int64_t qbase = ((int64_t)Q.qrow * L.H + (head_ok ? head : 0)) * D;
+            auto q8 = [&](int dd, float (&v)[8]) {
+                if constexpr (!F32A) {
+                    const uint4 u = *(const uint4 *)((const uint16_t *)A.q + qbase + dd);
+                    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        v[2 * j] = __uint_as_float(w[j] << 16);
+                        v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                    }
+                } else {
+                    const float4 a = *(const float4 *)((const float *)A.q + qbase + dd);
+                    const float4 b = *(const float4 *)((const float *)A.q + qbase + dd + 4);
+                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+                }
+            };
+#pragma unroll
+            for (int e = 0; e < QPP; ++e) {
+                const int kp = QPP * DQ + e, ch = 4 * kp + g;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (head_ok && kp < KP && ch < NCH) q8(16 * ch + 8 * h, v);
+                    bf16x8 f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) f[j] = f2bf(v[j]);
+                    Qn[e][h] = f;
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KR; ++ks) {
+                const int ch = 4 * ks + g;
+                float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (head_ok && DQ == kParts - 1 && ch < RCH) q8(DN + 8 * ch, v);
+                bf16x8 f;
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    float a = 0.0f, b = 0.0f;
+                    if (ch < RCH) {
+                        const float2 cs = rope_tab[(8 * ch + j) / 2];
+                        a = v[j] * cs.x - v[j + 1] * cs.y;
+                        b = v[j] * cs.y + v[j + 1] * cs.x;
+                    }
+                    f[j] = f2bf(a);
+                    f[j + 1] = f2bf(b);
+                }
+                Qr[ks] = f;
+            }
+        }
+        const float tau2 = L.tau * 1.4426950408889634f;   // logits in base 2
+
+        // ---- this part's partial logits of the chunk in buffer b (k_attend's
+        // chains: code pairs in order, then the RoPE steps); rows = records
+        // 16rb + 4g + i, lane column = head c16
+        auto partial = [&](float (&an)[2][4], float (&ar)[2][4], int b) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, bb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int e = 0; e < QPP; ++e) {
+                    const int kp = QPP * DQ + e, ch = 4 * kp + g;
+                    if (kp < KP) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            union { u32x4 v; bf16x8 b; } cv;
+                            cv.v = (u32x4){0, 0, 0, 0};
+                            if (NCH % 4 == 0 || ch < NCH) cv.v = *(const u32x4 *)hslot(b, 2 * ch + h, 16 * rb + c16);
+                            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Qn[e][h], a, 0, 0, 0);
+                        }
+                    }
+                }
+                if (DQ == kParts - 1) {
+#pragma unroll
+                    for (int ks = 0; ks < KR; ++ks) {
+                        const int ch = 4 * ks + g;
+                        union { u32x4 v; bf16x8 b; } cv;
+                        cv.v = (u32x4){0, 0, 0, 0};
+                        if (RCH % 4 == 0 || ch < RCH) cv.v = *(const u32x4 *)hslot(b, 2 * NCH + ch, 16 * rb + c16);
+                        bb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, Qr[ks], bb, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    an[rb][i] = a[i];
+                    ar[rb][i] = bb[i];
+                }
+                __builtin_amdgcn_sched_barrier(0);   // one record block's operands at a time
+            }
+        };
+
+        // ---- the rest of a chunk step, after the partials are exchanged: logits,
+        // online softmax, O^T += V^T P^T on this part's dim blocks
+        auto finish = [&](auto &S, int ck, int b) {
+            constexpr int NO = sizeof(S.O) / sizeof(S.O[0]);
+            float lg[2][4], sc[2][4];
+            const uint32_t vm = vmask[ck];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * rb + 4 * g + i, k = (rb * 4 + i) * 64 + lane;
+                    const bool ok = (vm >> r) & 1u;
+                    sc[rb][i] = scl[b * kChunk + r];
+                    float a = xch[k];
+#pragma unroll
+                    for (int q = 1; q < kParts; ++q) a = a + xch[q * XW + k];
+                    lg[rb][i] = ok ? tau2 * (sc[rb][i] * a + xch[kParts * XW + k]) : -INFINITY;
+                }
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, lg[rb][i]);
+            cmax = head_max(cmax);
+            const float m_new = lazy_max(S.m, cmax);
+            float p[2][4];
+            float alpha = 1.0f;
+            if (m_new == -INFINITY) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[rb][i] = 0.0f;
+            } else {
+                alpha = __builtin_amdgcn_exp2f(S.m - m_new);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) p[rb][i] = __builtin_amdgcn_exp2f(lg[rb][i] - m_new);
+            }
+            float ps = 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ps = ps + p[rb][i];
+            ps = head_sum(ps);
+            S.l = S.l * alpha + ps;
+            S.m = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // alpha == 1 leaves O as it is
+#pragma unroll
+                for (int i = 0; i < NO; ++i) S.O[i] = S.O[i] * alpha;
+            }
+            // k-slot j of lane group g is record 4g+j (j < 4) or 16+4g+(j-4)
+            bf16x8 Pn, Pr;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int rb = j >> 2, i = j & 3;
+                Pn[j] = f2bf(p[rb][i] * sc[rb][i]);
+                Pr[j] = f2bf(p[rb][i]);
+            }
+            // every dim from the bf16 rows: ds_read_b64_tr_b16 -- lanes 4r..4r+3
+            // address row r (record 4g+r, resp. 16+4g+r), 4 dims each; lane c16
+            // receives dim 16db + c16 of the 4 records
+            const int r16 = c16 >> 2, q16 = c16 & 3;
+#pragma unroll
+            for (int ii = 0; ii < NO; ++ii) {
+                if (ii % 8 == 0) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+                const int db = DBQ * DQ + ii;
+                if (db < NDB) {
+                    const int ch = 2 * db + (q16 >> 1);
+                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(hslot(b, ch, 4 * g + r16) + 8 * (q16 & 1)));
+                    i16x4 hi =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_p)(hslot(b, ch, 16 + 4 * g + r16) + 8 * (q16 & 1)));
+                    union { i16x4 s[2]; bf16x8 b; } cv;
+                    cv.s[0] = lo;
+                    cv.s[1] = hi;
+                    S.O[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cv.b, db < NCH ? Pn : Pr, S.O[ii], 0, 0, 0);
+                }
+            }
+        };
+
+        // ---- output rows d = 16db + 4g + i of head `head`, with the sink:
+        // out = O * f / (l * f + 2^(z - M)),  f = 2^(m - M),  M = max(m, z)
+        const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
+        auto emit = [&](float m, float l, int db, const f32x4 &o) {
+            const float z = A.sinks[head] * 1.4426950408889634f;
+            const float M = fmaxf(m, z);
+            const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            const float den = l * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
+            const float cf = den > 0.0f ? f / den : 0.0f;
+            const int dd = db * 16 + 4 * g;
+            if constexpr (!F32A) {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                const bf16x4 v = {f2bf(o[0] * cf), f2bf(o[1] * cf), f2bf(o[2] * cf), f2bf(o[3] * cf)};
+                *(bf16x4 *)((uint16_t *)A.out + obase + dd) = v;
+            } else {
+                *(float4 *)((float *)A.out + obase + dd) = make_float4(o[0] * cf, o[1] * cf, o[2] * cf, o[3] * cf);
+            }
+        };
+
+        // ---- the chunks in processing order: subset 0 (chunks 0, 4, 8, ...),
+        // then subsets 1, 2, 3, each subset's state folded into the
+        // accumulated one after its last chunk (empty subsets too, as k_attend
+        // folds them).  The accumulated state is not touched inside a
+        // subset's loop, so it is the one the compiler keeps out of registers
+        // there.
+        auto next_of = [&](int ck) {
+            if (ck + kSubsets < nchunks) return ck + kSubsets;
+            for (int s = ck % kSubsets + 1; s < kSubsets; ++s)
+                if (s < nchunks) return s;
+            return -1;
+        };
+        AttnState<DBQ> acc, cur;
+        state_clear(acc);
+        u32x4 pre[NLP];
+        int cn = nchunks > 0 ? 0 : -1;                   // the next chunk to compute
+        int cn1 = cn >= 0 ? next_of(cn) : -1;            // and the one after it
+        if (cn >= 0) {
+            issue(pre, cn);
+            stage(pre, 0);
+        }
+        if (cn1 >= 0) issue(pre, cn1);
+        __syncthreads();                                 // the first chunk staged
+        int b = 0;
+#pragma unroll 1
+        for (int s = 0; s < kSubsets; ++s) {
+            state_clear(cur);
+#pragma unroll 1
+            for (int ck = s; ck < nchunks; ck += kSubsets) {
+                const int cn2 = cn1 >= 0 ? next_of(cn1) : -1;
+                float an[2][4], ar[2][4];
+                partial(an, ar, b);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int k = (rb * 4 + i) * 64 + lane;
+                        xch[DQ * XW + k] = an[rb][i];
+                        if (DQ == kParts - 1) xch[kParts * XW + k] = ar[rb][i];
+                    }
+                if (cn1 >= 0) stage(pre, b ^ 1);         // the next chunk into the other buffer
+                if (cn2 >= 0) issue(pre, cn2);           // and the one after on its way
+                __syncthreads();                         // partials and the next chunk visible
+                finish(cur, ck, b);
+                __syncthreads();                         // buffer b and the exchange are free again
+                b ^= 1;
+                cn1 = cn2;
+            }
+            if (s == 0) {
+                acc = cur;
+            } else {
+                float m, l, fa, fb;
+                fold_scales(acc.m, acc.l, cur.m, cur.l, m, l, fa, fb);
+#pragma unroll
+                for (int i = 0; i < DBQ; ++i) acc.O[i] = fold_o(acc.O[i], fa, cur.O[i], fb);
+                acc.m = m;
+                acc.l = l;
+            }
+        }
+        if (head_ok) {
+#pragma unroll
+            for (int i = 0; i < DBQ; ++i)
+                if (DBQ * DQ + i < NDB) emit(acc.m, acc.l, DBQ * DQ + i, acc.O[i]);
+        }
+    };
+    if (dq == 0) part_body(std::integral_constant<int, 0>());
+    else part_body(std::integral_constant<int, kParts - 1>());
+}
+
 // ---------------------------------------------------------------- fp32 records
 // Records stored as d fp32 values (the reference-precision storage mode): one
 // wave per (query, head), lane l holding dims [l*VPL, l*VPL + VPL).  The
@@ -1826,7 +2238,7 @@ int64_t attend_lo_lds_bytes(int64_t list_max) {
 
 int64_t attend_lds_max(const Lay &L, int64_t list_max) {
     const int64_t lo = L.d == 512 ? attend_lo_lds_bytes<512, 64>(list_max) : attend_lo_lds_bytes<64, 16>(list_max);
-    const int64_t hi = L.d == 512 ? attend_lds_bytes<512, 64, 1>(list_max) : attend_lds_bytes<64, 16, 1>(list_max);
+    const int64_t hi = L.d == 512 ? HqShape<512, 64>::lds_bytes(list_max) : attend_lds_bytes<64, 16, 1>(list_max);
     return lo > hi ? lo : hi;
 }
 
@@ -1869,6 +2281,19 @@ static hipError_t launch_lo(const AttnArgs &A, hipStream_t s) {
 }
 
 template <int D, int DR, bool CSA, bool PREFILL, bool F32A>
+static hipError_t launch_hq(const AttnArgs &A, hipStream_t s) {
+    static int64_t lim = 0;
+    const int64_t lds = HqShape<D, DR>::lds_bytes(attend_list_max(A.L, A.C, CSA));
+    hipError_t e = raise_lds_limit((const void *)k_attend_hq<D, DR, CSA, PREFILL, F32A>, lds, lim);
+    if (e != hipSuccess) return e;
+    const int groups = (A.nq + 7) / 8;
+    const int nhq = (A.nhg + HqShape<D, DR>::NHQ - 1) / HqShape<D, DR>::NHQ;
+    hipLaunchKernelGGL((k_attend_hq<D, DR, CSA, PREFILL, F32A>), dim3(groups * 8 * nhq), dim3(HqShape<D, DR>::NT),
+                       (size_t)lds, s, A);
+    return hipGetLastError();
+}
+
+template <int D, int DR, bool CSA, bool PREFILL, bool F32A>
 static hipError_t launch_lo8(const AttnArgs &A, hipStream_t s) {
     static int64_t lim = 0;
     constexpr int64_t lds = Lo8Shape<D, DR>::LDS;
@@ -1884,7 +2309,12 @@ static hipError_t launch_lo8(const AttnArgs &A, hipStream_t s) {
 // V4 shape), else the four-wave one.
 template <int D, int DR, bool CSA, bool PREFILL>
 static hipError_t launch_t(const AttnArgs &A, bool hi, hipStream_t s) {
-    if (hi) return launch_gr<D, DR, 1, CSA, PREFILL>(A, s);
+    if (hi) {
+        if constexpr (D == 512)
+            return A.L.act == DSV4_DT_BF16 ? launch_hq<D, DR, CSA, PREFILL, false>(A, s)
+                                           : launch_hq<D, DR, CSA, PREFILL, true>(A, s);
+        return launch_gr<D, DR, 1, CSA, PREFILL>(A, s);
+    }
     if constexpr (D == 512)
         if (attend_list_max(A.L, A.C, CSA) <= Lo8Shape<D, DR>::MAX_LIST)
             return A.L.act == DSV4_DT_BF16 ? launch_lo8<D, DR, CSA, PREFILL, false>(A, s)
