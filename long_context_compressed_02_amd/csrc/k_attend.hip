@@ -1952,18 +1952,26 @@ __global__ __launch_bounds__((HqShape<D, DR>::NT)) __attribute__((amdgpu_waves_p
         auto finish = [&](auto &S, int ck, int b) {
             constexpr int NO = sizeof(S.O) / sizeof(S.O[0]);
             float lg[2][4], sc[2][4];
-            const uint32_t vm = vmask[ck];
+            const uint32_t vmg = vmask[ck] >> (4 * g);   // bit 16rb+i: record 16rb+4g+i usable
+            f32x4 xa[kParts][2], xr[2], xc[2];            // one 16-byte read per array and record block
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int k = (rb * 64 + lane) * 4;      // [rb][lane][i]
+#pragma unroll
+                for (int q = 0; q < kParts; ++q) xa[q][rb] = *(const f32x4 *)(xch + q * XW + k);
+                xr[rb] = *(const f32x4 *)(xch + kParts * XW + k);
+                xc[rb] = *(const f32x4 *)(scl + b * kChunk + 16 * rb + 4 * g);   // scales of records 16rb+4g+i
+            }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rb + 4 * g + i, k = (rb * 4 + i) * 64 + lane;
-                    const bool ok = (vm >> r) & 1u;
-                    sc[rb][i] = scl[b * kChunk + r];
-                    float a = xch[k];
+                    const bool ok = (vmg >> (16 * rb + i)) & 1u;
+                    sc[rb][i] = xc[rb][i];
+                    float a = xa[0][rb][i];
 #pragma unroll
-                    for (int q = 1; q < kParts; ++q) a = a + xch[q * XW + k];
-                    lg[rb][i] = ok ? tau2 * (sc[rb][i] * a + xch[kParts * XW + k]) : -INFINITY;
+                    for (int q = 1; q < kParts; ++q) a = a + xa[q][rb][i];
+                    lg[rb][i] = ok ? tau2 * (sc[rb][i] * a + xr[rb][i]) : -INFINITY;
                 }
             float cmax = -INFINITY;
 #pragma unroll
@@ -2079,13 +2087,12 @@ __global__ __launch_bounds__((HqShape<D, DR>::NT)) __attribute__((amdgpu_waves_p
                 float an[2][4], ar[2][4];
                 partial(an, ar, b);
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int k = (rb * 4 + i) * 64 + lane;
-                        xch[DQ * XW + k] = an[rb][i];
-                        if (DQ == kParts - 1) xch[kParts * XW + k] = ar[rb][i];
-                    }
+                for (int rb = 0; rb < 2; ++rb) {
+                    const int k = (rb * 64 + lane) * 4;  // [rb][lane][i]: one 16-byte write a lane
+                    *(f32x4 *)(xch + DQ * XW + k) = (f32x4){an[rb][0], an[rb][1], an[rb][2], an[rb][3]};
+                    if (DQ == kParts - 1)
+                        *(f32x4 *)(xch + kParts * XW + k) = (f32x4){ar[rb][0], ar[rb][1], ar[rb][2], ar[rb][3]};
+                }
                 if (cn1 >= 0) stage(pre, b ^ 1);         // the next chunk into the other buffer
                 if (cn2 >= 0) issue(pre, cn2);           // and the one after on its way
                 __syncthreads();                         // partials and the next chunk visible
