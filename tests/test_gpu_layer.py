@@ -196,3 +196,55 @@ def test_prefill_chunk_on_prefix(kind, idx_store):
     assert diffs <= 2
     # the state after the chunk: window ring and pending ring hold the chunk's tail
     Hh.assert_records_close(Hh.window_rows(cache, 0, range(T - oc.window, T)), wrec[-oc.window:], oc.d_rope)
+
+
+@pytest.mark.parametrize("kind", [B.DSV4_CSA, B.DSV4_HCA], ids=["csa", "hca"])
+def test_prefill_from_position_0_production_shape(kind):
+    """Production shape, a 200-token chunk prefilled from position 0: the first
+    queries see fewer window tokens than one 32-record chunk (and no entries),
+    which the prefill attention layouts take on their general start.  Sampled
+    queries against the oracle (CSA over the GPU's own selection)."""
+    k = 512
+    act = B.DSV4_DT_BF16
+    cfg, oc = Hh.cfgs(synth.CSA_PREFILL_8K.shape(), act=act, topk=k)
+    csa = kind == B.DSV4_CSA
+    kname = "csa" if csa else "hca"
+    C = 200
+    bt, nb, mb = Hh.block_table([C], seed=6)
+    cache = B.LayerCache(cfg, kind, 1, mb, nb, bt)
+    g = np.random.default_rng(23)
+    raw = [g.standard_normal((C, n), dtype=np.float32) for n in (oc.d, oc.d, oc.idx_dim, oc.idx_dim)]
+    dev = [Hh.act_tensor(a, act) for a in raw]
+    ex = [d[1] for d in dev]
+    cu, r0, p0 = Hh.i32([0, C]), Hh.i32([0]), Hh.i32([0])
+    win = torch.empty((C + oc.window) * cache.layout.record_bytes, dtype=torch.uint8, device=Hh.DEV)
+    B.dsv4_compress_kv_prefill(cfg, cache, dev[0][0], dev[1][0], dev[2][0] if csa else None,
+                               dev[3][0] if csa else None, cu, r0, p0, C, win)
+    q, qI, wq = synth.decode_queries(synth.CSA_PREFILL_8K, C, sub=11)
+    qt, qx = Hh.act_tensor(q, act)
+    qIt, _ = Hh.act_tensor(qI, act)
+    sinks = synth.sinks(synth.CSA_PREFILL_8K)
+    st = torch.from_numpy(sinks).to(Hh.DEV)
+    out = torch.empty((C, oc.n_heads, oc.d), dtype=torch.bfloat16, device=Hh.DEV)
+    if csa:
+        ws = torch.empty(B.dsv4_workspace_bytes(cfg, C, mb * 32), dtype=torch.uint8, device=Hh.DEV)
+        tk = torch.empty((C, k), dtype=torch.int32, device=Hh.DEV)
+        B.dsv4_index_topk_prefill(cfg, cache, qIt, torch.from_numpy(wq).to(Hh.DEV), cu, r0, p0, C, tk, ws)
+        B.dsv4_csa_attend_prefill(cfg, cache, qt, cu, r0, p0, C, tk, win, st, out)
+    else:
+        B.dsv4_hca_attend_prefill(cfg, cache, qt, cu, r0, p0, C, win, st, out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    m = oc.m_csa if csa else oc.m_hca
+    js = list(range(C // m))
+    ents = O.entries_from_pool(kname, ex[0], ex[1], js, oc, token0=0)
+    wrec = O.window_records(ex[0], np.arange(0, C), oc)
+    window_of = lambda u: wrec[u]
+    gtk = tk.cpu().numpy() if csa else None
+    for i in [0, 1, 2, 5, 30, 31, 32, 33, 64, 127, 128, 150, C - 1]:
+        if csa:
+            o = Hh.attend_on_selection(i, qx[i], sinks, ents, gtk[i], window_of, oc)
+        else:
+            o = O.hca_query(i, qx[i], sinks, ents, window_of, oc)
+        err = Hh.rel_err_per_head(got[i], o)
+        assert err.max() <= 2e-2, (i, err.max())
