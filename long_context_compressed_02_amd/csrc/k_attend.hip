@@ -574,12 +574,17 @@ __global__ __launch_bounds__(64 * kParts * NSW) __attribute__((amdgpu_waves_per_
         // ---- output rows d = 16db + 4g + i of head `head`, with the sink:
         // out = O * f / (l * f + 2^(z - M)),  f = 2^(m - M),  M = max(m, z)
         const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
-        auto emit = [&](float m, float l, int db, const f32x4 &o) {
+        // (the normalisation is computed once: with the output stores in
+        // between, the compiler re-read the sink for every block, each read
+        // waiting for the stores before it)
+        auto out_scale = [&](float m, float l) {
             const float z = A.sinks[head] * 1.4426950408889634f;
             const float M = fmaxf(m, z);
             const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
             const float den = l * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
-            const float cf = den > 0.0f ? f / den : 0.0f;
+            return den > 0.0f ? f / den : 0.0f;
+        };
+        auto emit = [&](float cf, int db, const f32x4 &o) {
             const int dd = db * 16 + 4 * g;
             if (L.act == DSV4_DT_BF16) {
                 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -624,9 +629,10 @@ __global__ __launch_bounds__(64 * kParts * NSW) __attribute__((amdgpu_waves_per_
                 }
             }
             if (head_ok) {
+                const float cf = out_scale(acc.m, acc.l);
     #pragma unroll
                 for (int i = 0; i < DBQ; ++i)
-                    if (DBQ * DQ + i < NDB) emit(acc.m, acc.l, DBQ * DQ + i, acc.O[i]);
+                    if (DBQ * DQ + i < NDB) emit(cf, DBQ * DQ + i, acc.O[i]);
             }
         }
     };
@@ -2038,12 +2044,17 @@ __global__ __launch_bounds__((HqShape<D, DR>::NT)) __attribute__((amdgpu_waves_p
         // ---- output rows d = 16db + 4g + i of head `head`, with the sink:
         // out = O * f / (l * f + 2^(z - M)),  f = 2^(m - M),  M = max(m, z)
         const int64_t obase = ((int64_t)Q.qrow * L.H + head) * D;
-        auto emit = [&](float m, float l, int db, const f32x4 &o) {
+        // (the normalisation is computed once: with the output stores in
+        // between, the compiler re-read the sink for every block, each read
+        // waiting for the stores before it)
+        auto out_scale = [&](float m, float l) {
             const float z = A.sinks[head] * 1.4426950408889634f;
             const float M = fmaxf(m, z);
             const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
             const float den = l * f + ((z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - M));
-            const float cf = den > 0.0f ? f / den : 0.0f;
+            return den > 0.0f ? f / den : 0.0f;
+        };
+        auto emit = [&](float cf, int db, const f32x4 &o) {
             const int dd = db * 16 + 4 * g;
             if constexpr (!F32A) {
                 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -2113,9 +2124,10 @@ __global__ __launch_bounds__((HqShape<D, DR>::NT)) __attribute__((amdgpu_waves_p
             }
         }
         if (head_ok) {
+            const float cf = out_scale(acc.m, acc.l);
 #pragma unroll
             for (int i = 0; i < DBQ; ++i)
-                if (DBQ * DQ + i < NDB) emit(acc.m, acc.l, DBQ * DQ + i, acc.O[i]);
+                if (DBQ * DQ + i < NDB) emit(cf, DBQ * DQ + i, acc.O[i]);
         }
     };
     if (dq == 0) part_body(std::integral_constant<int, 0>());
