@@ -133,10 +133,11 @@ static_assert(kKeysPerWave % 64 == 0, "scoring ranges are whole pipeline groups"
 // the MFMA returns sum_b 2^(xq_b + xk_b) * (codes of block b . codes of block
 // b) (exact products, fp32 sums): the dot product of the stored values.  The
 // head weights then apply as they are (wq = w).
-// The query rows are quantised inside the kernel: wave w < HB quantises heads
-// [16w, 16w+16) of the workgroup's query (the same operations as
-// k_quant_index_q, so the same codes and weights) into LDS, while the first
-// keys are already on their way.
+// The query rows are quantised inside the kernel, with the decision rule of
+// k_quant_index_q (so the same codes and weights), into LDS while the first
+// keys are already on their way: E4M3 rows by four threads each (32 dims a
+// thread, the row maximum over the four), MXFP4 rows by wave w < HB for heads
+// [16w, 16w+16) in the separate quantiser's lane layout.
 template <int HB, bool FULL, bool F4>
 __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C, const void *qI,
                                                             const float *w, const int32_t *req,
