@@ -98,6 +98,22 @@ __device__ __forceinline__ float group_sum4(float v) {
     return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
+// Four partial sums at once: lane group g of the result holds the sum over
+// the four lane groups of v_g, added exactly as group_sum4 adds it, (v(g0) +
+// v(g1)) + (v(g2) + v(g3)).  The row-swap permutes exchange two registers at
+// a time, so the four take three permutes and three adds (group_sum4 takes
+// two and two each).
+__device__ __forceinline__ float group_sum4x4(float v0, float v1, float v2, float v3) {
+    // rows (2k, 2k+1): v0 -> [v0 r0, v1 r0, v0 r2, v1 r2], v1 -> [v0 r1, v1 r1, v0 r3, v1 r3]
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+    const float a = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);   // [v0 r0+r1, v1 r0+r1, v0 r2+r3, v1 r2+r3]
+    const float c = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+    // rows 2, 3 of a <-> rows 0, 1 of c: [a r0, a r1, c r0, c r1] and [a r2, a r3, c r2, c r3]
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(c), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // The weighted ReLU term of a head: w * max(0, x) + acc in one rounding (fma).
 // max(0, x) is taken on the bits (integer max with 0: a negative float is a
 // negative integer), one instruction where a float max would also canonicalise
@@ -579,11 +595,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             tsc[b][tid] = stg_s;
             if constexpr (F4) tsw[b][tid] = stg_w;
         };
-        uint32_t kmn[QW], kmx[QW];
-        // rows two at a time with no branch between them (their MFMAs, weightings
-        // and cross-lane sums overlap); rows inactive or past their visible keys
-        // store nothing
-        auto score_sb = [&](int b, int sb, int kb) {
+        // Two 16-key sub-blocks of the wave's two rows per step: the four
+        // partial sums are reduced together (group_sum4x4), after which lane
+        // group g holds sub-block g / 2 of row g % 2, and every lane scores its
+        // own key (the sum, scale and extremes of a key are the decode
+        // scorer's, operation for operation).  Rows inactive or past their
+        // visible keys store nothing.
+        static_assert(QW == 2, "two rows a wave: the four lane groups take two rows of two sub-blocks");
+        static_assert((kPfChunk / 16) % 2 == 0, "sub-blocks in pairs inside a tile");
+        uint32_t kmn = 0xffffffffu, kmx = 0u;            // extremes of the lane's row (g % 2)
+        auto partials = [&](int b, int sb, float (&part)[2]) {
             i32x8 Bk;
             const uint8_t *kr = tile[b] + (sb * 16 + c16) * kPfRowBytes;
             Bk.lo = *(const i32x4 *)(kr + 16 * g);
@@ -594,47 +615,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             } else {
                 Bk.hi = *(const i32x4 *)(kr + 64 + 16 * g);
             }
-            const float sk = tsc[b][sb * 16 + c16];
+            f32x4 acc[2][HB];
 #pragma unroll
-            for (int i0 = 0; i0 < QW; i0 += 2) {
-                f32x4 acc[2][HB];
+            for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        if constexpr (F4)
-                            acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                A[i0 + ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, (int)sa[i0 + ii][hb], 0,
-                                (int)sbk);
-                        else
-                            acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                A[i0 + ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
-                    }
-                float part[2];
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    part[ii] = 0.0f;
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) {
-                        const f32x4 w4 = wls[wr0 + i0 + ii][hb * 4 + g];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) part[ii] = relu_fma(acc[ii][hb][j], w4[j], part[ii]);
-                    }
+                for (int hb = 0; hb < HB; ++hb) {
+                    if constexpr (F4)
+                        acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            A[ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, (int)sa[ii][hb], 0, (int)sbk);
+                    else
+                        acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            A[ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
                 }
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) part[ii] = group_sum4(part[ii]);
+            for (int ii = 0; ii < 2; ++ii) {
+                part[ii] = 0.0f;
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = i0 + ii, rw = wr0 + i;
-                    if (g == 0 && ((act >> rw) & 1) && kb + c16 < Nq[rw]) {
-                        const float v = sk * part[ii];
-                        scores[(int64_t)(row0 + rw) * ld + kb + c16] = v;
-                        if (fabsf(v) < INFINITY) {
-                            const uint32_t u = score_key(v);
-                            kmn[i] = min(kmn[i], u);
-                            kmx[i] = max(kmx[i], u);
-                        }
-                    }
+                for (int hb = 0; hb < HB; ++hb) {
+                    const f32x4 w4 = wls[wr0 + ii][hb * 4 + g];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) part[ii] = relu_fma(acc[ii][hb][j], w4[j], part[ii]);
+                }
+            }
+        };
+        const int ls = g >> 1, lr = g & 1, lrw = wr0 + lr;   // the lane's sub-block (of the pair) and row
+        const bool lact = ((act >> lrw) & 1) != 0;
+        const int lN = Nq[lrw];
+        float *lsrow = scores + (int64_t)(row0 + lrw) * ld;
+        auto score_pair = [&](int b, int sb, int kb) {   // sub-blocks sb, sb + 1; kb: the first key of sb
+            float p0[2], p1[2];
+            partials(b, sb, p0);
+            __builtin_amdgcn_sched_barrier(0);           // one sub-block's MFMA results live at a time
+            partials(b, sb + 1, p1);
+            const float part = group_sum4x4(p0[0], p0[1], p1[0], p1[1]);
+            const int key = kb + 16 * ls + c16;
+            const float sk = tsc[b][(sb + ls) * 16 + c16];
+            if (lact && key < lN) {
+                const float v = sk * part;
+                lsrow[key] = v;
+                if (fabsf(v) < INFINITY) {
+                    const uint32_t u = score_key(v);
+                    kmn = min(kmn, u);
+                    kmx = max(kmx, u);
                 }
             }
         };
@@ -645,30 +667,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         for (int c = 0; c < nch; ++c) {
             const int kc0 = kbeg + c * kPfChunk, b = c & 1;
             if (c + 1 < nch) load_tile(kc0 + kPfChunk);  // in flight while this tile is scored
-#pragma unroll
-            for (int i = 0; i < QW; ++i) {
-                kmn[i] = 0xffffffffu;
-                kmx[i] = 0u;
-            }
+            kmn = 0xffffffffu;
+            kmx = 0u;
 #pragma unroll 1
-            for (int sb = 0; sb < kPfChunk / 16; ++sb) {
+            for (int sb = 0; sb < kPfChunk / 16; sb += 2) {
                 const int kb = kc0 + sb * 16;
                 if (kb >= kend) break;                   // workgroup-uniform
-                score_sb(b, sb, kb);
+                score_pair(b, sb, kb);
             }
             // this tile's extremes per row (the record the decode scorer's wave
-            // for these keys writes)
-#pragma unroll
-            for (int i = 0; i < QW; ++i) {
-                const int rw = wr0 + i;
-                if (!((act >> rw) & 1) || kc0 >= Nq[rw]) continue;   // wave-uniform
-                uint32_t mn = kmn[i], mx = kmx[i];
+            // for these keys writes): over the lanes of the row's two lane
+            // groups (lane bit 4 is the row), found in lanes 0 and 16
+            {
+                uint32_t mn = kmn, mx = kmx;
 #pragma unroll
                 for (int o = 32; o >= 1; o >>= 1) {
+                    if (o == 16) continue;
                     mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
                     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
                 }
-                if (lane == 0) wr[(int64_t)(row0 + rw) * nwr + kc0 / kKeysPerWave] = make_uint2(mn, mx);
+                if ((lane & ~16) == 0 && lact && kc0 < lN)
+                    wr[(int64_t)(row0 + lrw) * nwr + kc0 / kKeysPerWave] = make_uint2(mn, mx);
             }
             if (c + 1 < nch) store_tile(b ^ 1);
             __syncthreads();                             // next tile visible; this one free
@@ -1381,7 +1400,7 @@ __global__ __launch_bounds__(kTkThreads) void k_tk_final(TkArgs A) {
 // sure-ranks [n][kTkCandMax] each.
 static inline int64_t al256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base) {
+int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base, int64_t *scores_off, int64_t *scores_ld) {
     const int64_t ld = (nmax + kTkSeg - 1) / kTkSeg * kTkSeg;
     const int s_max = (int)(ld / kTkSeg);
     const int nwr = (int)(ld / kKeysPerWave);
@@ -1397,6 +1416,8 @@ int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *b
     const int64_t o_ck = off; off = al256(off + (int64_t)n * kTkCandMax * 4);
     const int64_t o_cp = off; off = al256(off + (int64_t)n * kTkCandMax * 4);
     const int64_t o_cr = off; off = al256(off + (int64_t)n * kTkCandMax * 4);
+    if (scores_off) *scores_off = o_sc;
+    if (scores_ld) *scores_ld = ld;
     if (w) {
         w->q8 = base + o_q8;
         w->wq = (float *)(base + o_wq);
