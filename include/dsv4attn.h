@@ -198,6 +198,20 @@ dsv4_status dsv4_get_layout(const dsv4_cfg *cfg, int32_t kind, dsv4_layout *out)
 dsv4_status dsv4_workspace_bytes(const dsv4_cfg *cfg, int32_t n_queries, int32_t max_entries,
                                  int64_t *out);
 
+/* Where dsv4_index_topk_decode (prefill = 0) or dsv4_index_topk_prefill
+ * (prefill = 1) leaves the indexer scores I[j] in its workspace, for reading
+ * them back (tests, analysis): score j of query i -- i < n_queries, j below
+ * the query's visible entry count -- is the fp32 at byte
+ * *offset + 4 * (i * *ld + j) of ws_dev, valid until the workspace is used
+ * again.  n_queries is the call's B (decode) or total_tokens (prefill); for
+ * the prefill call this holds when its workspace fits all its queries at once
+ * (ws_bytes >= dsv4_workspace_bytes(cfg, total_tokens, max_blocks*128/m)).
+ * Caller-owned outputs; nothing is launched.  DSV4_ERR_INVALID_ARG for null
+ * outputs, n_queries outside [1, 65535], prefill not 0 or 1, or an invalid
+ * cfg or cache. */
+dsv4_status dsv4_index_scores_layout(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t n_queries,
+                                     int32_t prefill, int64_t *offset, int64_t *ld);
+
 /*
  * Append + compress, decode: one new token per request.
  * Token b (position pos_dev[b], request req_dev[b]) is RoPE-rotated at its

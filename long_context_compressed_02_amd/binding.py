@@ -36,7 +36,7 @@ EXPORTS = [
     "dsv4_out_proj_pack", "dsv4_cache_dump_bytes", "dsv4_cache_dump", "dsv4_cache_load",
     "dsv4_mx_pack_bytes", "dsv4_mx_pack_weight", "dsv4_mx_linear", "dsv4_index_q_proj_ws_bytes",
     "dsv4_index_q_proj", "dsv4_cache_read_entries", "dsv4_index_topk_decode_noalloc", "dsv4_kv_proj_ws_bytes",
-    "dsv4_kv_proj",
+    "dsv4_kv_proj", "dsv4_index_scores_layout",
 ]
 DSV4_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -83,6 +83,7 @@ def lib():
         sig = {
             "dsv4_get_layout": [cp, i32, ctypes.POINTER(Layout)],
             "dsv4_workspace_bytes": [cp, i32, i32, ctypes.POINTER(i64)],
+            "dsv4_index_scores_layout": [cp, kp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)],
             "dsv4_compress_kv_decode": [cp, kp, vp, vp, vp, vp, vp, vp, i32, vp],
             "dsv4_compress_kv_prefill": [cp, kp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp],
             "dsv4_index_topk_decode": [cp, kp, vp, vp, vp, vp, i32, vp, vp, i64, vp],
@@ -183,6 +184,14 @@ class LayerCache:
 
 
 # --------------------------------------------------------------------- entry points
+def dsv4_index_scores_layout(cfg, cache: LayerCache, n_queries: int, prefill: bool):
+    """(byte offset, row stride in floats) of the score rows an index call leaves in its workspace."""
+    off, ld = ctypes.c_int64(), ctypes.c_int64()
+    _ck("dsv4_index_scores_layout", lib().dsv4_index_scores_layout(
+        ctypes.byref(cfg), ctypes.byref(cache.c), n_queries, 1 if prefill else 0, ctypes.byref(off), ctypes.byref(ld)))
+    return off.value, ld.value
+
+
 def dsv4_compress_kv_decode(cfg, cache: LayerCache, kv, gate, kI, gI, req, pos, stream=None):
     _ck("dsv4_compress_kv_decode", lib().dsv4_compress_kv_decode(
         ctypes.byref(cfg), ctypes.byref(cache.c), _p(kv), _p(gate), _p(kI), _p(gI), _p(req), _p(pos),

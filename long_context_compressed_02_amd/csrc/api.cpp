@@ -197,6 +197,22 @@ dsv4_status dsv4_workspace_bytes(const dsv4_cfg *cfg, int32_t n_queries, int32_t
     return DSV4_OK;
 }
 
+dsv4_status dsv4_index_scores_layout(const dsv4_cfg *cfg, const dsv4_cache *cache, int32_t n_queries,
+                                     int32_t prefill, int64_t *offset, int64_t *ld) {
+    if (!offset || !ld || n_queries < 1 || n_queries > kMaxGridRows || (prefill != 0 && prefill != 1))
+        return DSV4_ERR_INVALID_ARG;
+    Lay L;
+    dsv4_status st = make_layout(cfg, DSV4_CSA, &L);
+    if (st != DSV4_OK) return st;
+    if ((st = check_cache(L, cache, DSV4_CSA)) != DSV4_OK) return st;
+    int64_t off = 0, stride = 0;
+    index_ws_bytes(L, n_queries, (int64_t)cache->max_blocks * L.epb, nullptr, nullptr, &off, &stride);
+    // a prefill call's workspace starts with its per-query (request, position) rows
+    *offset = (prefill ? al((int64_t)n_queries * 8, 256) : 0) + off;
+    *ld = stride;
+    return DSV4_OK;
+}
+
 dsv4_status dsv4_compress_kv_decode(const dsv4_cfg *cfg, const dsv4_cache *cache, const void *kv,
                                     const void *gate, const void *kI, const void *gI, const int32_t *req_dev,
                                     const int32_t *pos_dev, int32_t B, void *stream) {

@@ -53,7 +53,11 @@ struct IndexWs {
     int64_t ld;
     int nwr, s_max;
 };
-int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base);
+// Bytes of the indexer's workspace for n queries of at most nmax visible
+// entries; with w, its regions carved from base.  scores_off / scores_ld
+// (optional): byte offset of the score rows and their stride in floats.
+int64_t index_ws_bytes(const Lay &L, int n, int64_t nmax, IndexWs *w, uint8_t *base, int64_t *scores_off = nullptr,
+                       int64_t *scores_ld = nullptr);
 hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows, const IndexWs &ws,
                           hipStream_t s);
 hipError_t launch_score_decode(const Lay &L, const dsv4_cache &C, const void *qI, const float *w,
