@@ -80,3 +80,21 @@ def test_topk_rows_more_rows_than_one_launch():
     print("topk_rows 70000 rows", flush=True)
     got = _run(rows, 4, max_n=16)
     _check(got, rows, 4)
+
+
+@pytest.mark.parametrize("max_n", [65536, 80000])
+def test_topk_rows_alone_and_among_empty_rows(max_n):
+    # The same rows selected alone and as the first rows of a batch of 1106
+    # (the rest empty): rows of at most 16 segments (65536 scores) take the
+    # split pass that finds the boundary bin itself, longer ones the separate
+    # boundary-bin pass.  Both batches return the oracle's lists, the empty
+    # rows only padding.
+    rows = [synth.score_row(kind, n, 40 + i) for i, (kind, n) in enumerate(
+        [("normal", max_n), ("ties", max_n - 1), ("special", max_n // 2 + 3), ("crowded", 9000),
+         ("huge", max_n - 4095), ("normal", 700)])]
+    print(f"topk_rows alone / among empty rows max_n={max_n}", flush=True)
+    alone = _run(rows, 1024, max_n=max_n)
+    _check(alone, rows, 1024)
+    wide = _run(rows + [np.zeros(0, np.float32)] * 1100, 1024, max_n=max_n)
+    _check(wide[:len(rows)], rows, 1024)
+    assert (wide[len(rows):] == -1).all()
