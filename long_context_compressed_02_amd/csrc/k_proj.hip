@@ -142,9 +142,150 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmArgs G) {
             }
 }
 
+// Large batches with LDS-staged tiles: a workgroup of 8 waves owns a 256x256
+// tile of C, wave (wm, wn) of it 128x64 (8 x 4 blocks of 16x16).  k advances
+// in tiles of 64 (two MFMA k-steps): all 512 threads copy the tile's A and B
+// operands (32 KB each) from memory into LDS, laid out in MFMA operand order
+// -- per (k-step, 16-row block) one kilobyte, lane l's 16 bytes at 16 l -- so
+// the copy's stores and the waves' operand reads are both 64 consecutive
+// 16-byte slots (no bank conflicts).  Two LDS stages and two register sets:
+// tiles t+1 and t+2 are in flight while tile t is multiplied, then tile t+1 is
+// stored into the other stage; one barrier per tile.  Each wave's operand bytes are read from LDS
+// instead of from the L1 / L2 caches, and each byte fetched from memory feeds
+// 256 rows or columns.  Every output element is still one wave's chain of
+// 16x16x32 MFMAs over the k-steps in increasing order, so the results are
+// bitwise those of the other tilings.
+//
+// Workgroups are dealt to the 8 XCDs in turn: workgroup id w computes tile
+// (w mod 8) * per + w / 8, so each XCD runs a contiguous range of tiles, taken
+// in groups of four row tiles column by column (the XCD's concurrent
+// workgroups then share their A and B tiles in its L2).
+constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64;
+constexpr int kLdsGroupM = 4;
+constexpr int kLdsStage = (kLdsBM + kLdsBN) * kLdsBK * 2;     // bytes of one LDS stage
+constexpr int kLdsBytes = 2 * kLdsStage;
+
+__global__ __launch_bounds__(512) void k_gemm_nt_lds(GemmArgs G, int nx, int ny, int per) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;                 // 2 x 4 waves
+    const int z = blockIdx.y;
+    const int w = blockIdx.x;
+    const int T = (w & 7) * per + (w >> 3);                  // this workgroup's tile
+    if (T >= nx * ny) return;
+    const int gsz = kLdsGroupM * nx;                         // tiles of a group of row tiles
+    const int fr = (T / gsz) * kLdsGroupM;
+    const int rows = ny - fr < kLdsGroupM ? ny - fr : kLdsGroupM;
+    const int ty = fr + (T % gsz) % rows, tx = (T % gsz) / rows;
+    const int m0 = ty * kLdsBM, n0 = tx * kLdsBN;
+    const uint16_t *A = G.A + (int64_t)z * G.sA;
+    const uint16_t *B = G.B + (int64_t)z * G.sB;
+    const int nk = G.K / 32;                                 // k-steps
+    const int nkt = G.K / kLdsBK;                            // k-tiles
+
+    // the copy: thread t moves pieces p = t + 512 u (u < 4) of A and of B, in
+    // operand order p = (k-step s, block i, lane l): A row m0 + 16 i + l % 16
+    // at k = 32 s + 8 (l / 16) (rows past M read row M-1, never stored); B the
+    // packed kilobyte of column block n0 / 16 + i, k-step s
+    const uint16_t *ga[4];
+    const uint16_t *gb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int p = tid + 512 * u, s = p >> 10, i = (p >> 6) & 15, l = p & 63;
+        int row = m0 + 16 * i + (l & 15);
+        row = row < G.M ? row : G.M - 1;
+        ga[u] = A + (int64_t)row * G.lda + 32 * s + 8 * (l >> 4);
+        gb[u] = B + ((int64_t)(n0 / 16 + i) * nk + s) * 512 + 8 * l;
+    }
+    // two tiles' loads in flight: tile j's in register set j mod 2 (a tile
+    // past the end re-reads the last one: every load unconditional, never used)
+    u32x4 ra[2][4], rb[2][4];
+    auto fetch = [&](int set, int kt) {
+        const int kc = kt < nkt ? kt : nkt - 1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            ra[set][u] = *(const u32x4 *)(ga[u] + (int64_t)kLdsBK * kc);
+            rb[set][u] = *(const u32x4 *)(gb[u] + (int64_t)1024 * kc);   // two packed k-steps a tile
+        }
+    };
+    auto stash = [&](int set, int st) {
+        uint8_t *sa = smem + st * kLdsStage, *sb = sa + kLdsBM * kLdsBK * 2;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            *(u32x4 *)(sa + 16 * (tid + 512 * u)) = ra[set][u];
+            *(u32x4 *)(sb + 16 * (tid + 512 * u)) = rb[set][u];
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](int st) {
+        const uint8_t *sa = smem + st * kLdsStage, *sb = sa + kLdsBM * kLdsBK * 2;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            u32x4 fa[8], fb[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fa[i] = *(const u32x4 *)(sa + (((s * 16 + 8 * wm + i) * 64) + lane) * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[j] = *(const u32x4 *)(sb + (((s * 16 + 4 * wn + j) * 64) + lane) * 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j],
+                                                                        0, 0, 0);
+        }
+    };
+    // tile kt is multiplied from stage kt mod 2 while tiles kt+1 (set (kt+1)
+    // mod 2) and kt+2 are on their way; then tile kt+1 goes into the other
+    // stage and its registers take tile kt+3
+    fetch(0, 0);
+    stash(0, 0);
+    fetch(1, 1);
+    fetch(0, 2);
+    __syncthreads();
+#pragma unroll 1
+    for (int kt = 0; kt < nkt; kt += 2) {
+        compute(0);
+        if (kt + 1 < nkt) {                                  // (uniform)
+            stash(1, 1);
+            fetch(1, kt + 3);
+        }
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            compute(1);
+            if (kt + 2 < nkt) {
+                stash(0, 0);
+                fetch(0, kt + 4);
+            }
+            __syncthreads();
+        }
+    }
+    // lane (g, c16) holds rows 4g+e, column c16 of each 16x16 block
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 128 * wm + 16 * i + 4 * g + e, col = n0 + 64 * wn + 16 * j + c16;
+                if (row >= G.M) continue;
+                const int64_t off = (int64_t)z * G.sC + (int64_t)row * G.ldc + col;
+                if (G.c_f32) ((float *)G.C)[off] = acc[i][j][e];
+                else ((uint16_t *)G.C)[off] = bf16_bits(acc[i][j][e]);
+            }
+}
+
 // Tilings.  Small batches: a wave owns one 16x16 block and keeps 8 k-steps of
 // loads in flight (the weights are streamed once; parallelism comes from the
-// columns).  Large batches: a wave owns 64x64, a workgroup 128x128.
+// columns).  Large batches: 256x256 workgroup tiles staged through LDS where N
+// and K allow (N a multiple of 256, K of 64), else a wave owns 64x64 straight
+// from memory, a workgroup 128x128.
 constexpr int kProjSmallRows = 256;
 constexpr int kSmallTileM = 32, kSmallTileN = 32;
 constexpr int kLargeTileM = 128, kLargeTileN = 128;
@@ -155,6 +296,15 @@ static hipError_t launch_gemm(const GemmArgs &G, int batch, hipStream_t s) {
     if (G.M <= kProjSmallRows) {
         dim3 grid((unsigned)(G.N / kSmallTileN), (unsigned)((G.M + kSmallTileM - 1) / kSmallTileM), (unsigned)batch);
         hipLaunchKernelGGL((k_gemm_nt<1, 1, 2, 2, 8>), grid, dim3(256), 0, s, G);
+    } else if (G.N % kLdsBN == 0 && G.K % kLdsBK == 0) {
+        // (one fixed size, set once: the initialisation of a local static is thread-safe)
+        static const hipError_t lds_e =
+            hipFuncSetAttribute((const void *)k_gemm_nt_lds, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        if (lds_e != hipSuccess) return lds_e;
+        const int nx = G.N / kLdsBN, ny = (G.M + kLdsBM - 1) / kLdsBM;
+        const int per = (nx * ny + 7) / 8;
+        hipLaunchKernelGGL(k_gemm_nt_lds, dim3((unsigned)(8 * per), (unsigned)batch), dim3(512), (size_t)kLdsBytes, s,
+                           G, nx, ny, per);
     } else {
         dim3 grid((unsigned)(G.N / kLargeTileN), (unsigned)((G.M + kLargeTileM - 1) / kLargeTileM), (unsigned)batch);
         hipLaunchKernelGGL((k_gemm_nt<4, 4, 2, 2, 2>), grid, dim3(256), 0, s, G);
