@@ -272,10 +272,167 @@ __global__ __launch_bounds__(256) void k_mx_gemm(MxArgs G) {
         }
 }
 
+// Large inputs with LDS-staged tiles: a workgroup of 8 waves owns a tile of
+// 16 row blocks x CB column blocks (256x256 or, where that leaves compute
+// units idle, 256x128), wave (wm, wn) 64 x 8 CB of it (4 x CB/2 blocks).  Per
+// k-step all 512 threads copy the tile's operands into one of two LDS stages
+// in the packed order (A codes 32 KB, B codes CB KB, the 64 scale words of
+// each block), so the copy's stores and the waves' reads are 64 consecutive
+// slots; the next k-step's loads are in flight in registers while the current
+// one is multiplied.  Each output is still one wave's chain over
+// the k-steps in increasing order with the same instruction: bitwise the other
+// tilings' result.  Tiles go to the XCDs in contiguous runs, four row tiles
+// at a time column by column.
+constexpr int kMxLdsRows = 256;                                   // rows of a tile
+constexpr int kMxLdsA = 16 * 2048;
+template <int CB>
+struct MxLds {
+    static constexpr int B = CB * 1024, S = (16 + CB) * 256;       // B codes, A and B scale words
+    static constexpr int STAGE = kMxLdsA + B + S;
+    static constexpr int BYTES = 2 * STAGE;
+    static constexpr int NB = CB * 64 / 512;                       // B pieces a thread copies
+    static_assert(CB == 8 || CB == 16, "two tile widths");
+};
+
+template <int CB>
+__global__ __launch_bounds__(512) void k_mx_gemm_lds(MxArgs G, int per) {
+    using Ly = MxLds<CB>;
+    constexpr int WJ = CB / 2;                                     // column blocks a wave owns
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;                       // 4 x 2 waves
+    const int nx = G.tiles_x, ny = G.tiles_y;
+    const int T = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (T >= nx * ny) return;
+    const int gsz = 4 * nx, fr = (T / gsz) * 4;
+    const int rows = ny - fr < 4 ? ny - fr : 4;
+    const int ty = fr + (T % gsz) % rows, tx = (T % gsz) / rows;
+    const int nks = G.K / 128, nq = (nks + 3) / 4;
+    const int rbs = (G.M + 15) / 16;
+    const int rb0 = ty * 16, cb0 = tx * CB;
+    // the copy: A pieces p = t + 512 u (u < 4) -- block p / 128, 16 bytes at
+    // 16 (p mod 128) of its 2 KB; B pieces p = t + 512 u (u < 2) -- block p / 64;
+    // scale piece t: 16 bytes of the A (t < 256) or B block's 256-byte word row
+    const uint8_t *ga[4];
+    const uint8_t *gb[Ly::NB];
+    const uint8_t *gs;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int pc = tid + 512 * u;
+        const int64_t rb = rb0 + (pc >> 7) < rbs ? rb0 + (pc >> 7) : rbs - 1;   // (past the rows: the last block)
+        ga[u] = G.A + rb * nks * 2048 + 16 * (pc & 127);
+    }
+#pragma unroll
+    for (int u = 0; u < Ly::NB; ++u) {
+        const int pc = tid + 512 * u;
+        gb[u] = G.B + (int64_t)(cb0 + (pc >> 6)) * nks * 1024 + 16 * (pc & 63);
+    }
+    // scale piece t < 16 (16 + CB): 16 bytes of an A (block t / 16 < 16) or a
+    // B block's word row; the other threads copy none
+    const bool scopy = tid < 16 * (16 + CB);
+    {
+        const int blk = tid >> 4, off = 16 * (tid & 15);
+        if (blk < 16) {
+            const int64_t rb = rb0 + blk < rbs ? rb0 + blk : rbs - 1;
+            gs = G.A + G.a_scale_off + rb * nq * 256 + off;
+        } else {
+            const int cb = scopy ? cb0 + blk - 16 : cb0;
+            gs = G.B + G.b_scale_off + (int64_t)cb * nq * 256 + off;
+        }
+    }
+    u32x4 ra[4], rbv[Ly::NB], rs;
+    auto fetch = [&](int ks) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ra[u] = *(const u32x4 *)(ga[u] + (int64_t)2048 * ks);
+#pragma unroll
+        for (int u = 0; u < Ly::NB; ++u) rbv[u] = *(const u32x4 *)(gb[u] + (int64_t)1024 * ks);
+        rs = *(const u32x4 *)(gs + (int64_t)256 * (ks >> 2));       // (every thread: in bounds)
+    };
+    auto stash = [&](int st) {
+        uint8_t *sp = smem + st * Ly::STAGE;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *(u32x4 *)(sp + 16 * (tid + 512 * u)) = ra[u];
+#pragma unroll
+        for (int u = 0; u < Ly::NB; ++u) *(u32x4 *)(sp + kMxLdsA + 16 * (tid + 512 * u)) = rbv[u];
+        if (scopy) *(u32x4 *)(sp + kMxLdsA + Ly::B + 16 * tid) = rs;   // A words, then B words
+    };
+    f32x4 acc[4][WJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) acc[i][j] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    const i32x4 z4 = {0, 0, 0, 0};
+    fetch(0);
+    stash(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int ks = 0; ks < nks; ++ks) {
+        if (ks + 1 < nks) fetch(ks + 1);                           // (uniform)
+        const uint8_t *sp = smem + (ks & 1) * Ly::STAGE;
+        const uint32_t *sws = (const uint32_t *)(sp + kMxLdsA + Ly::B);
+        const int sh = 8 * (ks & 3);
+        i32x4 fb[WJ];
+        uint32_t sb[WJ];
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            fb[j] = *(const i32x4 *)(sp + kMxLdsA + ((WJ * wn + j) * 64 + lane) * 16);
+            sb[j] = sws[(16 + WJ * wn + j) * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            i32x8 a;
+            a.lo = *(const i32x4 *)(sp + ((4 * wm + i) * 128 + lane) * 16);
+            a.hi = *(const i32x4 *)(sp + ((4 * wm + i) * 128 + 64 + lane) * 16);
+            const uint32_t sa = sws[(4 * wm + i) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < WJ; ++j) {
+                i32x8 b;
+                b.lo = fb[j];
+                b.hi = z4;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i][j], 0, 4, 0, (int)(sa >> sh), 0,
+                                                                            (int)(sb[j] >> sh));
+            }
+        }
+        if (ks + 1 < nks) stash((ks + 1) & 1);                     // the stage read one step ago
+        __syncthreads();
+    }
+    // lane (g, c16) holds rows 4g+e, column c16 of each 16x16 block
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < WJ; ++j) {
+            const int col = 16 * (cb0 + WJ * wn + j) + c16;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * (rb0 + 4 * wm + i) + 4 * g + e;
+                if (row >= G.M) continue;
+                const int64_t off = (int64_t)row * G.ldc + col;
+                if (G.c_f32) ((float *)G.C)[off] = acc[i][j][e];
+                else ((uint16_t *)G.C)[off] = bf16_bits(acc[i][j][e]);
+            }
+        }
+}
+
 // Tilings.  Up to 64 rows: a wave owns all (2 or 4) row blocks of one
 // column block and keeps 8 k-steps of loads in flight -- the weights stream
-// once.  Larger: a wave owns 64x64, a workgroup 128x128.
+// once.  Larger: 256x256 (or 256x128) tiles staged through LDS where N is a
+// multiple of 256 (128), else a wave owns 64x64, a workgroup 128x128,
+// straight from memory.
 constexpr int kMxSmallRows = 64;
+
+template <int CB>
+static hipError_t launch_lds(MxArgs G, hipStream_t s) {
+    // (one fixed size, set once: the initialisation of a local static is thread-safe)
+    static const hipError_t lds_e = hipFuncSetAttribute((const void *)k_mx_gemm_lds<CB>,
+                                                        hipFuncAttributeMaxDynamicSharedMemorySize, MxLds<CB>::BYTES);
+    if (lds_e != hipSuccess) return lds_e;
+    G.tiles_x = G.N / (16 * CB);
+    G.tiles_y = (G.M + kMxLdsRows - 1) / kMxLdsRows;
+    const int per = (G.tiles_x * G.tiles_y + 7) / 8;
+    hipLaunchKernelGGL(k_mx_gemm_lds<CB>, dim3((unsigned)(8 * per)), dim3(512), (size_t)MxLds<CB>::BYTES, s, G, per);
+    return hipGetLastError();
+}
 
 hipError_t launch_mx_quant(const uint16_t *X, int rows, int K, bool fp8, uint8_t *P, hipStream_t s) {
     const int nq = (K / 128 + 3) / 4;
@@ -308,7 +465,16 @@ hipError_t launch_mx_gemm(const uint8_t *A, const uint8_t *Bp, int M, int N, int
     MxArgs G{A, Bp, C, mx_code_bytes(M, K, true), mx_code_bytes(N, K, false), ldc, M, N, K, c_f32, 0, 0, 0};
     if (M <= 32) launch_tiled<2, 1, 1, 4, 8>(G, s);
     else if (M <= kMxSmallRows) launch_tiled<4, 1, 1, 4, 8>(G, s);
-    else launch_tiled<4, 4, 2, 2, 2>(G, s);
+    else if (N % 128 == 0) {
+        // 256-wide tiles unless they would leave compute units idle
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        const int64_t wide = (int64_t)(N / 256) * ((M + kMxLdsRows - 1) / kMxLdsRows);
+        if (N % 256 == 0 && wide >= cus) return launch_lds<16>(G, s);
+        return launch_lds<8>(G, s);
+    } else launch_tiled<4, 4, 2, 2, 2>(G, s);
     return hipGetLastError();
 }
 

@@ -89,10 +89,13 @@ def test_mx_weight_pack_layout():
     assert np.array_equal(dec, O.mxfp4_rows(_f64(wt)))
 
 
+@pytest.mark.parametrize("N", [48, 256])
 @pytest.mark.parametrize("K", [128, 384, 1024])
-def test_mx_linear_small_ragged(K):
-    g = np.random.default_rng([5, K])
-    N = 48                                            # 3 column blocks: a ragged column tile
+def test_mx_linear_small_ragged(K, N):
+    # N = 48: 3 column blocks, a ragged column tile of the 128x128 tiling;
+    # N = 256: above 64 rows the 256x256 LDS-staged tiling (one, three or
+    # eight k-steps; 257 and 300 rows: a ragged second row tile)
+    g = np.random.default_rng([5, K, N])
     w = _bf16(g.standard_normal((N, K)) / np.sqrt(K))
     wp = _pack(w)
     for M in (1, 20, 37, 64, 256, 257, 300):          # every tiling and quantiser split, ragged rows
