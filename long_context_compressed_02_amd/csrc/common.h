@@ -139,9 +139,16 @@ __device__ __forceinline__ void rope_cs(const Lay &L, int64_t pos, int i, float 
 // theta_i for a lane-dependent i < n, read from the argument block with
 // uniform (scalar) loads: a per-lane indexed read is a vector load, and the
 // wait for it also waits for every vector load issued before it.
+// (Each value passes readfirstlane: without it the compiler folds the select
+// chain back into one per-lane load.)
 __device__ __forceinline__ double theta_pick(const Lay &L, int i, int n) {
     double th = 0.0;
-    for (int k = 0; k < n && k < 64; ++k) th = i == k ? L.theta[k] : th;
+    for (int k = 0; k < n && k < 64; ++k) {
+        const uint64_t b = (uint64_t)__double_as_longlong(L.theta[k]);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+        th = i == k ? __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)) : th;
+    }
     return th;
 }
 
