@@ -604,6 +604,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         static_assert(QW == 2, "two rows a wave: the four lane groups take two rows of two sub-blocks");
         static_assert((kPfChunk / 16) % 2 == 0, "sub-blocks in pairs inside a tile");
         uint32_t kmn = 0xffffffffu, kmx = 0u;            // extremes of the lane's row (g % 2)
+        // (MXFP4) the lane's head weights held in registers for the pass: the
+        // same 32 values serve every sub-block, and read from LDS per
+        // sub-block they were four times the key operand's LDS bytes.  (The
+        // E4M3 kernel has no registers to spare for them.)
+        constexpr bool WREG = F4;
+        f32x4 wreg[WREG ? 2 : 1][WREG ? HB : 1];
+        if constexpr (WREG) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) wreg[ii][hb] = wls[wr0 + ii][hb * 4 + g];
+        }
         auto partials = [&](int b, int sb, float (&part)[2]) {
             i32x8 Bk;
             const uint8_t *kr = tile[b] + (sb * 16 + c16) * kPfRowBytes;
@@ -632,7 +644,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 part[ii] = 0.0f;
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
-                    const f32x4 w4 = wls[wr0 + ii][hb * 4 + g];
+                    f32x4 w4;
+                    if constexpr (WREG) w4 = wreg[ii][hb];
+                    else w4 = wls[wr0 + ii][hb * 4 + g];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) part[ii] = relu_fma(acc[ii][hb][j], w4[j], part[ii]);
                 }
