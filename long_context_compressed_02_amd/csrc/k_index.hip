@@ -560,13 +560,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         // one tile's loads: thread piece tid + 256u is piece (u mod PK) of key (tid + 256u) / PK;
         // thread tid also fetches key tid's scale.  Keys past the end, or in
         // unmapped blocks, read block 0 and get scale 0.
-        i32x4 stg[PKMAX];
+        // DMA (full-width E4M3 keys): the codes go straight into LDS
+        // (global_load_lds, 16 bytes a lane): wave w's load u fills the 64
+        // consecutive 16-byte slots (9w + u) * 64 + lane of the tile, whose rows
+        // are 9 slots (a key's 8 pieces and the pad slot, which takes piece 0
+        // again and is never read).  No staging registers: they hold the head
+        // weights instead.
+        constexpr bool DMA = FULL && !F4;
+        constexpr int SLOTS = kPfRowBytes / 16;
+        static_assert(!DMA || (kPfChunk * SLOTS) % 256 == 0, "the waves' loads cover the tile's slots");
+        i32x4 stg[DMA ? 1 : PKMAX];
         float stg_s;
         uint32_t stg_w = 0;
-        auto load_tile = [&](int kc0) {
+        auto load_tile = [&](int kc0, int tb) {
+            if constexpr (DMA) {
+#pragma unroll
+                for (int u = 0; u < kPfChunk * SLOTS / 256; ++u) {
+                    const int sl = (wave * (kPfChunk * SLOTS / 256) + u) * 64 + lane;
+                    const int kk = sl / SLOTS, pp = sl % SLOTS, k = kc0 + kk;
+                    const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
+                    const bool ok = bid >= 0 && bid < C.n_blocks;
+                    const uint8_t *src =
+                        pool + (ok ? (int64_t)bid * L.index_block_bytes + (k % L.epb) * L.key_bytes + (pp < 8 ? pp : 0) * 16 : 0);
+                    __builtin_amdgcn_global_load_lds(
+                        (const __attribute__((address_space(1))) void *)src,
+                        (__attribute__((address_space(3))) void *)(tile[tb] + (sl - lane) * 16), 16, 0, 0);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < PKMAX; ++u) {
-                if (u >= PK) break;
+                if (DMA || u >= PK) break;
                 const int pc = tid + 256 * u, kk = pc / PK, off = (pc % PK) * 16, k = kc0 + kk;
                 const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
                 const bool ok = bid >= 0 && bid < C.n_blocks;
@@ -588,7 +611,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         auto store_tile = [&](int b) {
 #pragma unroll
             for (int u = 0; u < PKMAX; ++u) {
-                if (u >= PK) break;
+                if (DMA || u >= PK) break;
                 const int pc = tid + 256 * u, kk = pc / PK, off = (pc % PK) * 16;
                 *(i32x4 *)(tile[b] + kk * kPfRowBytes + off) = stg[u];
             }
@@ -604,11 +627,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         static_assert(QW == 2, "two rows a wave: the four lane groups take two rows of two sub-blocks");
         static_assert((kPfChunk / 16) % 2 == 0, "sub-blocks in pairs inside a tile");
         uint32_t kmn = 0xffffffffu, kmx = 0u;            // extremes of the lane's row (g % 2)
-        // (MXFP4) the lane's head weights held in registers for the pass: the
+        // The lane's head weights held in registers for the pass (MXFP4 rows,
+        // and E4M3 rows whose tiles are copied without staging registers): the
         // same 32 values serve every sub-block, and read from LDS per
-        // sub-block they were four times the key operand's LDS bytes.  (The
-        // E4M3 kernel has no registers to spare for them.)
-        constexpr bool WREG = F4;
+        // sub-block they were four times the key operand's LDS bytes.
+        constexpr bool WREG = F4 || DMA;
         f32x4 wreg[WREG ? 2 : 1][WREG ? HB : 1];
         if constexpr (WREG) {
 #pragma unroll
@@ -674,13 +697,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 }
             }
         };
-        load_tile(kbeg);
+        // (DMA: every wave waits for its own copies before each tile barrier)
+        auto copies_done = [&]() {
+            if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        load_tile(kbeg, 0);
         store_tile(0);
+        copies_done();
         __syncthreads();
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
             const int kc0 = kbeg + c * kPfChunk, b = c & 1;
-            if (c + 1 < nch) load_tile(kc0 + kPfChunk);  // in flight while this tile is scored
+            if (c + 1 < nch) load_tile(kc0 + kPfChunk, b ^ 1);   // in flight while this tile is scored
             kmn = 0xffffffffu;
             kmx = 0u;
 #pragma unroll 1
@@ -704,6 +732,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                     wr[(int64_t)(row0 + lrw) * nwr + kc0 / kKeysPerWave] = make_uint2(mn, mx);
             }
             if (c + 1 < nch) store_tile(b ^ 1);
+            copies_done();
             __syncthreads();                             // next tile visible; this one free
         }
     }
