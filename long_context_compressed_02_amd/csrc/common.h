@@ -136,20 +136,24 @@ __device__ __forceinline__ void rope_cs_theta(double theta, int64_t pos, float &
 __device__ __forceinline__ void rope_cs(const Lay &L, int64_t pos, int i, float &c, float &s) {
     rope_cs_theta(L.theta[i], pos, c, s);
 }
-// theta_i for a lane-dependent i < n, read from the argument block with
-// uniform (scalar) loads: a per-lane indexed read is a vector load, and the
-// wait for it also waits for every vector load issued before it.
-// (Each value passes readfirstlane: without it the compiler folds the select
-// chain back into one per-lane load.)
-__device__ __forceinline__ double theta_pick(const Lay &L, int i, int n) {
-    double th = 0.0;
-    for (int k = 0; k < n && k < 64; ++k) {
+// theta_l for lane l < n of the wave, read from the argument block with
+// uniform (scalar) loads and written into each lane with v_writelane: a
+// per-lane indexed read is a vector load, and the wait for it also waits for
+// every vector load issued before it (a select chain over the n values, the
+// earlier form, was folded back into that load by the compiler or, with the
+// values forced uniform, held enough registers to spill).
+__device__ __forceinline__ double theta_lane(const Lay &L, int n) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+        if (k >= n) break;
         const uint64_t b = (uint64_t)__double_as_longlong(L.theta[k]);
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-        th = i == k ? __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)) : th;
+        const uint32_t blo = (uint32_t)b, bhi = (uint32_t)(b >> 32);
+        // (register moves only: v_writelane_b32 takes a scalar source and a constant lane)
+        asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(lo) : "s"(blo), "i"(k));
+        asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(hi) : "s"(bhi), "i"(k));
     }
-    return th;
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // Wave-wide max over the 64 lanes, returned to every lane.  Max is exact and

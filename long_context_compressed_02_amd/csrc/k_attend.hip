@@ -326,7 +326,7 @@ __global__ __launch_bounds__(64 * kParts * NSW) __attribute__((amdgpu_waves_per_
     if (last_ok >= 0) atomicMax(&safe_sh, last_ok);
     if (tid < DR / 2) {
         float c, sn;
-        rope_cs_theta(theta_pick(L, tid, DR / 2), Q.t, c, sn);   // (scalar reads of theta: no wait on the loads in flight)
+        rope_cs_theta(theta_lane(L, DR / 2), Q.t, c, sn);   // (lane l: theta_l from scalar reads)
         rope_tab[tid] = make_float2(c, sn);
     }
     __syncthreads();
@@ -908,7 +908,7 @@ __global__ __launch_bounds__(64 * kSubsets) void k_attend_lo(AttnArgs A) {
         }
     if (lane < DR / 2) {
         float c, sn;
-        rope_cs_theta(theta_pick(L, lane, DR / 2), Q.t, c, sn);   // (scalar reads of theta: no wait on the loads in flight)
+        rope_cs_theta(theta_lane(L, DR / 2), Q.t, c, sn);   // (lane l: theta_l from scalar reads)
         rtab[lane] = make_float2(c, sn);
     }
     wave_lds_fence();
@@ -1385,7 +1385,7 @@ __global__ __launch_bounds__(64 * kSubsets * kParts) void k_attend_lo8(AttnArgs 
         if constexpr (DQ == 1) {
             if (lane < DR / 2) {
                 float c, sn;
-                rope_cs_theta(theta_pick(L, lane, DR / 2), Q.t, c, sn);   // (scalar reads of theta: no wait on the loads in flight)
+                rope_cs_theta(theta_lane(L, DR / 2), Q.t, c, sn);   // (lane l: theta_l from scalar reads)
                 rtab[lane] = make_float2(c, sn);
             }
         }
@@ -1805,7 +1805,7 @@ __global__ __launch_bounds__((HqShape<D, DR>::NT)) __attribute__((amdgpu_waves_p
     if (last_ok >= 0) atomicMax(&safe_sh, last_ok);
     if (tid < DR / 2) {
         float c, sn;
-        rope_cs_theta(theta_pick(L, tid, DR / 2), Q.t, c, sn);   // (scalar reads of theta: no wait on the loads in flight)
+        rope_cs_theta(theta_lane(L, DR / 2), Q.t, c, sn);   // (lane l: theta_l from scalar reads)
         rope_tab[tid] = make_float2(c, sn);
     }
     __syncthreads();

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_compress_decode(Lay L, dsv4_cache C, co
     // there), on the last wave while the others start their loads
     if (tid >= 192 && tid - 192 < DR / 2) {
         float c, sn;
-        rope_cs_theta(theta_pick(L, tid - 192, DR / 2), t, c, sn);
+        rope_cs_theta(theta_lane(L, DR / 2), t, c, sn);
         cs_tab[tid - 192] = make_float2(c, sn);
     }
     // 2. one batch of loads into LDS: token slot s of the window (the new one
