@@ -110,6 +110,24 @@ def test_mx_linear_small_ragged(K, N):
         assert (out[M // 2] == 0).all()
 
 
+@pytest.mark.parametrize("M, N, K", [(1300, 256, 384), (4100, 4096, 128)])
+def test_mx_linear_lds_tile_groups(M, N, K):
+    # The LDS-staged tilings over several groups of four row tiles (the XCD
+    # tile order), the last row tile ragged: 1300 x 256 takes 256x128 tiles
+    # (12 of them, too few for 256-wide ones), 4100 x 4096 the 256x256 tiles
+    # (17 x 16 = 272 of them).  Every row against the oracle; the last 100
+    # rows bitwise the same in a launch of their own (the 64-row tilings).
+    g = np.random.default_rng([8, M, N])
+    w = _bf16(g.standard_normal((N, K)) / np.sqrt(K))
+    wp = _pack(w)
+    x = _bf16(g.standard_normal((M, K)) * g.lognormal(0, 1, (M, 1)))
+    print(f"mx_linear LDS tile groups M={M} N={N} K={K}", flush=True)
+    out = _linear(x, wp, N)
+    _check_f32(out, x, w)
+    tail = _linear(x[M - 100:].contiguous(), wp, N)
+    assert torch.equal(tail.view(torch.int32), out[M - 100:].view(torch.int32))
+
+
 def test_mx_linear_batch_invariance_and_bf16_out():
     g = np.random.default_rng(9)
     N, K = 256, 1024
