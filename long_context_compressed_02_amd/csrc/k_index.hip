@@ -74,18 +74,29 @@ __device__ __forceinline__ void load_q_pair(const Lay &L, const void *qI, int64_
     x1 = 2 * lane + 1 < dI ? x1 : 0.0f;
 }
 
-// One wave per (query, head) row (prefill batches; decode quantises inside
-// the scoring kernel).
+// kQuantRows (query, head) rows a wave, one after another, their loads issued
+// first (prefill batches; decode quantises inside the scoring kernel).  With
+// one row a wave the waves did too little to cover their start.
+constexpr int kQuantRows = 8;
 __global__ __launch_bounds__(256) void k_quant_index_q(Lay L, const void *qI, const float *w,
                                                        int rows, uint8_t *q8, float *wq) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    float x0, x1;
-    load_q_pair(L, qI, row, x0, x1);
-    const float wr = w ? w[row] : 1.0f;
-    const float v = L.idx_store == DSV4_STORE_MXFP4 ? quant_q_row<true>(L, x0, x1, wr, q8 + row * 128)
-                                                    : quant_q_row<false>(L, x0, x1, wr, q8 + row * 128);
-    if ((threadIdx.x & 63) == 0) wq[row] = v;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kQuantRows;
+    if (row0 >= rows) return;
+    float x0[kQuantRows], x1[kQuantRows], wr[kQuantRows];
+#pragma unroll
+    for (int i = 0; i < kQuantRows; ++i) {          // (rows past the end re-read the last one, never stored)
+        const int64_t row = row0 + i < rows ? row0 + i : rows - 1;
+        load_q_pair(L, qI, row, x0[i], x1[i]);
+        wr[i] = w ? w[row] : 1.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kQuantRows; ++i) {
+        const int64_t row = row0 + i;
+        if (row >= rows) break;                      // (wave-uniform)
+        const float v = L.idx_store == DSV4_STORE_MXFP4 ? quant_q_row<true>(L, x0[i], x1[i], wr[i], q8 + row * 128)
+                                                        : quant_q_row<false>(L, x0[i], x1[i], wr[i], q8 + row * 128);
+        if ((threadIdx.x & 63) == 0) wq[row] = v;
+    }
 }
 
 // p(l) + p(l^16) + p(l^32) + p(l^48) as (p(l) + p(l^16)) + (p(l^32) + p(l^48)):
@@ -1105,29 +1116,43 @@ __global__ __launch_bounds__(kTkThreads) void k_tk_bin(TkArgs A) {
     uint32_t above;
     tk_find_bin(hist, kTkBins, k, wt, &bstar, &above);
     // per segment: elements above b* and inside b* (NaN scores form the bin
-    // below bin 0); wave w takes segments w, w + 4, ...
-    for (int s = wave; s < S; s += kTkWaves) {
-        const uint16_t *h = gh + (int64_t)s * kTkBins + 32 * lane;
-        uint32_t sure = 0, all = 0, inb = 0;
+    // below bin 0); wave w takes segments w, w + 4, ..., the loads of four of
+    // them at a time in flight (segments past S re-read segment S-1, unused)
+    constexpr int SB = 4;
+    for (int s0 = wave; s0 < S; s0 += SB * kTkWaves) {
+        uint4 hv[SB][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t e[8];
-            tk_unpack8(*(const uint4 *)(h + 8 * j), e);
+        for (int b4 = 0; b4 < SB; ++b4) {
+            const int s = min(s0 + b4 * kTkWaves, S - 1);
+            const uint16_t *h = gh + (int64_t)s * kTkBins + 32 * lane;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int b = 32 * lane + 8 * j + i;
-                all += e[i];
-                sure += b > bstar ? e[i] : 0u;
-                inb += b == bstar ? e[i] : 0u;
-            }
+            for (int j = 0; j < 4; ++j) hv[b4][j] = *(const uint4 *)(h + 8 * j);
         }
-        sure = wave_sum(sure);
-        all = wave_sum(all);
-        inb = wave_sum(inb);
-        if (lane == 0) {
-            const uint32_t ns = (uint32_t)min((int64_t)kTkSeg, N - (int64_t)s * kTkSeg);
-            seg_sure[s] = sure;
-            seg_cand[s] = bstar >= 0 ? inb : ns - all;
+#pragma unroll
+        for (int b4 = 0; b4 < SB; ++b4) {
+            const int s = s0 + b4 * kTkWaves;
+            if (s >= S) break;                       // (wave-uniform)
+            uint32_t sure = 0, all = 0, inb = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t e[8];
+                tk_unpack8(hv[b4][j], e);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int b = 32 * lane + 8 * j + i;
+                    all += e[i];
+                    sure += b > bstar ? e[i] : 0u;
+                    inb += b == bstar ? e[i] : 0u;
+                }
+            }
+            sure = wave_sum(sure);
+            all = wave_sum(all);
+            inb = wave_sum(inb);
+            if (lane == 0) {
+                const uint32_t ns = (uint32_t)min((int64_t)kTkSeg, N - (int64_t)s * kTkSeg);
+                seg_sure[s] = sure;
+                seg_cand[s] = bstar >= 0 ? inb : ns - all;
+            }
         }
     }
     __syncthreads();
@@ -1505,7 +1530,8 @@ hipError_t launch_expand_queries(const int32_t *cu, const int32_t *req, const in
 
 hipError_t launch_quant_q(const Lay &L, const void *qI, const float *w, int rows, const IndexWs &ws,
                           hipStream_t s) {
-    hipLaunchKernelGGL(k_quant_index_q, dim3((rows + 3) / 4), dim3(256), 0, s, L, qI, w, rows, ws.q8, ws.wq);
+    const int64_t waves = (rows + kQuantRows - 1) / kQuantRows;
+    hipLaunchKernelGGL(k_quant_index_q, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, L, qI, w, rows, ws.q8, ws.wq);
     return hipGetLastError();
 }
 
