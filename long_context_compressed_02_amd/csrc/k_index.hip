@@ -583,16 +583,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         i32x4 stg[DMA ? 1 : PKMAX];
         float stg_s;
         uint32_t stg_w = 0;
+        // key k (>= 0) sits in block k >> lgb at slot k & slot_mask: the
+        // entries per block, 128 / m, are a power of two (divisions by the
+        // layout's runtime values took a few dozen instructions a key)
+        const uint32_t lgb = (uint32_t)__builtin_ctz((uint32_t)L.epb);
+        const uint32_t slot_mask = (uint32_t)L.epb - 1u;
         auto load_tile = [&](int kc0, int tb) {
             if constexpr (DMA) {
 #pragma unroll
                 for (int u = 0; u < kPfChunk * SLOTS / 256; ++u) {
                     const int sl = (wave * (kPfChunk * SLOTS / 256) + u) * 64 + lane;
                     const int kk = sl / SLOTS, pp = sl % SLOTS, k = kc0 + kk;
-                    const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
+                    const int bid = k < Nmax ? btl[(int)((uint32_t)k >> lgb) - blk0] : -1;
                     const bool ok = bid >= 0 && bid < C.n_blocks;
-                    const uint8_t *src =
-                        pool + (ok ? (int64_t)bid * L.index_block_bytes + (k % L.epb) * L.key_bytes + (pp < 8 ? pp : 0) * 16 : 0);
+                    const uint8_t *src = pool + (ok ? (int64_t)bid * L.index_block_bytes +
+                                                          (int)((uint32_t)k & slot_mask) * L.key_bytes + (pp < 8 ? pp : 0) * 16
+                                                    : 0);
                     __builtin_amdgcn_global_load_lds(
                         (const __attribute__((address_space(1))) void *)src,
                         (__attribute__((address_space(3))) void *)(tile[tb] + (sl - lane) * 16), 16, 0, 0);
@@ -602,16 +608,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             for (int u = 0; u < PKMAX; ++u) {
                 if (DMA || u >= PK) break;
                 const int pc = tid + 256 * u, kk = pc / PK, off = (pc % PK) * 16, k = kc0 + kk;
-                const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
+                const int bid = k < Nmax ? btl[(int)((uint32_t)k >> lgb) - blk0] : -1;
                 const bool ok = bid >= 0 && bid < C.n_blocks;
-                const uint8_t *src = pool + (ok ? (int64_t)bid * L.index_block_bytes + (k % L.epb) * L.key_bytes + off : 0);
+                const uint8_t *src =
+                    pool + (ok ? (int64_t)bid * L.index_block_bytes + (int)((uint32_t)k & slot_mask) * L.key_bytes + off : 0);
                 stg[u] = *(const i32x4 *)src;
             }
             const int k = kc0 + tid;
-            const int bid = k < Nmax ? btl[(k * L.m) / kBlockTokens - blk0] : -1;
+            const int bid = k < Nmax ? btl[(int)((uint32_t)k >> lgb) - blk0] : -1;
             const bool ok = bid >= 0 && bid < C.n_blocks;
             const uint32_t sv = *(const uint32_t *)(pool + (ok ? (int64_t)bid * L.index_block_bytes + L.key_scale_off +
-                                                                  (k % L.epb) * 4 : 0));
+                                                                  (int)((uint32_t)k & slot_mask) * 4 : 0));
             if constexpr (F4) {
                 stg_s = ok ? 1.0f : 0.0f;
                 stg_w = sv;
