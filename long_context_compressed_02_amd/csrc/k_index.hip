@@ -680,6 +680,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                         acc[ii][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             A[ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
                 }
+            // the eight products issue back to back into their own registers:
+            // left to itself the compiler reused two accumulators, so each
+            // product waited for the previous one's epilogue
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii) {
                 part[ii] = 0.0f;
