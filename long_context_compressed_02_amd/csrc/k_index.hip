@@ -277,6 +277,7 @@ __global__ __launch_bounds__(256) void k_index_score_decode(Lay L, dsv4_cache C,
                 acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     A[hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
         }
+        __builtin_amdgcn_sched_barrier(0);         // the products back to back, each into its own registers
         float part = 0.0f;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
