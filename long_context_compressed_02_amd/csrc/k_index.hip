@@ -468,8 +468,9 @@ __global__ __launch_bounds__(256) void k_index_score_f32(Lay L, dsv4_cache C, co
 // all rows of the workgroup.  A (row, 16-key sub-block) score takes exactly
 // the decode scorer's operations, so a prefilled query scores bitwise like a
 // decode step.  Rows of several requests in one workgroup are taken one
-// request at a time.  Compiled for three waves per SIMD (the compiler spills
-// a few registers): 2 % faster than two on the 8K prefill chunk, measured.
+// request at a time.  The kernel asks the compiler for three waves per SIMD;
+// the full-width variants (128-dim rows) need more registers than that allows
+// (E4M3 254, MXFP4 228) and run two, which their LDS tiles allow anyway.
 constexpr int kPfWaveRows = 2;
 constexpr int kPfRows = 4 * kPfWaveRows;
 constexpr int kPfKeys = 2048;
@@ -658,6 +659,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) wreg[ii][hb] = wls[wr0 + ii][hb * 4 + g];
         }
+        // MXFP4 rows: a sub-block's eight products, then their epilogue
         auto partials = [&](int b, int sb, float (&part)[2]) {
             i32x8 Bk;
             const uint8_t *kr = tile[b] + (sb * 16 + c16) * kPfRowBytes;
@@ -702,6 +704,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const bool lact = ((act >> lrw) & 1) != 0;
         const int lN = Nq[lrw];
         float *lsrow = scores + (int64_t)(row0 + lrw) * ld;
+        // E4M3 rows: a sub-block's key operand, and the products of one row
+        // of the wave with it (HB MFMAs)
+        auto load_b = [&](int b, int sb, i32x8 &Bk) {
+            const uint8_t *kr = tile[b] + (sb * 16 + c16) * kPfRowBytes;
+            Bk.lo = *(const i32x4 *)(kr + 16 * g);
+            Bk.hi = *(const i32x4 *)(kr + 64 + 16 * g);
+        };
+        auto mma = [&](const i32x8 &Bk, int ii, f32x4 (&acc)[HB]) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    A[ii][hb], Bk, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+        };
+        // ReLU and head weight of those products, summed in head order (the
+        // decode scorer's chain)
+        auto epi = [&](const f32x4 (&acc)[HB], int ii) {
+            float part = 0.0f;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                f32x4 w4;
+                if constexpr (WREG) w4 = wreg[ii][hb];
+                else w4 = wls[wr0 + ii][hb * 4 + g];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part = relu_fma(acc[hb][j], w4[j], part);
+            }
+            return part;
+        };
+        // Software pipeline over (sub-block, row) halves: each stage issues
+        // the next half's products between the epilogue instructions of the
+        // current one (one MFMA per eight VALU operations), so one wave keeps
+        // the matrix unit and the VALU busy together.  X and Y take turns as
+        // the accumulators; the sums and their order are unchanged.
+        auto interleave = [&]() {
+#pragma unroll
+            for (int i = 0; i < HB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+            }
+        };
+        auto score_tile = [&](int b, int kc0) {
+            const int np = min(kPfChunk / 32, (kend - kc0 + 31) / 32);   // sub-block pairs holding keys
+            i32x8 Bc, Bn;
+            f32x4 X[HB], Y[HB];
+            load_b(b, 0, Bc);
+            mma(Bc, 0, X);
+#pragma unroll 1
+            for (int p = 0; p < np; ++p) {
+                const int sb = 2 * p;
+                const bool more = p + 1 < np;
+                __builtin_amdgcn_sched_barrier(0);
+                load_b(b, sb + 1, Bn);
+                mma(Bc, 1, Y);
+                const float r0 = epi(X, 0);
+                interleave();
+                __builtin_amdgcn_sched_barrier(0);
+                mma(Bn, 0, X);
+                const float r1 = epi(Y, 1);
+                interleave();
+                __builtin_amdgcn_sched_barrier(0);
+                load_b(b, more ? sb + 2 : sb, Bc);   // (the last pair: its own again, in bounds)
+                mma(Bn, 1, Y);
+                const float r2 = epi(X, 0);
+                interleave();
+                __builtin_amdgcn_sched_barrier(0);
+                mma(Bc, 0, X);                           // (after the last pair: discarded)
+                const float r3 = epi(Y, 1);
+                interleave();
+                // X is read only by the next pass: without this use the
+                // compiler sinks its products to the top of the loop, out of
+                // this stage's interleave
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) asm volatile("" : "+v"(X[hb]));
+                __builtin_amdgcn_sched_barrier(0);
+                // the four partial sums reduced together: lane group g then
+                // holds sub-block sb + g / 2 of row g % 2
+                const float part = group_sum4x4(r0, r1, r2, r3);
+                const int key = kc0 + sb * 16 + 16 * ls + c16;
+                const float sk = tsc[b][(sb + ls) * 16 + c16];
+                if (lact && key < lN) {
+                    const float v = sk * part;
+                    lsrow[key] = v;
+                    if (fabsf(v) < INFINITY) {
+                        const uint32_t u = score_key(v);
+                        kmn = min(kmn, u);
+                        kmx = max(kmx, u);
+                    }
+                }
+            }
+        };
         auto score_pair = [&](int b, int sb, int kb) {   // sub-blocks sb, sb + 1; kb: the first key of sb
             float p0[2], p1[2];
             partials(b, sb, p0);
@@ -734,11 +825,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             if (c + 1 < nch) load_tile(kc0 + kPfChunk, b ^ 1);   // in flight while this tile is scored
             kmn = 0xffffffffu;
             kmx = 0u;
+            if constexpr (F4) {
 #pragma unroll 1
-            for (int sb = 0; sb < kPfChunk / 16; sb += 2) {
-                const int kb = kc0 + sb * 16;
-                if (kb >= kend) break;                   // workgroup-uniform
-                score_pair(b, sb, kb);
+                for (int sb = 0; sb < kPfChunk / 16; sb += 2) {
+                    const int kb = kc0 + sb * 16;
+                    if (kb >= kend) break;               // workgroup-uniform
+                    score_pair(b, sb, kb);
+                }
+            } else {
+                score_tile(b, kc0);
             }
             // this tile's extremes per row (the record the decode scorer's wave
             // for these keys writes): over the lanes of the row's two lane
