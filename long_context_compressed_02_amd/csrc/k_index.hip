@@ -733,9 +733,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         };
         // Software pipeline over (sub-block, row) halves: each stage issues
         // the next half's products between the epilogue instructions of the
-        // current one (one MFMA per eight VALU operations), so one wave keeps
-        // the matrix unit and the VALU busy together.  X and Y take turns as
-        // the accumulators; the sums and their order are unchanged.
+        // current one (one MFMA per eight VALU operations), so one wave feeds
+        // the matrix unit and the VALU together (only in part: each of these
+        // MFMAs holds the VALU issue for about half of its 32 cycles).  X and
+        // Y take turns as the accumulators; the sums and their order are
+        // unchanged.
         auto interleave = [&]() {
 #pragma unroll
             for (int i = 0; i < HB; ++i) {
